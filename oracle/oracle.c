@@ -1,0 +1,337 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the lightning-indexer score + top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  The GPU product
+ * path never links, imports or calls it, and it shares no code, header,
+ * table or helper with the GPU path.
+ *
+ * What it computes (one query token t at absolute position pos_t):
+ *
+ *   1. Visible rows.  A compressed KV row j summarises the r raw tokens
+ *      r*j .. r*j+r-1 and becomes visible once the last of them has been
+ *      seen, i.e. when r*j + r - 1 <= pos_t.  So the visible rows are
+ *      j = 0 .. n_t-1 with n_t = floor((pos_t + 1) / r), clamped to [0, N].
+ *      ("How I made DeepSeek 12x faster on a Mac Studio", section
+ *      "1: the kernels": the lightning indexer scores *compressed* KV.)
+ *
+ *   2. Score of a visible row:
+ *        s[t,j] = sum over index heads h of  w[t,h] * max(0, q[t,h,:] . k[j,:])
+ *      where every index head of token t is dotted with the same compressed
+ *      row k[j].
+ *
+ *   3. Selection: the min(n_t, topk) best rows under the order
+ *      (score descending, row index ascending) -- i.e. among equal scores the
+ *      lower row wins.  ("1: the kernels" on the same page: the indexer keeps
+ *      the top 512 rows per token; the streaming top-k there is stated to
+ *      give byte-identical output to a full sort, so the oracle *is* the
+ *      full sort.)
+ *
+ *   4. Output: the selected rows in ascending row order, then -1 padding up
+ *      to topk entries.  When every visible row fits (n_t <= topk) this is
+ *      exactly 0 .. n_t-1 ("How I turned one oversized DeepSeek optimization
+ *      into three merged oMLX PRs", section "3. Do not rank candidates when
+ *      every candidate wins": the same sequential indices are produced).
+ *      With n_t = 0 the row is all -1.
+ *
+ * Arithmetic: fp16 / bf16 inputs are decoded exactly to double (decoders
+ * written from the IEEE 754 binary16 definition and from bfloat16 being the
+ * top half of an IEEE binary32); every product, dot product, ReLU, weight
+ * multiply and head sum is done in double; the sort compares doubles.
+ * Non-finite inputs are rejected (status ORACLE_ERR_NONFINITE).
+ *
+ * Nothing here is blocked, fused or reordered: per token it scores every
+ * visible row, sorts all of them, takes the first m, and sorts those by row.
+ * Threads (pthreads) only split the token list; each token is computed by
+ * one thread from start to finish.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F16 1
+#define ORACLE_BF16 2
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_NONFINITE (-2)
+#define ORACLE_ERR_NOMEM (-3)
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_half_to_double(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 10) & 0x1F;
+    int frac = bits & 0x3FF;
+    double mag;
+    if (expo == 0x1F)
+        mag = frac ? NAN : INFINITY;
+    else if (expo == 0)
+        mag = ldexp((double)frac, -24);              /* subnormal: frac * 2^-14 * 2^-10 */
+    else
+        mag = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/2^10) * 2^(expo-15) */
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32 -- 1 sign bit, 8 exponent
+ * bits (bias 127), 7 fraction bits. */
+double oracle_bf16_to_double(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 7) & 0xFF;
+    int frac = bits & 0x7F;
+    double mag;
+    if (expo == 0xFF)
+        mag = frac ? NAN : INFINITY;
+    else if (expo == 0)
+        mag = ldexp((double)frac, -133);              /* frac * 2^-126 * 2^-7 */
+    else
+        mag = ldexp((double)(128 + frac), expo - 134); /* (1 + frac/2^7) * 2^(expo-127) */
+    return sign ? -mag : mag;
+}
+
+static double decode(uint16_t bits, int dtype)
+{
+    return dtype == ORACLE_F16 ? oracle_half_to_double(bits) : oracle_bf16_to_double(bits);
+}
+
+/* Number of compressed rows visible to a token at absolute position pos:
+ * row j is visible iff ratio*j + ratio - 1 <= pos and j < N. */
+int64_t oracle_visible_rows(int64_t pos, int64_t ratio, int64_t n_rows)
+{
+    int64_t n;
+    if (pos < 0)
+        return 0;
+    n = (pos + 1) / ratio;
+    if (n > n_rows)
+        n = n_rows;
+    return n;
+}
+
+typedef struct {
+    double score;
+    int64_t row;
+} scored_row;
+
+/* Order of selection: higher score first; among equal scores, lower row first. */
+static int by_score_desc_row_asc(const void *pa, const void *pb)
+{
+    const scored_row *a = (const scored_row *)pa;
+    const scored_row *b = (const scored_row *)pb;
+    if (a->score > b->score)
+        return -1;
+    if (a->score < b->score)
+        return 1;
+    if (a->row < b->row)
+        return -1;
+    if (a->row > b->row)
+        return 1;
+    return 0;
+}
+
+static int by_row_asc(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa;
+    int64_t b = *(const int64_t *)pb;
+    return (a > b) - (a < b);
+}
+
+typedef struct {
+    /* problem */
+    const uint16_t *q;   /* [T][H][D] raw fp16/bf16 bits */
+    const double *k;     /* [N][D] decoded rows */
+    const float *w;      /* [T][H] */
+    const int32_t *pos;  /* [T] */
+    int64_t T, N;
+    int H, D, dtype, ratio, topk;
+    const int64_t *tokens; /* which tokens to compute (length n_out) */
+    int64_t n_out;
+    int32_t *out;        /* [n_out][topk] */
+    double *scores;      /* optional [n_out][N]; -inf where not visible */
+    /* threading */
+    int nthreads;
+    int tid;
+    int status;
+} job;
+
+static void *run_job(void *arg)
+{
+    job *jb = (job *)arg;
+    const int H = jb->H, D = jb->D;
+    double *qt = (double *)malloc(sizeof(double) * (size_t)H * (size_t)D);
+    scored_row *rows = (scored_row *)malloc(sizeof(scored_row) * (size_t)(jb->N > 0 ? jb->N : 1));
+    int64_t *chosen = (int64_t *)malloc(sizeof(int64_t) * (size_t)(jb->topk > 0 ? jb->topk : 1));
+    int64_t i;
+    jb->status = ORACLE_OK;
+    if (!qt || !rows || !chosen) {
+        jb->status = ORACLE_ERR_NOMEM;
+        goto done;
+    }
+    for (i = jb->tid; i < jb->n_out; i += jb->nthreads) {
+        const int64_t t = jb->tokens ? jb->tokens[i] : i;
+        const float *wt = jb->w + t * H;
+        int32_t *o = jb->out + i * jb->topk;
+        const int64_t n = oracle_visible_rows(jb->pos[t], jb->ratio, jb->N);
+        int64_t j, m, c;
+        int h, d;
+        for (h = 0; h < H; ++h) {
+            if (!isfinite((double)wt[h])) {
+                jb->status = ORACLE_ERR_NONFINITE;
+                goto done;
+            }
+            for (d = 0; d < D; ++d) {
+                double v = decode(jb->q[(t * H + h) * D + d], jb->dtype);
+                if (!isfinite(v)) {
+                    jb->status = ORACLE_ERR_NONFINITE;
+                    goto done;
+                }
+                qt[h * D + d] = v;
+            }
+        }
+        /* score every visible row */
+        for (j = 0; j < n; ++j) {
+            const double *kj = jb->k + j * D;
+            double s = 0.0;
+            for (h = 0; h < H; ++h) {
+                double x = 0.0;
+                for (d = 0; d < D; ++d)
+                    x += qt[h * D + d] * kj[d];
+                s += (double)wt[h] * (x > 0.0 ? x : 0.0);
+            }
+            rows[j].score = s;
+            rows[j].row = j;
+        }
+        if (jb->scores) {
+            double *so = jb->scores + i * jb->N;
+            for (j = 0; j < jb->N; ++j)
+                so[j] = j < n ? rows[j].score : -INFINITY;
+        }
+        /* full sort, keep the first m, emit them in ascending row order */
+        qsort(rows, (size_t)n, sizeof(scored_row), by_score_desc_row_asc);
+        m = n < jb->topk ? n : jb->topk;
+        for (c = 0; c < m; ++c)
+            chosen[c] = rows[c].row;
+        qsort(chosen, (size_t)m, sizeof(int64_t), by_row_asc);
+        for (c = 0; c < jb->topk; ++c)
+            o[c] = c < m ? (int32_t)chosen[c] : -1;
+    }
+done:
+    free(qt);
+    free(rows);
+    free(chosen);
+    return NULL;
+}
+
+/*
+ * Score and select for the tokens listed in `tokens` (or all T tokens when
+ * `tokens` is NULL, in which case n_out must equal T).
+ *
+ *   q      [T][H][D]  raw fp16 (dtype 1) or bf16 (dtype 2) bits
+ *   k      [N][D]     raw bits, same dtype
+ *   w      [T][H]     float32 head weights
+ *   pos    [T]        int32 absolute positions
+ *   out    [n_out][topk] int32: ascending selected rows, then -1
+ *   scores optional [n_out][N] double: the score of every visible row,
+ *          -inf for rows the token cannot see
+ *   threads  worker threads (<= 0: 1)
+ *
+ * Returns ORACLE_OK, ORACLE_ERR_ARG, ORACLE_ERR_NONFINITE or ORACLE_ERR_NOMEM.
+ */
+int oracle_score_topk(const uint16_t *q, const uint16_t *k, const float *w, const int32_t *pos,
+                      int64_t T, int64_t N, int H, int D, int dtype, int ratio, int topk,
+                      const int64_t *tokens, int64_t n_out, int32_t *out, double *scores,
+                      int threads)
+{
+    double *kd;
+    job *jobs;
+    pthread_t *tids;
+    int *started;
+    int64_t i, need_rows = 0;
+    int th, status = ORACLE_OK;
+
+    if (T < 0 || N < 0 || H < 1 || D < 1 || ratio < 1 || topk < 1 || n_out < 0)
+        return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+        return ORACLE_ERR_ARG;
+    if (!tokens && n_out != T)
+        return ORACLE_ERR_ARG;
+    if (n_out > 0 && (!q || !w || !pos || !out))
+        return ORACLE_ERR_ARG;
+    if (N > 0 && n_out > 0 && !k)
+        return ORACLE_ERR_ARG;
+    for (i = 0; i < n_out; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        int64_t n;
+        if (t < 0 || t >= T)
+            return ORACLE_ERR_ARG;
+        n = oracle_visible_rows(pos[t], ratio, N);
+        if (n > need_rows)
+            need_rows = n;
+    }
+    if (threads < 1)
+        threads = 1;
+
+    /* decode only the rows some requested token can see */
+    kd = (double *)malloc(sizeof(double) * (size_t)(need_rows > 0 ? need_rows * D : 1));
+    if (!kd)
+        return ORACLE_ERR_NOMEM;
+    for (i = 0; i < need_rows * D; ++i) {
+        kd[i] = decode(k[i], dtype);
+        if (!isfinite(kd[i])) {
+            free(kd);
+            return ORACLE_ERR_NONFINITE;
+        }
+    }
+
+    jobs = (job *)calloc((size_t)threads, sizeof(job));
+    tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    started = (int *)calloc((size_t)threads, sizeof(int));
+    if (!jobs || !tids || !started) {
+        free(kd);
+        free(jobs);
+        free(tids);
+        free(started);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (th = 0; th < threads; ++th) {
+        job *jb = &jobs[th];
+        jb->q = q;
+        jb->k = kd;
+        jb->w = w;
+        jb->pos = pos;
+        jb->T = T;
+        jb->N = N;
+        jb->H = H;
+        jb->D = D;
+        jb->dtype = dtype;
+        jb->ratio = ratio;
+        jb->topk = topk;
+        jb->tokens = tokens;
+        jb->n_out = n_out;
+        jb->out = out;
+        jb->scores = scores;
+        jb->nthreads = threads;
+        jb->tid = th;
+    }
+    /* thread 0's share runs on the calling thread; a share whose thread
+     * cannot be started also runs here, so every token is always computed */
+    for (th = 1; th < threads; ++th)
+        started[th] = pthread_create(&tids[th], NULL, run_job, &jobs[th]) == 0;
+    run_job(&jobs[0]);
+    for (th = 1; th < threads; ++th) {
+        if (started[th])
+            pthread_join(tids[th], NULL);
+        else
+            run_job(&jobs[th]);
+    }
+    for (th = 0; th < threads; ++th)
+        if (jobs[th].status != ORACLE_OK)
+            status = jobs[th].status;
+    free(kd);
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
+}

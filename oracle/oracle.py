@@ -1,0 +1,120 @@
+"""ctypes front end of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The GPU product path never
+imports this module.
+
+The oracle computes, for each query token, the lightning-indexer score of
+every causally visible compressed row in double precision, sorts all of them
+by (score descending, row ascending), keeps the first min(n_t, topk), and
+returns those rows in ascending order padded with -1 (the definition is
+written out at the top of oracle.c, with its sources).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+DTYPES = {"f16": 1, "bf16": 2}
+STATUS = {0: "ok", -1: "invalid argument", -2: "non-finite input", -3: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(out: str = LIB, src: str = SRC) -> str:
+    """Compile oracle.c into a shared library with the system C compiler."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
+           "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class Oracle:
+    """One loaded copy of the oracle library (the tests also load mutated copies)."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            raise OracleError(f"oracle library {path} is not built; run __graft_entry__.build()")
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_visible_rows.restype = ctypes.c_int64
+        lib.oracle_visible_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.oracle_score_topk.restype = I
+        lib.oracle_score_topk.argtypes = [P, P, P, P, I64, I64, I, I, I, I, I, P, I64, P, P, I]
+        self.lib = lib
+
+    def half_to_double(self, bits: int) -> float:
+        return self.lib.oracle_half_to_double(int(bits))
+
+    def bf16_to_double(self, bits: int) -> float:
+        return self.lib.oracle_bf16_to_double(int(bits))
+
+    def visible_rows(self, pos: int, ratio: int, n_rows: int) -> int:
+        return self.lib.oracle_visible_rows(int(pos), int(ratio), int(n_rows))
+
+    def score_topk(self, q_bits, k_bits, w, pos, *, H: int, D: int, dtype: str, ratio: int,
+                   topk: int, tokens=None, want_scores: bool = False, threads: int = 1):
+        """Run the oracle on host arrays.
+
+        q_bits  uint16 [T, H, D] (raw fp16/bf16 bits)
+        k_bits  uint16 [N, D]
+        w       float32 [T, H]
+        pos     int32 [T]
+        tokens  optional int64 list of token indices to compute (default: all)
+
+        Returns out int32 [n_out, topk] (and scores float64 [n_out, N] with -inf
+        where a row is not visible, when want_scores).
+        """
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        T = int(pos.shape[0])
+        N = int(k_bits.shape[0]) if k_bits.ndim == 2 else 0
+        if q_bits.size != T * H * D or w.size != T * H or (N and k_bits.shape[1] != D):
+            raise OracleError("oracle: inconsistent shapes")
+        if tokens is None:
+            tok = None
+            n_out = T
+        else:
+            tok = np.ascontiguousarray(tokens, dtype=np.int64)
+            n_out = int(tok.shape[0])
+        out = np.empty((n_out, topk), dtype=np.int32)
+        scores = np.empty((n_out, N), dtype=np.float64) if want_scores else None
+
+        def ptr(a):
+            return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+        st = self.lib.oracle_score_topk(ptr(q_bits), ptr(k_bits) if N else None, ptr(w), ptr(pos),
+                                        T, N, H, D, DTYPES[dtype], ratio, topk, ptr(tok), n_out,
+                                        ptr(out), ptr(scores), int(threads))
+        if st != 0:
+            raise OracleError(f"oracle_score_topk: {STATUS.get(st, st)}")
+        return (out, scores) if want_scores else out
+
+
+_default = None
+
+
+def load() -> Oracle:
+    """The oracle built from oracle.c (loaded once per process)."""
+    global _default
+    if _default is None:
+        _default = Oracle(LIB)
+    return _default

@@ -1,0 +1,403 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle (``oracle.oracle.Oracle``) and
+raises AssertionError when the oracle disagrees with:
+  * a library routine (numpy's binary16 conversion, the bfloat16 <-> binary32
+    bit identity, numpy lexsort for the one-head case),
+  * exact rational arithmetic written out in plain Python (fractions),
+  * brute force over every candidate subset on tiny inputs,
+  * closed forms whose answer follows from the definition by hand,
+  * the hand-worked fixtures in tests/golden/,
+  * invariants of the output (ascending, unique, causal, all-fit sequential,
+    dominance of every selected row over every unselected visible row).
+
+The functions are plain so that test_oracle.py can run them against the real
+oracle and against deliberately mutated copies of it (each mutant must fail
+at least one pin).  Run as a script, ``python oracle_pins.py LIB`` exits 0 when
+every pin passes on that library and 1 otherwise.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+import sys
+from fractions import Fraction
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from oracle.oracle import Oracle, OracleError  # noqa: E402
+from sparse_attention_kv_ds_amd import synth  # noqa: E402
+
+GOLDEN = os.path.join(HERE, "golden", "hand_worked.txt")
+
+
+# ----------------------------------------------------------------------------
+# helpers (exact arithmetic, independent of the oracle)
+# ----------------------------------------------------------------------------
+
+def exact_value(bits: int, dtype: str) -> Fraction:
+    """Exact rational value of one fp16/bf16 bit pattern via numpy / the bit identity."""
+    if dtype == "f16":
+        v = float(np.array([bits], dtype=np.uint16).view(np.float16)[0])
+    else:
+        v = float(np.array([int(bits) << 16], dtype=np.uint32).view(np.float32)[0])
+    return Fraction(v)
+
+
+def exact_scores(q_bits, k_bits, w, pos, H, D, dtype, ratio):
+    """Scores as exact fractions, straight from the definition (None = not visible)."""
+    T = len(pos)
+    N = k_bits.shape[0]
+    kv = [[exact_value(k_bits[j, d], dtype) for d in range(D)] for j in range(N)]
+    out = []
+    for t in range(T):
+        # visible rows by their definition: rows whose r raw tokens all precede or equal pos
+        vis = [j for j in range(N) if ratio * j + ratio - 1 <= int(pos[t])]
+        qv = [[exact_value(q_bits[t, h, d], dtype) for d in range(D)] for h in range(H)]
+        row = [None] * N
+        for j in vis:
+            s = Fraction(0)
+            for h in range(H):
+                x = sum((qv[h][d] * kv[j][d] for d in range(D)), Fraction(0))
+                s += Fraction(float(w[t, h])) * max(x, Fraction(0))
+            row[j] = s
+        out.append(row)
+    return out
+
+
+def check_output_row(o, n, topk, where=""):
+    """Invariants of one output row for a token with n visible rows."""
+    m = min(n, topk)
+    sel = [int(x) for x in o[:m]]
+    assert all(x == -1 for x in o[m:]), f"{where}: padding must be -1: {list(o)}"
+    assert all(0 <= x < n for x in sel), f"{where}: row outside [0,{n}): {sel}"
+    assert all(a < b for a, b in zip(sel, sel[1:])), f"{where}: not strictly ascending: {sel}"
+    if n <= topk:
+        assert sel == list(range(n)), f"{where}: all-fit row must be sequential: {sel}"
+    return sel
+
+
+def rand_int_case(rng, T, N, H, D, lo, hi, ratio, pos_hi, dtype="f16", wexp=3):
+    q = synth.to_bits(rng.integers(lo, hi + 1, size=(T, H, D)).astype(np.float64), dtype)
+    k = synth.to_bits(rng.integers(lo, hi + 1, size=(N, D)).astype(np.float64), dtype)
+    w = ((rng.integers(0, 2, size=(T, H)) * 2 - 1) *
+         np.ldexp(1.0, -rng.integers(0, wexp + 1, size=(T, H)))).astype(np.float32)
+    pos = rng.integers(-2, pos_hi + 1, size=T).astype(np.int32)
+    return q, k, w, pos
+
+
+# ----------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------
+
+def pin_half_decode(orc: Oracle):
+    """Every binary16 pattern decodes to numpy's float16 value (a library routine)."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        ref = allbits.view(np.float16).astype(np.float64)
+    for b in range(65536):
+        got = orc.half_to_double(b)
+        r = ref[b]
+        if math.isnan(r):
+            assert math.isnan(got), f"f16 {b:#06x}: expected NaN, got {got}"
+        else:
+            assert got == r and math.copysign(1, got) == math.copysign(1, r), \
+                f"f16 {b:#06x}: {got} != {r}"
+
+
+def pin_bf16_decode(orc: Oracle):
+    """Every bfloat16 pattern decodes to the binary32 with the same top 16 bits."""
+    with np.errstate(invalid="ignore"):
+        ref = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    for b in range(65536):
+        got = orc.bf16_to_double(b)
+        r = ref[b]
+        if math.isnan(r):
+            assert math.isnan(got), f"bf16 {b:#06x}: expected NaN, got {got}"
+        else:
+            assert got == r and math.copysign(1, got) == math.copysign(1, r), \
+                f"bf16 {b:#06x}: {got} != {r}"
+
+
+def pin_visible_rows(orc: Oracle):
+    """n_t equals the count of rows j < N with ratio*j + ratio - 1 <= pos (brute force)."""
+    for ratio in range(1, 7):
+        for N in (0, 1, 5, 12):
+            for pos in range(-3, 60):
+                want = sum(1 for j in range(N) if ratio * j + ratio - 1 <= pos)
+                got = orc.visible_rows(pos, ratio, N)
+                assert got == want, f"visible_rows(pos={pos}, r={ratio}, N={N}) = {got}, want {want}"
+
+
+def parse_golden(path: str = GOLDEN):
+    cases = []
+    cur = None
+    with open(path) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, _, rest = line.partition(" ")
+            if key == "case":
+                cur = {"name": rest.strip(), "scores": {}, "out": {}}
+                cases.append(cur)
+            elif key in ("scores", "out"):
+                t, _, vals = rest.partition(":")
+                conv = float if key == "scores" else int
+                cur[key][int(t)] = [conv(v) for v in vals.split()]
+            elif key == "dtype":
+                cur["dtype"] = rest.strip()
+            elif key in ("T", "N", "H", "D", "ratio", "topk"):
+                cur[key] = int(rest)
+            else:
+                cur[key] = [float(v) for v in rest.split()]
+    return cases
+
+
+def pin_golden(orc: Oracle):
+    """The hand-worked examples in tests/golden/hand_worked.txt."""
+    for c in parse_golden():
+        T, N, H, D = c["T"], c["N"], c["H"], c["D"]
+        q = synth.to_bits(np.array(c["q"]).reshape(T, H, D), c["dtype"])
+        k = synth.to_bits(np.array(c["k"]).reshape(N, D), c["dtype"])
+        w = np.array(c["w"], dtype=np.float32).reshape(T, H)
+        pos = np.array(c["pos"], dtype=np.int32)
+        out, sc = orc.score_topk(q, k, w, pos, H=H, D=D, dtype=c["dtype"], ratio=c["ratio"],
+                                 topk=c["topk"], want_scores=True)
+        for t, want in c["scores"].items():
+            assert list(sc[t]) == want, f"golden {c['name']} token {t}: scores {list(sc[t])} != {want}"
+        for t, want in c["out"].items():
+            assert list(out[t]) == want, f"golden {c['name']} token {t}: out {list(out[t])} != {want}"
+
+
+def pin_exact_integer_scores(orc: Oracle):
+    """Integer-valued inputs with power-of-two weights: oracle scores equal the exact rationals."""
+    rng = np.random.default_rng(11)
+    for trial in range(12):
+        T, N = int(rng.integers(1, 5)), int(rng.integers(0, 10))
+        H, D = int(rng.integers(1, 6)), int(rng.integers(1, 7))
+        ratio = int(rng.integers(1, 5))
+        dtype = "f16" if trial % 2 == 0 else "bf16"
+        q, k, w, pos = rand_int_case(rng, T, N, H, D, -4, 4, ratio, ratio * N + 3, dtype)
+        _, sc = orc.score_topk(q, k, w, pos, H=H, D=D, dtype=dtype, ratio=ratio, topk=3,
+                               want_scores=True)
+        ex = exact_scores(q, k, w, pos, H, D, dtype, ratio)
+        for t in range(T):
+            for j in range(N):
+                if ex[t][j] is None:
+                    assert sc[t, j] == -math.inf, f"trial {trial}: ({t},{j}) should be invisible"
+                else:
+                    assert math.isfinite(sc[t, j]) and Fraction(sc[t, j]) == ex[t][j], \
+                        f"trial {trial}: score ({t},{j}) {sc[t, j]} != {ex[t][j]}"
+
+
+def pin_gaussian_scores(orc: Oracle):
+    """Gaussian fp16/bf16 inputs: oracle scores agree with exact rationals to double rounding."""
+    rng = np.random.default_rng(12)
+    for dtype in ("f16", "bf16"):
+        T, N, H, D, ratio = 3, 9, 4, 16, 2
+        q = synth.to_bits(rng.standard_normal((T, H, D)) / math.sqrt(128), dtype)
+        k = synth.to_bits(rng.standard_normal((N, D)) / math.sqrt(128), dtype)
+        w = rng.random((T, H), dtype=np.float32)
+        pos = np.array([3, 10, 17], dtype=np.int32)
+        _, sc = orc.score_topk(q, k, w, pos, H=H, D=D, dtype=dtype, ratio=ratio, topk=4,
+                               want_scores=True)
+        ex = exact_scores(q, k, w, pos, H, D, dtype, ratio)
+        for t in range(T):
+            for j in range(N):
+                if ex[t][j] is None:
+                    assert sc[t, j] == -math.inf
+                else:
+                    e = float(ex[t][j])
+                    assert abs(sc[t, j] - e) <= 1e-12 * max(1.0, abs(e)), \
+                        f"{dtype} ({t},{j}): {sc[t, j]} vs exact {e}"
+
+
+def pin_bruteforce_selection(orc: Oracle):
+    """Tiny tie-heavy inputs: the oracle's set is the unique subset whose sorted
+    (score desc, row asc) key list is lexicographically largest, over every subset."""
+    rng = np.random.default_rng(13)
+    for trial in range(40):
+        T, N = int(rng.integers(1, 7)), int(rng.integers(0, 13))
+        H, D = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        topk = int(rng.integers(1, 6))
+        ratio = int(rng.integers(1, 4))
+        lo, hi = (-1, 1) if trial % 2 == 0 else (-3, 3)
+        q, k, w, pos = rand_int_case(rng, T, N, H, D, lo, hi, ratio, ratio * N + 2, wexp=1)
+        out = orc.score_topk(q, k, w, pos, H=H, D=D, dtype="f16", ratio=ratio, topk=topk)
+        ex = exact_scores(q, k, w, pos, H, D, "f16", ratio)
+        for t in range(T):
+            vis = [j for j in range(N) if ex[t][j] is not None]
+            m = min(len(vis), topk)
+            best, best_key = None, None
+            for sub in itertools.combinations(vis, m):
+                key = sorted(((ex[t][j], -j) for j in sub), reverse=True)
+                if best_key is None or key > best_key:
+                    best, best_key = sub, key
+            want = sorted(best) + [-1] * (topk - m)
+            assert list(out[t]) == want, f"trial {trial} token {t}: {list(out[t])} != {want}"
+
+
+def pin_closed_forms(orc: Oracle):
+    """Inputs whose answer follows from the definition by hand.
+
+    Rows k[j] = (j+1) e0 (as an exact small integer), one head, q = +-e0:
+      (i)   q = e0,  w = 1  -> s = j+1 increasing      -> rows n-k .. n-1
+      (ii)  q = -e0, w = 1  -> every score is 0         -> rows 0 .. k-1 (ties)
+      (iii) q = e0,  w = -1 -> s = -(j+1) decreasing    -> rows 0 .. k-1
+      (iv)  several heads, only head h* has q = e0 and weight 1, the others
+            have q = -e0 (ReLU zeroes them)            -> same as (i)
+    """
+    N, D, topk, ratio = 40, 3, 7, 4
+    kf = np.zeros((N, D))
+    kf[:, 0] = np.arange(1, N + 1)
+    k = synth.to_bits(kf, "f16")
+    pos = np.array([0, 3, 27, 28, 31, 100, 159, 10_000], dtype=np.int32)
+    T = len(pos)
+    ns = [min((int(p) + 1) // ratio, N) for p in pos]
+    e0 = np.zeros(D)
+    e0[0] = 1
+    for case in ("i", "ii", "iii", "iv"):
+        H = 3 if case == "iv" else 1
+        qf = np.zeros((T, H, D))
+        wv = np.ones((T, H), dtype=np.float32)
+        if case == "i":
+            qf[:, 0] = e0
+        elif case == "ii":
+            qf[:, 0] = -e0
+        elif case == "iii":
+            qf[:, 0] = e0
+            wv[:] = -1
+        else:
+            qf[:, :] = -e0
+            qf[:, 1] = e0
+            wv[:, 0] = 5.0
+            wv[:, 2] = -3.0
+        out = orc.score_topk(synth.to_bits(qf, "f16"), k, wv, pos, H=H, D=D, dtype="f16",
+                             ratio=ratio, topk=topk)
+        for t, n in enumerate(ns):
+            m = min(n, topk)
+            if case in ("i", "iv"):
+                want = list(range(n - m, n))
+            else:
+                want = list(range(m))
+            want += [-1] * (topk - m)
+            assert list(out[t]) == want, f"closed form ({case}) pos {pos[t]}: {list(out[t])} != {want}"
+
+
+def pin_one_head_library(orc: Oracle):
+    """H = 1, w = 1: the result is the top-k of ReLU(K q) under numpy lexsort (score desc, row asc)."""
+    rng = np.random.default_rng(14)
+    N, D, topk = 300, 8, 25
+    q, k, _, _ = rand_int_case(rng, 6, N, 1, D, -2, 2, 1, 1)
+    w = np.ones((6, 1), dtype=np.float32)
+    pos = np.array([5, 20, 24, 25, 150, 299], dtype=np.int32)
+    out = orc.score_topk(q, k, w, pos, H=1, D=D, dtype="f16", ratio=1, topk=topk)
+    kf = k.view(np.float16).astype(np.float64)
+    for t in range(6):
+        n = int(pos[t]) + 1
+        s = np.maximum(kf[:n] @ q[t, 0].view(np.float16).astype(np.float64), 0.0)
+        order = np.lexsort((np.arange(n), -s))
+        m = min(n, topk)
+        want = sorted(order[:m].tolist()) + [-1] * (topk - m)
+        assert list(out[t]) == want, f"one-head token {t}: {list(out[t])} != {want}"
+
+
+def pin_invariants(orc: Oracle):
+    """Output invariants plus dominance, on the tiny workload and random shapes."""
+    rng = np.random.default_rng(15)
+    cases = []
+    d = synth.make("tiny")
+    wl = d["wl"]
+    cases.append((d["q"], d["k"], d["w"], d["pos"], wl.H, wl.D, wl.dtype, wl.ratio, wl.topk))
+    for _ in range(4):
+        T, N, H, D = 9, 70, 3, 5
+        q, k, w, pos = rand_int_case(rng, T, N, H, D, -4, 4, 3, 3 * N + 5)
+        cases.append((q, k, w, pos, H, D, "f16", 3, 16))
+    for q, k, w, pos, H, D, dtype, ratio, topk in cases:
+        out, sc = orc.score_topk(q, k, w, pos, H=H, D=D, dtype=dtype, ratio=ratio, topk=topk,
+                                 want_scores=True)
+        N = k.shape[0]
+        for t in range(len(pos)):
+            n = sum(1 for j in range(N) if ratio * j + ratio - 1 <= int(pos[t]))
+            sel = check_output_row(out[t], n, topk, f"token {t}")
+            rest = [j for j in range(n) if j not in set(sel)]
+            if sel and rest:
+                worst_sel = min((sc[t, j], -j) for j in sel)
+                best_rest = max((sc[t, j], -j) for j in rest)
+                assert worst_sel > best_rest, f"token {t}: dominance violated"
+
+
+def pin_threads_and_subsets(orc: Oracle):
+    """Threads only split tokens; a token subset gives the same rows as the full run."""
+    d = synth.make("tiny")
+    wl = d["wl"]
+    args = dict(H=wl.H, D=wl.D, dtype=wl.dtype, ratio=wl.ratio, topk=wl.topk)
+    full = orc.score_topk(d["q"], d["k"], d["w"], d["pos"], threads=1, **args)
+    par = orc.score_topk(d["q"], d["k"], d["w"], d["pos"], threads=5, **args)
+    assert np.array_equal(full, par), "threaded result differs"
+    toks = np.array([255, 0, 77, 200, 77], dtype=np.int64)
+    sub = orc.score_topk(d["q"], d["k"], d["w"], d["pos"], tokens=toks, threads=2, **args)
+    assert np.array_equal(sub, full[toks]), "token-subset result differs"
+
+
+def pin_empty_and_all_fit(orc: Oracle):
+    """n_t = 0 gives all -1; n_t <= topk gives 0..n_t-1; N = 0 and T = 0 are valid."""
+    rng = np.random.default_rng(16)
+    q, k, w, pos = rand_int_case(rng, 5, 8, 2, 3, -4, 4, 4, 1)
+    pos = np.array([-7, 0, 2, 3, 35], dtype=np.int32)  # n = 0, 0, 0, 1, 8
+    out = orc.score_topk(q, k, w, pos, H=2, D=3, dtype="f16", ratio=4, topk=8)
+    assert [list(r) for r in out] == [[-1] * 8, [-1] * 8, [-1] * 8, [0] + [-1] * 7,
+                                      list(range(8))], f"empty/all-fit: {out}"
+    out0 = orc.score_topk(q, np.zeros((0, 3), np.uint16), w, pos, H=2, D=3, dtype="f16",
+                          ratio=4, topk=3)
+    assert (out0 == -1).all(), "N = 0 must give all -1"
+    outT = orc.score_topk(np.zeros((0, 2, 3), np.uint16), k, np.zeros((0, 2), np.float32),
+                          np.zeros(0, np.int32), H=2, D=3, dtype="f16", ratio=4, topk=3)
+    assert outT.shape == (0, 3)
+
+
+def pin_nonfinite_rejected(orc: Oracle):
+    """Non-finite inputs are refused rather than given a made-up order."""
+    rng = np.random.default_rng(17)
+    q, k, w, pos = rand_int_case(rng, 2, 4, 1, 2, -2, 2, 1, 3)
+    pos[:] = 3
+    bad_q = q.copy()
+    bad_q[1, 0, 1] = 0x7C00  # fp16 +inf
+    bad_k = k.copy()
+    bad_k[2, 0] = 0x7E00     # fp16 NaN
+    bad_w = w.copy()
+    bad_w[0, 0] = np.inf
+    for qq, kk, ww in ((bad_q, k, w), (q, bad_k, w), (q, k, bad_w)):
+        try:
+            orc.score_topk(qq, kk, ww, pos, H=1, D=2, dtype="f16", ratio=1, topk=2)
+        except OracleError:
+            continue
+        raise AssertionError("non-finite input was accepted")
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
+
+
+def run_all(orc: Oracle):
+    """Run every pin; return the list of (name, message) failures."""
+    fails = []
+    for p in PINS:
+        try:
+            p(orc)
+        except Exception as e:  # any exception from a pin counts as that pin failing
+            fails.append((p.__name__, f"{type(e).__name__}: {str(e)[:200]}"))
+    return fails
+
+
+if __name__ == "__main__":
+    fails = run_all(Oracle(sys.argv[1]))
+    for name, msg in fails:
+        print(f"FAIL {name}: {msg}")
+    sys.exit(1 if fails else 0)

@@ -1,0 +1,73 @@
+"""The CPU oracle against its pins (no GPU), and the pins against mutated oracles.
+
+The pins live in oracle_pins.py; each is run here on the real oracle.  The
+mutation test then plants one plausible mistake at a time in a private copy of
+oracle.c (a dropped term, a wrong sign, index or bias, a reversed order, a
+transposed operand), builds it, and requires that at least one pin fails on
+it -- evidence that the pins constrain every part of the definition.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle_pins
+from oracle import oracle as oracle_mod
+
+
+@pytest.fixture(scope="module")
+def orc():
+    if not os.path.exists(oracle_mod.LIB):
+        oracle_mod.build()
+    return oracle_mod.load()
+
+
+@pytest.mark.parametrize("pin", oracle_pins.PINS, ids=lambda p: p.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# (name, text in oracle.c, replacement): each must occur exactly once.
+MUTANTS = [
+    ("score_order_reversed", "if (a->score > b->score)", "if (a->score < b->score)"),
+    ("tie_break_reversed",
+     "if (a->row < b->row)\n        return -1;\n    if (a->row > b->row)\n        return 1;",
+     "if (a->row < b->row)\n        return 1;\n    if (a->row > b->row)\n        return -1;"),
+    ("relu_dropped", "(x > 0.0 ? x : 0.0)", "x"),
+    ("relu_wrong_side", "(x > 0.0 ? x : 0.0)", "(x < 0.0 ? x : 0.0)"),
+    ("weight_dropped", "s += (double)wt[h] *", "s += 1.0 *"),
+    ("first_head_dropped", "for (h = 0; h < H; ++h) {\n                double x",
+     "for (h = 1; h < H; ++h) {\n                double x"),
+    ("k_row_reversed", "x += qt[h * D + d] * kj[d];", "x += qt[h * D + d] * kj[D - 1 - d];"),
+    ("q_transposed", "jb->q[(t * H + h) * D + d]", "jb->q[(t * D + d) * H + h]"),
+    ("q_sign", "qt[h * D + d] = v;", "qt[h * D + d] = -v;"),
+    ("causal_off_by_one", "n = (pos + 1) / ratio;", "n = pos / ratio;"),
+    ("causal_inclusive_partial", "n = (pos + 1) / ratio;", "n = (pos + ratio) / ratio;"),
+    ("output_descending", "return (a > b) - (a < b);", "return (a < b) - (a > b);"),
+    ("pad_zero", "o[c] = c < m ? (int32_t)chosen[c] : -1;", "o[c] = c < m ? (int32_t)chosen[c] : 0;"),
+    ("keeps_one_less", "m = n < jb->topk ? n : jb->topk;", "m = n < jb->topk ? n : jb->topk - 1;"),
+    ("f16_bias", "expo - 25); /*", "expo - 24); /*"),
+    ("f16_subnormal", "ldexp((double)frac, -24);", "ldexp((double)frac, -25);"),
+    ("bf16_bias", "expo - 134); /*", "expo - 133); /*"),
+    ("bf16_frac_bits", "int frac = bits & 0x7F;", "int frac = bits & 0x3F;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(oracle_mod.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "mutant.c")
+        so = os.path.join(tmp, "libmutant.so")
+        with open(c, "w") as f:
+            f.write(src.replace(old, new))
+        oracle_mod.build(out=so, src=c)
+        # a separate process, so that a mutant which misbehaves badly cannot take
+        # the test runner down with it
+        r = subprocess.run([sys.executable, oracle_pins.__file__, so], capture_output=True,
+                           text=True, timeout=300)
+        assert r.returncode == 1, f"mutant {name} passed every pin:\n{r.stdout}{r.stderr}"
+        assert "FAIL" in r.stdout
