@@ -1,0 +1,132 @@
+/*
+ * ds_indexer.h -- C ABI of the MI355X (gfx950) lightning indexer.
+ *
+ * The lightning indexer of DeepSeek V4 sparse attention scores every query
+ * token against the compressed KV rows it can see and keeps the best rows per
+ * token (top 512 in the model) for the sparse attention that follows ("How I
+ * made DeepSeek 12x faster on a Mac Studio", section "1: the kernels").
+ *
+ * For a query token t at absolute position pos[t], with compression ratio r:
+ *
+ *   n_t     = clamp(floor((pos[t] + 1) / r), 0, N)      rows 0..n_t-1 are visible
+ *                                                       (row j covers raw tokens
+ *                                                       r*j .. r*j+r-1)
+ *   s[t,j]  = sum_h  w[t,h] * max(0, q[t,h,:] . k[j,:])  for j < n_t
+ *   out[t]  = the min(n_t, topk) rows with the largest s[t,j] (among equal
+ *             scores the lower row wins), listed in ascending row order and
+ *             padded with -1 up to topk entries.
+ *
+ * A token whose visible rows all fit (n_t <= topk) gets 0 .. n_t-1 without any
+ * scoring ("How I turned one oversized DeepSeek optimization into three merged
+ * oMLX PRs", section "3. Do not rank candidates when every candidate wins").
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the handle's device, dense and
+ *     row-major, owned by the caller; the library never frees or retains them
+ *     beyond the call.  q and k must be 16-byte aligned; w, pos, out, scores
+ *     4-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting: the caller keeps every buffer alive and
+ *     unmodified until the stream reaches that point.  No host synchronisation
+ *     happens inside a call.
+ *   - A handle owns device scratch (the score matrix and selection candidates);
+ *     two calls on one handle must not run concurrently (use one handle per
+ *     concurrently used stream).
+ *   - Errors are returned as status codes (no exceptions, no abort).  Argument
+ *     errors are detected on the host before anything is launched, and leave
+ *     the outputs untouched.  Positions are device data and are not checked:
+ *     the clamp above defines every value (negative => nothing visible).
+ *   - Inputs are assumed finite; for non-finite q, k or w the output is
+ *     unspecified (but the call stays in bounds and terminates).
+ */
+#ifndef DS_INDEXER_H
+#define DS_INDEXER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ds_indexer ds_indexer;
+
+/* element types of q and k */
+enum { DS_F16 = 1, DS_BF16 = 2 };
+
+/* status codes */
+enum {
+    DS_OK = 0,
+    DS_ERR_INVALID_ARG = -1, /* null / misaligned pointer, negative size, topk < 1, ... */
+    DS_ERR_UNSUPPORTED = -2, /* head count / head dim / dtype combination not compiled  */
+    DS_ERR_CAPACITY = -3,    /* T, N or topk above what the handle was created for      */
+    DS_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed              */
+    DS_ERR_OOM = -5          /* device scratch could not be allocated                   */
+};
+
+/*
+ * Create a handle for one device and one problem family.
+ *
+ *   out        receives the handle (set to NULL on failure)
+ *   device     HIP device ordinal
+ *   n_heads    index heads H: 4, 8, 16, 32 or 64
+ *   head_dim   D: 32, 64 or 128
+ *   dtype      DS_F16 or DS_BF16 (type of q and k)
+ *   max_topk   largest topk any call will ask for (1 .. 2048)
+ *   max_tokens largest T of any call (>= 1)
+ *   max_rows   largest N of any call (>= 1)
+ *
+ * Allocates max_tokens * round_up(max_rows, 64) * 4 bytes of score scratch
+ * plus a few MiB of selection scratch on `device`.  Returns DS_OK,
+ * DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_OOM or DS_ERR_HIP.
+ */
+int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, int dtype,
+                      int max_topk, int64_t max_tokens, int64_t max_rows);
+
+/*
+ * Score and select (the operation defined at the top of this file).
+ *
+ *   q      [T][H][D]  dtype   query of every index head of every token
+ *   k      [N][D]     dtype   compressed KV rows, shared by all index heads
+ *   w      [T][H]     float32 per-token head weights
+ *   pos    [T]        int32   absolute position of each query token
+ *   T, N              number of tokens / rows (0 allowed; N = 0 => all -1)
+ *   ratio             compression ratio r >= 1
+ *   topk              rows kept per token, 1 <= topk <= max_topk
+ *   out    [T][topk]  int32   result: ascending selected rows, then -1
+ *   stream            hipStream_t to enqueue on (NULL = null stream)
+ *
+ * T == 1 uses the single-token decode kernels (K streamed once across the
+ * whole GPU, multi-work-group selection); T > 1 uses the prefill kernels.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY or DS_ERR_HIP.
+ */
+int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const float *w,
+                          const int32_t *pos, int64_t T, int64_t N, int ratio, int topk,
+                          int32_t *out, void *stream);
+
+/*
+ * Release the handle and its device scratch.  NULL is accepted and ignored.
+ * Waits for the handle's device to finish outstanding work first.
+ */
+void ds_indexer_destroy(ds_indexer *ix);
+
+/*
+ * Test and inspection helper: the scores s[t,j] themselves, as computed by the
+ * same scorer kernels the selection uses.
+ *
+ *   scores [T][N] float32 (device): s[t,j] for every visible row, -inf for
+ *          every row token t cannot see.
+ * Other arguments as in ds_indexer_score_topk.  Returns DS_OK,
+ * DS_ERR_INVALID_ARG, DS_ERR_CAPACITY or DS_ERR_HIP.
+ */
+int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float *w,
+                      const int32_t *pos, int64_t T, int64_t N, int ratio, float *scores,
+                      void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *ds_indexer_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_INDEXER_H */

@@ -1,0 +1,246 @@
+// api.cpp -- the C ABI of libds_indexer.so: argument checks, device scratch,
+// and the choice between the prefill and the single-token decode kernels.
+// Every step of the computation runs in the HIP kernels of scorer.hip and
+// topk.hip; this file only validates and launches.
+#include "ds_indexer.h"
+#include "internal.hpp"
+
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <new>
+#include <stdint.h>
+
+struct ds_indexer {
+    int device;
+    int H, D, dtype, max_topk;
+    int64_t max_tokens, max_rows;
+    long long ldS;     // row stride of the score scratch (floats)
+    float *S;          // [max_tokens][ldS] scores
+    uint64_t *cand;    // [kDecodeUnion] decode partition candidates
+    int *pcount;       // [decode partitions]
+    uint64_t *pmin;    // [decode partitions]
+    bool decode_ok;    // single-token path available (max_rows small enough)
+};
+
+namespace {
+
+constexpr int kMaxTopk = 2048;
+// single-token path: partitions of kDecodePart rows, at least 16 candidates each
+constexpr int64_t kDecodeMaxRows = (int64_t)dsi::kDecodeUnion / 16 * dsi::kDecodePart;
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess)
+            return;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard()
+    {
+        if (ok && prev >= 0)
+            (void)hipSetDevice(prev);
+    }
+};
+
+bool aligned(const void *p, uintptr_t a)
+{
+    return ((uintptr_t)p % a) == 0;
+}
+
+// candidates kept per decode partition: about twice the k best spread over the
+// partitions, at least 16, and at most what the merge holds
+int decode_kp(int64_t N, int topk)
+{
+    const int64_t P = (N + dsi::kDecodePart - 1) / dsi::kDecodePart;
+    int64_t kp = (2 * (int64_t)topk + P - 1) / P;
+    kp = (kp + 15) / 16 * 16;
+    if (kp < 16)
+        kp = 16;
+    if (kp > topk)
+        kp = topk;
+    if (kp > dsi::kDecodePart)
+        kp = dsi::kDecodePart;
+    if (P * kp > dsi::kDecodeUnion)
+        kp = dsi::kDecodeUnion / P;
+    return (int)kp;
+}
+
+int check_call(const ds_indexer *ix, const void *q, const void *k, const float *w,
+               const int32_t *pos, int64_t T, int64_t N, int ratio, const void *out)
+{
+    if (!ix || T < 0 || N < 0 || ratio < 1)
+        return DS_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !w || !pos || !out))
+        return DS_ERR_INVALID_ARG;
+    if (T > 0 && N > 0 && !k)
+        return DS_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(pos, 4) ||
+        !aligned(out, 4))
+        return DS_ERR_INVALID_ARG;
+    if (T > ix->max_tokens || N > ix->max_rows)
+        return DS_ERR_CAPACITY;
+    return DS_OK;
+}
+
+dsi::Problem problem(const ds_indexer *ix, const void *q, const void *k, const float *w,
+                     const int32_t *pos, int64_t T, int64_t N, int ratio)
+{
+    dsi::Problem p;
+    p.q = q;
+    p.k = k;
+    p.w = w;
+    p.pos = pos;
+    p.T = (int)T;
+    p.N = (int)N;
+    p.ratio = ratio;
+    p.H = ix->H;
+    p.D = ix->D;
+    p.dtype = ix->dtype;
+    return p;
+}
+
+} // namespace
+
+extern "C" {
+
+int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, int dtype,
+                      int max_topk, int64_t max_tokens, int64_t max_rows)
+{
+    if (!out)
+        return DS_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (device < 0 || max_topk < 1 || max_topk > kMaxTopk || max_tokens < 1 || max_rows < 1 ||
+        max_tokens > INT_MAX || max_rows > INT_MAX - 64)
+        return DS_ERR_INVALID_ARG;
+    if (!dsi::scorer_supported(n_heads, head_dim, dtype))
+        return DS_ERR_UNSUPPORTED;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess)
+        return DS_ERR_HIP;
+    if (device >= ndev)
+        return DS_ERR_INVALID_ARG;
+
+    DeviceGuard g(device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    ds_indexer *ix = new (std::nothrow) ds_indexer();
+    if (!ix)
+        return DS_ERR_OOM;
+    ix->device = device;
+    ix->H = n_heads;
+    ix->D = head_dim;
+    ix->dtype = dtype;
+    ix->max_topk = max_topk;
+    ix->max_tokens = max_tokens;
+    ix->max_rows = max_rows;
+    ix->ldS = (max_rows + 63) / 64 * 64;
+    ix->decode_ok = max_rows <= kDecodeMaxRows;
+
+    const size_t s_bytes = (size_t)max_tokens * (size_t)ix->ldS * sizeof(float);
+    const int64_t parts = (max_rows + dsi::kDecodePart - 1) / dsi::kDecodePart;
+    bool ok = hipMalloc((void **)&ix->S, s_bytes) == hipSuccess;
+    if (ok && ix->decode_ok) {
+        ok = hipMalloc((void **)&ix->cand, sizeof(uint64_t) * dsi::kDecodeUnion) == hipSuccess &&
+             hipMalloc((void **)&ix->pcount, sizeof(int) * (size_t)parts) == hipSuccess &&
+             hipMalloc((void **)&ix->pmin, sizeof(uint64_t) * (size_t)parts) == hipSuccess;
+    }
+    if (!ok) {
+        (void)hipGetLastError();
+        hipFree(ix->S);
+        hipFree(ix->cand);
+        hipFree(ix->pcount);
+        hipFree(ix->pmin);
+        delete ix;
+        return DS_ERR_OOM;
+    }
+    *out = ix;
+    return DS_OK;
+}
+
+int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const float *w,
+                          const int32_t *pos, int64_t T, int64_t N, int ratio, int topk,
+                          int32_t *out, void *stream)
+{
+    int st = check_call(ix, q, k, w, pos, T, N, ratio, out);
+    if (st != DS_OK)
+        return st;
+    if (topk < 1)
+        return DS_ERR_INVALID_ARG;
+    if (topk > ix->max_topk)
+        return DS_ERR_CAPACITY;
+    if (T == 0)
+        return DS_OK;
+    DeviceGuard g(ix->device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
+    hipError_t e;
+    if (T == 1 && ix->decode_ok) {
+        e = dsi::launch_decode_scorer(p, topk, ix->S, s);
+        if (e == hipSuccess)
+            e = dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, decode_kp(N, topk),
+                                          ix->cand, ix->pcount, ix->pmin, out, s);
+    } else {
+        e = dsi::launch_prefill_scorer(p, topk, ix->S, ix->ldS, s);
+        if (e == hipSuccess)
+            e = dsi::launch_topk_stream(ix->S, ix->ldS, pos, (int)T, (int)N, ratio, topk, out, s);
+    }
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float *w,
+                      const int32_t *pos, int64_t T, int64_t N, int ratio, float *scores,
+                      void *stream)
+{
+    int st = check_call(ix, q, k, w, pos, T, N, ratio, scores);
+    if (st != DS_OK)
+        return st;
+    if (T == 0 || N == 0)
+        return DS_OK;
+    DeviceGuard g(ix->device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
+    hipError_t e = dsi::launch_fill(scores, T * N, -__builtin_huge_valf(), s);
+    if (e == hipSuccess) {
+        if (T == 1 && ix->decode_ok)
+            e = dsi::launch_decode_scorer(p, 0, scores, s);
+        else
+            e = dsi::launch_prefill_scorer(p, 0, scores, (long long)N, s);
+    }
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+void ds_indexer_destroy(ds_indexer *ix)
+{
+    if (!ix)
+        return;
+    {
+        DeviceGuard g(ix->device);
+        (void)hipDeviceSynchronize();
+        hipFree(ix->S);
+        hipFree(ix->cand);
+        hipFree(ix->pcount);
+        hipFree(ix->pmin);
+    }
+    delete ix;
+}
+
+const char *ds_indexer_status_str(int status)
+{
+    switch (status) {
+    case DS_OK: return "ok";
+    case DS_ERR_INVALID_ARG: return "invalid argument";
+    case DS_ERR_UNSUPPORTED: return "unsupported head count / head dim / dtype";
+    case DS_ERR_CAPACITY: return "problem larger than the handle's capacity";
+    case DS_ERR_HIP: return "HIP runtime error";
+    case DS_ERR_OOM: return "out of device memory";
+    default: return "unknown status";
+    }
+}
+
+} // extern "C"

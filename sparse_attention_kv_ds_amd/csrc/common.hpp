@@ -1,0 +1,115 @@
+// common.hpp -- device helpers shared by the indexer kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsi {
+
+constexpr int kWave = 64;
+
+// element-type tags for q and k
+constexpr int kF16 = 1;
+constexpr int kBF16 = 2;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One 32x32x16 MFMA step, C += A * B, where lane l supplies A row (l % 32)
+// and B column (l % 32), each as 8 consecutive elements of the contraction
+// dimension (16 bytes of raw fp16/bf16 bits).  Both operands use the same
+// lane -> contraction-index assignment, so the sum over the 16 contraction
+// indices is what it should be whatever order the matrix core uses inside.
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (DT == kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                      __builtin_bit_cast(half8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Accumulator layout of a 32x32 MFMA: lane l, register i holds
+// C[row][col] with col = l % 32 and row = 8*(i/4) + 4*(l/32) + i%4.
+__device__ __forceinline__ int acc_row(int i, int lane)
+{
+    return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Number of compressed rows visible from absolute position pos: row j covers
+// raw tokens ratio*j .. ratio*j+ratio-1 and is visible once all of them are.
+__device__ __forceinline__ int visible_rows(int32_t pos, int ratio, int n_rows)
+{
+    if (pos < 0)
+        return 0;
+    long long n = ((long long)pos + 1) / ratio;
+    return n < n_rows ? (int)n : n_rows;
+}
+
+// Unique, totally ordered selection key of (score, row): a larger key is a
+// better row.  High word: the score's bits mapped so that unsigned order is
+// float order (-0 folded onto +0 so equal scores compare equal); low word:
+// ~row, so among equal scores the lower row has the larger key.  Every key of
+// a finite (or -inf) score is > 0, so 0 can stand for "no key".
+__device__ __forceinline__ uint32_t ordered_score(float s)
+{
+    uint32_t b = __float_as_uint(s);
+    if (b == 0x80000000u)
+        b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t row)
+{
+    return ((uint64_t)ordered_score(s) << 32) | (uint64_t)(0xFFFFFFFFu - row);
+}
+
+__device__ __forceinline__ int key_row(uint64_t key)
+{
+    return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p)
+{
+    return __ballot(p);
+}
+
+__device__ __forceinline__ int popc(uint64_t m)
+{
+    return __popcll(m);
+}
+
+// lanes below this one in a mask
+__device__ __forceinline__ int mbcnt(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Order this wave's LDS accesses before/after the point (lanes of one wave
+// read what other lanes of the same wave wrote).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int wave_max(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t readfirstlane(uint32_t v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+} // namespace dsi

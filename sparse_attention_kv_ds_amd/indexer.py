@@ -1,0 +1,181 @@
+"""Thin Python binding of libds_indexer.so (the C ABI in include/ds_indexer.h).
+
+Argument marshalling only: every step of the indexer (scoring, skip path,
+selection) runs in the library's HIP kernels.  torch supplies device memory
+and the current stream.  There is no fallback: if the library is not built,
+importing this module raises.
+
+Functions with the C names take raw integers (device pointers, a stream
+handle); the ``Indexer`` class wraps them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libds_indexer.so")
+
+DS_F16 = 1
+DS_BF16 = 2
+DS_OK = 0
+DS_ERR_INVALID_ARG = -1
+DS_ERR_UNSUPPORTED = -2
+DS_ERR_CAPACITY = -3
+DS_ERR_HIP = -4
+DS_ERR_OOM = -5
+
+EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
+           "ds_indexer_scores", "ds_indexer_status_str")
+
+
+class IndexerError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {ds_indexer_status_str(status)} ({status})" if what
+                         else ds_indexer_status_str(status))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
+                          "the indexer has no non-HIP implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.ds_indexer_create.restype = I
+    lib.ds_indexer_create.argtypes = [ctypes.POINTER(P), I, I, I, I, I, I64, I64]
+    lib.ds_indexer_score_topk.restype = I
+    lib.ds_indexer_score_topk.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P]
+    lib.ds_indexer_destroy.restype = None
+    lib.ds_indexer_destroy.argtypes = [P]
+    lib.ds_indexer_scores.restype = I
+    lib.ds_indexer_scores.argtypes = [P, P, P, P, P, I64, I64, I, P, P]
+    lib.ds_indexer_status_str.restype = ctypes.c_char_p
+    lib.ds_indexer_status_str.argtypes = [I]
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+# --- the C entry points, same names --------------------------------------------------
+
+def ds_indexer_create(device: int, n_heads: int, head_dim: int, dtype: int, max_topk: int,
+                      max_tokens: int, max_rows: int):
+    """Returns (status, handle); handle is None unless status == DS_OK."""
+    h = ctypes.c_void_p()
+    st = _lib.ds_indexer_create(ctypes.byref(h), device, n_heads, head_dim, dtype, max_topk,
+                                max_tokens, max_rows)
+    return st, (h.value if st == DS_OK else None)
+
+
+def ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream) -> int:
+    return _lib.ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream)
+
+
+def ds_indexer_destroy(handle) -> None:
+    _lib.ds_indexer_destroy(handle)
+
+
+def ds_indexer_scores(handle, q, k, w, pos, T, N, ratio, scores, stream) -> int:
+    return _lib.ds_indexer_scores(handle, q, k, w, pos, T, N, ratio, scores, stream)
+
+
+def ds_indexer_status_str(status: int) -> str:
+    return _lib.ds_indexer_status_str(status).decode()
+
+
+# --- torch-facing wrapper -------------------------------------------------------------
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in ("f16", torch.float16, DS_F16):
+        return DS_F16
+    if dtype in ("bf16", torch.bfloat16, DS_BF16):
+        return DS_BF16
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+class Indexer:
+    """One library handle on one device.
+
+    q: [T, H, D] fp16/bf16 (or the raw bits as int16/uint16), k: [N, D] same,
+    w: [T, H] float32, pos: [T] int32, all contiguous on the handle's device.
+    Work is enqueued on torch's current stream of that device.
+    """
+
+    def __init__(self, n_heads: int, head_dim: int, dtype, max_topk: int, max_tokens: int,
+                 max_rows: int, device: int = 0):
+        self.H, self.D = n_heads, head_dim
+        self.dtype = _dtype_code(dtype)
+        self.device = device
+        st, h = ds_indexer_create(device, n_heads, head_dim, self.dtype, max_topk, max_tokens,
+                                  max_rows)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_create")
+        self.handle = h
+
+    def close(self) -> None:
+        if self.handle is not None:
+            ds_indexer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _check(self, q, k, w, pos):
+        import torch
+        dev = torch.device("cuda", self.device)
+        T = pos.shape[0]
+        N = k.shape[0]
+        elem = (torch.float16, torch.bfloat16, torch.int16, torch.uint16)
+        for name, t in (("q", q), ("k", k), ("w", w), ("pos", pos)):
+            if t.device != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+        if q.dtype not in elem or k.dtype not in elem or q.element_size() != 2:
+            raise ValueError("q and k must hold 16-bit elements")
+        if tuple(q.shape) != (T, self.H, self.D) or tuple(k.shape[1:]) != (self.D,):
+            raise ValueError(f"shapes: q {tuple(q.shape)}, k {tuple(k.shape)}")
+        if w.dtype != torch.float32 or tuple(w.shape) != (T, self.H):
+            raise ValueError("w must be float32 [T, H]")
+        if pos.dtype != torch.int32:
+            raise ValueError("pos must be int32 [T]")
+        return T, N, torch.cuda.current_stream(dev).cuda_stream
+
+    def score_topk(self, q, k, w, pos, ratio: int, topk: int, out=None):
+        import torch
+        T, N, stream = self._check(q, k, w, pos)
+        if out is None:
+            out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+        elif (out.dtype != torch.int32 or tuple(out.shape) != (T, topk) or not out.is_contiguous()
+              or out.device != q.device):
+            raise ValueError("out must be a contiguous int32 [T, topk] tensor on q's device")
+        st = ds_indexer_score_topk(self.handle, q.data_ptr(), k.data_ptr(), w.data_ptr(),
+                                   pos.data_ptr(), T, N, ratio, topk, out.data_ptr(), stream)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_score_topk")
+        return out
+
+    def scores(self, q, k, w, pos, ratio: int, out=None):
+        import torch
+        T, N, stream = self._check(q, k, w, pos)
+        if out is None:
+            out = torch.empty((T, N), dtype=torch.float32, device=q.device)
+        st = ds_indexer_scores(self.handle, q.data_ptr(), k.data_ptr(), w.data_ptr(),
+                               pos.data_ptr(), T, N, ratio, out.data_ptr(), stream)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_scores")
+        return out

@@ -1,0 +1,96 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds_indexer.h")
+
+
+@pytest.fixture(scope="module")
+def ix():
+    from sparse_attention_kv_ds_amd import indexer
+    return indexer
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds_indexer_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["ds_indexer_create", "ds_indexer_score_topk",
+                                           "ds_indexer_destroy", "ds_indexer_scores",
+                                           "ds_indexer_status_str"])
+
+
+def test_every_declared_symbol_is_exported(ix):
+    lib = ctypes.CDLL(ix.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    dyn = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ds_indexer_\w+)", dyn))
+    assert exported == set(declared_functions())
+
+
+def test_binding_names_match_the_header(ix):
+    for name in declared_functions():
+        assert callable(getattr(ix, name)), name
+    assert set(ix.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(ix):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = ix.ds_indexer_status_str(code)
+        assert s and s != "unknown status"
+    assert ix.ds_indexer_status_str(12345) == "unknown status"
+
+
+def test_header_constants_match_binding(ix):
+    text = open(HEADER).read()
+    for name in ("DS_F16", "DS_BF16", "DS_OK", "DS_ERR_INVALID_ARG", "DS_ERR_UNSUPPORTED",
+                 "DS_ERR_CAPACITY", "DS_ERR_HIP", "DS_ERR_OOM"):
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+        assert m and int(m.group(1)) == getattr(ix, name), name
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 64, 128, 1, 0, 16, 16), -1),          # max_topk < 1
+    ((0, 64, 128, 1, 4096, 16, 16), -1),       # max_topk too large
+    ((0, 64, 128, 1, 512, 0, 16), -1),         # max_tokens < 1
+    ((0, 64, 128, 1, 512, 16, 0), -1),         # max_rows < 1
+    ((-1, 64, 128, 1, 512, 16, 16), -1),       # device < 0
+    ((0, 48, 128, 1, 512, 16, 16), -2),        # head count not compiled
+    ((0, 64, 96, 1, 512, 16, 16), -2),         # head dim not compiled
+    ((0, 64, 128, 3, 512, 16, 16), -2),        # dtype
+])
+def test_create_rejects_bad_arguments_on_host(ix, args, want):
+    st, h = ix.ds_indexer_create(*args)
+    assert st == want and h is None
+
+
+def test_create_null_out_pointer(ix):
+    lib = ix.library()
+    assert lib.ds_indexer_create(None, 0, 64, 128, 1, 512, 16, 16) == ix.DS_ERR_INVALID_ARG
+
+
+def test_calls_on_null_handle(ix):
+    assert ix.ds_indexer_score_topk(None, 16, 16, 16, 16, 1, 1, 4, 1, 16, None) == -1
+    assert ix.ds_indexer_scores(None, 16, 16, 16, 16, 1, 1, 4, 16, None) == -1
+    ix.ds_indexer_destroy(None)  # accepted and ignored
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "sparse_attention_kv_ds_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b|liboracle|oracle_score",
+                                     text, flags=re.M), f"{f} reaches into the oracle"

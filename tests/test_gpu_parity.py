@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer-valued inputs (q, k integers, w = +-2^-n) make every fp32 sum exact in
+any order, so indices AND scores must match the oracle bit for bit.  Gaussian
+inputs must match scores within 1e-3 relative, and the selected set must agree
+except inside the tie margin around the oracle's k-th best score.  Full-size
+workloads are checked on sampled tokens against the oracle and on every token
+through properties that hold at any size (ascending, unique, causal, all-fit
+sequential, and dominance of the selected rows under the GPU's own scores).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as oracle_mod
+from oracle_pins import check_output_row, rand_int_case
+from sparse_attention_kv_ds_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+REL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_mod.load()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from sparse_attention_kv_ds_amd import indexer
+    return indexer
+
+
+def dev_inputs(q, k, w, pos):
+    return (torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).to(DEV),
+            torch.from_numpy(np.ascontiguousarray(k).view(np.int16)).to(DEV),
+            torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(DEV),
+            torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).to(DEV))
+
+
+def gpu_run(lib, q, k, w, pos, *, H, D, dtype, ratio, topk, scores=False, ix=None):
+    T, N = len(pos), k.shape[0]
+    own = ix is None
+    if own:
+        ix = lib.Indexer(H, D, dtype, max(topk, 1), max(T, 1), max(N, 1), device=0)
+    try:
+        tq, tk, tw, tp = dev_inputs(q, k, w, pos)
+        out = ix.score_topk(tq, tk, tw, tp, ratio, topk)
+        sc = ix.scores(tq, tk, tw, tp, ratio) if scores else None
+        torch.cuda.synchronize(DEV)
+        res = out.cpu().numpy()
+        return (res, sc.cpu().numpy()) if scores else res
+    finally:
+        if own:
+            ix.close()
+
+
+def visible(pos, ratio, N):
+    p = np.asarray(pos, dtype=np.int64)
+    return np.clip(np.where(p < 0, 0, (p + 1) // ratio), 0, N)
+
+
+def ordered_keys(scores_f32, rows):
+    """The unique selection key of (score, row) as uint64, computed on the host."""
+    b = np.ascontiguousarray(scores_f32, dtype=np.float32).view(np.uint32).copy()
+    b[b == 0x80000000] = 0
+    neg = (b & 0x80000000) != 0
+    o = np.where(neg, ~b, b | 0x80000000).astype(np.uint64)
+    return (o << np.uint64(32)) | (np.uint64(0xFFFFFFFF) - rows.astype(np.uint64))
+
+
+def check_all_tokens(out, gscores, pos, ratio, N, topk, where):
+    """Invariants on every token, plus dominance under the GPU's own scores."""
+    ns = visible(pos, ratio, N)
+    for t in range(len(pos)):
+        n = int(ns[t])
+        sel = check_output_row(out[t], n, topk, f"{where} token {t}")
+        if gscores is not None and n > topk:
+            rows = np.arange(n)
+            keys = ordered_keys(gscores[t, :n], rows)
+            mask = np.zeros(n, dtype=bool)
+            mask[sel] = True
+            assert keys[mask].min() > keys[~mask].max(), f"{where} token {t}: dominance"
+
+
+def check_tolerant(out_row, g_row, o_row, n, topk, where):
+    """Scores within REL relative; set agreement outside the tie margin."""
+    m = min(n, topk)
+    sel = check_output_row(out_row, n, topk, where)
+    if n == 0:
+        return
+    g = g_row[:n].astype(np.float64)
+    o = o_row[:n]
+    err = np.abs(g - o)
+    bad = np.nonzero(err > REL * np.abs(o))[0]
+    assert bad.size == 0, f"{where}: score row {bad[0]} gpu {g[bad[0]]} oracle {o[bad[0]]}"
+    if n <= topk:
+        return
+    order = np.lexsort((np.arange(n), -o))
+    tau = o[order[m - 1]]
+    delta = REL * abs(tau)
+    chosen = np.zeros(n, dtype=bool)
+    chosen[sel] = True
+    must = o > tau + delta
+    must_not = o < tau - delta
+    assert chosen[must].all(), f"{where}: a row clearly above the k-th score was dropped"
+    assert not chosen[must_not].any(), f"{where}: a row clearly below the k-th score was kept"
+    assert len(sel) == m
+
+
+def exact_case(lib, orc, q, k, w, pos, *, H, D, dtype, ratio, topk, where, ix=None):
+    out, sc = gpu_run(lib, q, k, w, pos, H=H, D=D, dtype=dtype, ratio=ratio, topk=topk,
+                      scores=True, ix=ix)
+    want, osc = orc.score_topk(q, k, w, pos, H=H, D=D, dtype=dtype, ratio=ratio, topk=topk,
+                               want_scores=True, threads=8)
+    diff = np.argwhere(out != want)
+    assert diff.size == 0, (f"{where}: token {diff[0][0]} got {out[diff[0][0]].tolist()} "
+                            f"want {want[diff[0][0]].tolist()}")
+    np.testing.assert_array_equal(sc.astype(np.float64), osc, err_msg=f"{where}: scores")
+
+
+# ---------------------------------------------------------------------------
+# small and medium shapes, bit-exact
+# ---------------------------------------------------------------------------
+
+def test_tiny_workload_bit_exact(lib, orc):
+    d = synth.make("tiny")
+    wl = d["wl"]
+    say("tiny workload T=256 N=64 H=4 D=32 k=48")
+    exact_case(lib, orc, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+               ratio=wl.ratio, topk=wl.topk, where="tiny")
+    n = visible(d["pos"], wl.ratio, wl.N)
+    assert (n <= wl.topk).sum() == 195 and (n == 0).sum() == 3  # skip-path tokens
+
+
+SHAPES = [
+    # H, D, dtype, topk, T, N, ratio
+    (4, 32, "f16", 48, 300, 257, 4),
+    (4, 64, "bf16", 5, 77, 1100, 1),
+    (8, 32, "f16", 48, 130, 700, 4),
+    (8, 128, "bf16", 100, 64, 1500, 2),
+    (16, 64, "f16", 1, 45, 2100, 3),
+    (16, 128, "f16", 512, 40, 3000, 1),
+    (32, 32, "bf16", 48, 70, 1500, 4),
+    (32, 128, "f16", 512, 33, 2500, 1),
+    (64, 32, "f16", 48, 20, 1025, 1),
+    (64, 64, "bf16", 200, 17, 1999, 1),
+    (64, 128, "f16", 512, 24, 2600, 1),
+    (64, 128, "bf16", 512, 9, 4100, 1),
+    (64, 128, "f16", 1, 10, 3000, 1),
+    (64, 128, "f16", 2048, 12, 5000, 1),
+]
+
+
+@pytest.mark.parametrize("H,D,dtype,topk,T,N,ratio", SHAPES)
+def test_shapes_bit_exact(lib, orc, H, D, dtype, topk, T, N, ratio):
+    say(f"shape H={H} D={D} {dtype} k={topk} T={T} N={N} r={ratio}")
+    rng = np.random.default_rng(1000 + H * 7 + D + T)
+    q, k, w, _ = rand_int_case(rng, T, N, H, D, -4, 4, ratio, 1, dtype)
+    # positions sweep from "nothing visible" through "all fit" to "all rows"
+    pos = np.sort(rng.integers(-3, ratio * (N + 40), size=T)).astype(np.int32)
+    pos[-1] = ratio * N + 5
+    exact_case(lib, orc, q, k, w, pos, H=H, D=D, dtype=dtype, ratio=ratio, topk=topk,
+               where=f"H{H}D{D}{dtype}k{topk}")
+
+
+def test_frontier_sweep_bit_exact(lib, orc):
+    """32 chunk start positions straddling n = 0 and n = topk, as consecutive chunks."""
+    H, D, topk, ratio, N, T = 8, 64, 48, 4, 300, 40
+    starts = sorted(set([-45, -39, -2, 0, 1, 3, 150, 170, 180, 185, 188, 189, 190, 191, 192, 193,
+                         194, 195, 196, 200, 230, 300, 500, 640, 700, 1000, 1150, 1160, 1170,
+                         1180, 1195, 1300]))
+    assert len(starts) == 32
+    rng = np.random.default_rng(7)
+    q, k, w, _ = rand_int_case(rng, T, N, H, D, -4, 4, ratio, 1, "f16")
+    lib_ix = lib.Indexer(H, D, "f16", topk, T, N, device=0)
+    try:
+        for p0 in starts:
+            say(f"frontier p0={p0}")
+            pos = np.arange(p0, p0 + T, dtype=np.int32)
+            exact_case(lib, orc, q, k, w, pos, H=H, D=D, dtype="f16", ratio=ratio, topk=topk,
+                       where=f"frontier {p0}", ix=lib_ix)
+    finally:
+        lib_ix.close()
+
+
+def test_edge_cases(lib, orc):
+    rng = np.random.default_rng(9)
+    H, D = 64, 128
+    q, k, w, _ = rand_int_case(rng, 6, 600, H, D, -4, 4, 4, 1, "f16")
+    ix = lib.Indexer(H, D, "f16", 512, 6, 600, device=0)
+    try:
+        say("edge: N = 0")
+        out = gpu_run(lib, q, k[:0], w, np.array([5, 9, 100, 0, -1, 3], np.int32), H=H, D=D,
+                      dtype="f16", ratio=4, topk=7, ix=ix)
+        assert (out == -1).all()
+        say("edge: T = 0")
+        out = gpu_run(lib, q[:0], k, w[:0], np.zeros(0, np.int32), H=H, D=D, dtype="f16",
+                      ratio=4, topk=7, ix=ix)
+        assert out.shape == (0, 7)
+        say("edge: every token all-fit / empty / negative / beyond N")
+        for pos, ratio, topk in (([0, 1, 2, 3, 4, 2047], 4, 512),
+                                 ([-100, -1, 2, 2**31 - 1, 599, 600], 1, 512),
+                                 ([-100, -1, 2, 2**31 - 1, 599, 600], 1, 3),
+                                 ([127, 128 * 5 - 1, 128 * 600, 10**6, 255, 0], 128, 2),
+                                 ([6, 5, 4, 3, 2, 1], 1, 1)):
+            pos = np.array(pos, dtype=np.int32)
+            exact_case(lib, orc, q, k, w, pos, H=H, D=D, dtype="f16", ratio=ratio, topk=topk,
+                       where=f"edge pos={pos.tolist()} r={ratio} k={topk}", ix=ix)
+        say("edge: all scores equal (ties broken by row)")
+        qz = np.zeros_like(q)
+        exact_case(lib, orc, qz, k, w, np.array([599, 2000, 2399, 9999, 100, 40], np.int32),
+                   H=H, D=D, dtype="f16", ratio=4, topk=17, where="all ties", ix=ix)
+    finally:
+        ix.close()
+
+
+def test_deterministic(lib):
+    d = synth.make("tiny")
+    wl = d["wl"]
+    a = gpu_run(lib, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                ratio=wl.ratio, topk=wl.topk, scores=True)
+    b = gpu_run(lib, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                ratio=wl.ratio, topk=wl.topk, scores=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# single-token decode path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,topk,dtype", [(100, 48, "f16"), (700, 512, "f16"), (1025, 512, "bf16"),
+                                          (5000, 512, "f16"), (70000, 512, "f16"),
+                                          (33000, 2048, "bf16"), (20000, 1, "f16")])
+def test_decode_integer_bit_exact(lib, orc, N, topk, dtype):
+    say(f"decode int N={N} k={topk} {dtype}")
+    rng = np.random.default_rng(N + topk)
+    q, k, w, _ = rand_int_case(rng, 1, N, 64, 128, -4, 4, 4, 1, dtype)
+    for p in (4 * N - 1, 4 * N + 100, 4 * (N // 2) + 1):
+        exact_case(lib, orc, q, k, w, np.array([p], np.int32), H=64, D=128, dtype=dtype, ratio=4,
+                   topk=topk, where=f"decode N={N} pos={p}")
+
+
+def test_decode_fallback_paths_exact(lib, orc):
+    """Scores rising with the row concentrate the best rows in the last partitions
+    (their short candidate lists cannot be trusted), and all-equal scores make
+    every partition's list a pure tie-break; both must stay exact."""
+    N, D, H = 40000, 128, 64
+    rng = np.random.default_rng(3)
+    kf = np.zeros((N, D))
+    kf[:, 0] = np.floor(np.arange(N) / 40)  # non-decreasing, exact in fp16 up to 2048
+    kf[:, 1:] = rng.integers(-1, 2, size=(N, D - 1))
+    k = synth.to_bits(kf, "f16")
+    qf = np.zeros((1, H, D))
+    qf[0, :, 0] = 1
+    w = np.ones((1, H), np.float32)
+    q = synth.to_bits(qf, "f16")
+    for topk in (512, 100):
+        say(f"decode rising scores k={topk}")
+        exact_case(lib, orc, q, k, w, np.array([4 * N - 1], np.int32), H=H, D=D, dtype="f16",
+                   ratio=4, topk=topk, where="decode rising")
+    say("decode all ties")
+    exact_case(lib, orc, np.zeros_like(q), k, w, np.array([4 * N - 1], np.int32), H=H, D=D,
+               dtype="f16", ratio=4, topk=512, where="decode ties")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the launch configuration the benchmark times)
+# ---------------------------------------------------------------------------
+
+def sample_tokens(T, rng, n=40):
+    idx = set(range(8)) | set(range(T - 8, T)) | set(rng.choice(T, size=n - 16, replace=False).tolist())
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["prefill8k", "prefill32k"])
+def test_integer_workloads_full_size(lib, orc, name):
+    say(f"full-size {name}")
+    d = synth.make(name)
+    wl = d["wl"]
+    out, sc = gpu_run(lib, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                      ratio=wl.ratio, topk=wl.topk, scores=True)
+    toks = sample_tokens(wl.T, np.random.default_rng(5))
+    want, osc = orc.score_topk(d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                               ratio=wl.ratio, topk=wl.topk, tokens=toks, want_scores=True,
+                               threads=16)
+    for i, t in enumerate(toks):
+        assert np.array_equal(out[t], want[i]), f"{name} token {t}: indices differ"
+        assert np.array_equal(sc[t].astype(np.float64), osc[i]), f"{name} token {t}: scores differ"
+    check_all_tokens(out, sc, d["pos"], wl.ratio, wl.N, wl.topk, name)
+
+
+def test_gaussian_prefill64k_full_size(lib, orc):
+    say("full-size prefill64k (bf16 gaussian)")
+    d = synth.make("prefill64k")
+    wl = d["wl"]
+    out, sc = gpu_run(lib, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                      ratio=wl.ratio, topk=wl.topk, scores=True)
+    toks = sample_tokens(wl.T, np.random.default_rng(6), n=24)
+    want, osc = orc.score_topk(d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                               ratio=wl.ratio, topk=wl.topk, tokens=toks, want_scores=True,
+                               threads=16)
+    ns = visible(d["pos"], wl.ratio, wl.N)
+    for i, t in enumerate(toks):
+        check_tolerant(out[t], sc[t], osc[i], int(ns[t]), wl.topk, f"64k token {t}")
+    check_all_tokens(out, sc, d["pos"], wl.ratio, wl.N, wl.topk, "64k")
+
+
+def test_decode1m_full_size(lib, orc):
+    say("full-size decode1m (fp16 gaussian, 262144 rows)")
+    d = synth.make("decode1m")
+    wl = d["wl"]
+    out, sc = gpu_run(lib, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                      ratio=wl.ratio, topk=wl.topk, scores=True)
+    want, osc = orc.score_topk(d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                               ratio=wl.ratio, topk=wl.topk, want_scores=True, threads=1)
+    n = int(visible(d["pos"], wl.ratio, wl.N)[0])
+    assert n == 262144
+    check_tolerant(out[0], sc[0], osc[0], n, wl.topk, "decode1m")
+    check_all_tokens(out, sc, d["pos"], wl.ratio, wl.N, wl.topk, "decode1m")
