@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the lightning indexer (score + top-k) on one MI355X.
+
+One step = one ds_indexer_score_topk call over one 2048-token prefill chunk at
+32k context (positions 30720..32767, ratio 4 -> 8192 compressed rows, 64 index
+heads x 128, top-512, fp16 integer-valued synthetic inputs): the scorer
+kernel, the skip path and the streaming top-k.  Inputs are resident in HBM
+before the timed region.  The headline value is scored pairs per second
+(sum over tokens of visible rows / step time); query tokens per second is
+reported beside it.
+
+The same run also times the 64k chunk (bf16 Gaussian, 16384 rows) and the
+single-token decode at the 1M window (262144 rows, 64 MiB of K streamed per
+call, 8 distinct K buffers rotated so every call reads HBM rather than the
+256 MB last-level cache), and times the CPU oracle on a bounded token sample of
+the headline workload.
+
+Per-kernel durations come from HIP events the library records around each of
+its launches on the call's stream (ds_indexer_timing), inside the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --only prefill32k|prefill64k|decode1m   (one workload, for profilers)
+       python bench.py --copy-calibration                       (plain copy kernel, for counters)
+       python bench.py --summarize-pmc DIR                      (fold rocprofv3 counter CSVs)
+       python bench.py --summarize-trace DIR                    (kernel table of a rocprofv3 trace)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer scored pairs/sec + query tokens/sec at 32k/64k context; decode HBM GB/s"
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0                               # MI355X HBM3E
+HEADLINE = "prefill32k"
+SECONDARY = ("prefill64k", "decode1m")
+DECODE_K_BUFFERS = 8
+KERNEL_SOURCES = {  # kernel class -> sources whose change invalidates stored counters
+    "score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
+    "decode_score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(cls: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[cls]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(wl) -> int:
+    import numpy as np
+    p = wl.positions.astype(np.int64)
+    n = np.clip(np.where(p < 0, 0, (p + 1) // wl.ratio), 0, wl.N)
+    return int(n.sum())
+
+
+def upload(d, dev):
+    import numpy as np
+    import torch
+    return (torch.from_numpy(d["q"].view(np.int16)).to(dev),
+            torch.from_numpy(d["k"].view(np.int16)).to(dev),
+            torch.from_numpy(d["w"]).to(dev),
+            torch.from_numpy(d["pos"]).to(dev))
+
+
+def time_workload(name: str, steps: int, warmup: int):
+    """Time `steps` calls of one workload; returns a result dict."""
+    import torch
+    from sparse_attention_kv_ds_amd import synth
+    from sparse_attention_kv_ds_amd.indexer import Indexer
+
+    dev = torch.device("cuda", 0)
+    d = synth.make(name)
+    wl = d["wl"]
+    q, k, w, pos = upload(d, dev)
+    ks = [k]
+    if wl.T == 1:  # decode: rotate distinct K buffers (> last-level cache) so reads hit HBM
+        ks += [torch.roll(k, shifts=997 * (i + 1), dims=0).contiguous()
+               for i in range(DECODE_K_BUFFERS - 1)]
+    out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
+    ix = Indexer(wl.H, wl.D, wl.dtype, wl.topk, wl.T, wl.N, device=0)
+    try:
+        for i in range(warmup):
+            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
+        torch.cuda.synchronize(dev)
+        ix.timing(True)
+        ix.timing_read()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        t0.record()
+        for i in range(steps):
+            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
+        t1.record()
+        torch.cuda.synchronize(dev)
+        ms = t0.elapsed_time(t1) / steps
+        per = ix.timing_read()
+        ix.timing(False)
+    finally:
+        ix.close()
+    kernels = {c: {"avg_ms": v[0] / v[1], "launches": v[1]} for c, v in per.items() if v[1]}
+    pairs = visible_pairs(wl)
+    res = {"workload": name, "ms_per_step": ms, "pairs": pairs, "tokens": wl.T,
+           "pairs_per_s": pairs / (ms * 1e-3), "query_tokens_per_s": wl.T / (ms * 1e-3),
+           "kernels": kernels, "wl": wl}
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step, "
+        + ", ".join(f"{c} {v['avg_ms'] * 1e3:.1f} us" for c, v in kernels.items()))
+    return res
+
+
+def stored_traffic(cls: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if the kernel is unchanged."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f).get(f"{cls}:{workload}")
+    if not rec or rec.get("source_hash") != source_hash(cls):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def roofline(res):
+    wl = res["wl"]
+    if wl.T == 1:
+        cls = "decode_score"
+        t = res["kernels"][cls]["avg_ms"] * 1e-3
+        # K streamed once + q + w + out (algorithmic bytes of one call)
+        algo = wl.N * wl.D * 2 + wl.H * wl.D * 2 + wl.H * 4 + wl.topk * 4
+        ach = algo / t / 1e9
+        return {"bound": "hbm", "kernel": "decode_scorer", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": stored_traffic(cls, res["workload"]),
+                "algorithmic_bytes_per_launch": algo}
+    cls = "score"
+    t = res["kernels"][cls]["avg_ms"] * 1e-3
+    flops = 2.0 * wl.H * wl.D * res["pairs"]
+    ach = flops / t / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    return {"bound": "mfma", "kernel": "prefill_scorer", "achieved": ach, "peak": peak,
+            "unit": "TFLOP/s", "frac": ach / peak, "traffic": stored_traffic(cls, res["workload"]),
+            "algorithmic_flops_per_launch": flops}
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The oracle, as it stands, on a bounded token sample of the same workload."""
+    import numpy as np
+    from oracle import oracle
+    from sparse_attention_kv_ds_amd import synth
+
+    d = synth.make(name)
+    wl = d["wl"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    orc = oracle.load()
+    p = wl.positions.astype(np.int64)
+    n_t = np.clip((p + 1) // wl.ratio, 0, wl.N)
+
+    def run(toks):
+        t = time.perf_counter()
+        orc.score_topk(d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                       ratio=wl.ratio, topk=wl.topk, tokens=toks, threads=cores)
+        return time.perf_counter() - t
+
+    probe = np.linspace(0, wl.T - 1, 2 * cores).astype(np.int64)
+    tp = run(probe)
+    count = int(min(wl.T, max(len(probe), len(probe) * budget_s / max(tp, 1e-3))))
+    toks = np.linspace(0, wl.T - 1, count).astype(np.int64)
+    el = run(toks)
+    pairs = int(n_t[toks].sum())
+    log(f"[bench] cpu oracle: {count} tokens, {pairs} pairs in {el:.2f} s on {cores} threads")
+    return {"value": pairs / el, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "sample": f"{count} of {wl.T} query tokens of {name} (evenly spaced), "
+                      f"{pairs} scored pairs, fp64 scoring + full sort, {el:.1f} s wall"}
+
+
+def copy_calibration(mib: int = 512, reps: int = 3):
+    """A plain device copy of known size, for scaling memory counters."""
+    import torch
+    dev = torch.device("cuda", 0)
+    a = torch.empty(mib * 2**20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize(dev)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4,
+                      "reps": reps}))
+
+
+def summarize_pmc(directory: str):
+    """Average per-dispatch counter values per kernel from rocprofv3 counter CSVs."""
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "?")
+        key = (name, r.get("Counter_Name", "?"))
+        acc.setdefault(key, {})
+        acc[key].setdefault(r.get("Dispatch_Id", "0"), 0.0)
+        acc[key][r.get("Dispatch_Id", "0")] += float(r.get("Counter_Value", 0.0))
+    out = {}
+    for (name, ctr), per in sorted(acc.items()):
+        vals = list(per.values())
+        out.setdefault(name, {})[ctr] = {"dispatches": len(vals), "avg": sum(vals) / len(vals)}
+    print(json.dumps(out, indent=1))
+
+
+def summarize_trace(directory: str):
+    """Per-kernel calls and durations (us) from a rocprofv3 --kernel-trace run
+    (its SQLite database, or its *kernel_stats.csv)."""
+    import sqlite3
+    rows = []
+    for db in glob.glob(os.path.join(directory, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(db)
+        q = ("select name, count(*), sum(duration), avg(duration), min(duration), max(duration), "
+             "max(grid_x), max(grid_y), max(workgroup_x), max(vgpr_count), max(accum_vgpr_count), "
+             "max(lds_size) from kernels group by name")
+        for r in con.execute(q):
+            rows.append((r[0], int(r[1]), r[2] / 1e3, r[3] / 1e3, r[4] / 1e3, r[5] / 1e3,
+                         f"{r[6]}x{r[7]}", r[8], r[9], r[10], r[11]))
+    for path in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
+                             float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                             float(r["MaxNs"]) / 1e3, "", "", "", "", ""))
+    print("| kernel | calls | total us | avg us | min us | max us | grid (threads) | wg | vgpr | agpr | lds B |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -r[2]):
+        print(f"| `{r[0][:100]}` | {r[1]} | {r[2]:.1f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]:.2f} | "
+              f"{r[6]} | {r[7]} | {r[8]} | {r[9]} | {r[10]} |")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc")
+    ap.add_argument("--summarize-trace")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the indexer kernels shard over "
+              "query tokens or rows without any collective; only the 1-GPU path is built); "
+              "use --gpus 1", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    if args.only:
+        res = time_workload(args.only, args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, "ms_per_step": res["ms_per_step"],
+                          "kernels": res["kernels"]}))
+        return 0
+
+    head = time_workload(HEADLINE, args.steps, args.warmup)
+    sec = [time_workload(n, args.steps, args.warmup) for n in SECONDARY]
+    line = {
+        "metric": METRIC,
+        "value": head["pairs_per_s"],
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["wl"].dtype,
+        "data": "synthetic (seeded; integer-valued fp16 q,k, power-of-two w)",
+        "config": {"workload": HEADLINE, "query_tokens": head["wl"].T,
+                   "positions": f"{head['wl'].p0}..{head['wl'].p0 + head['wl'].T - 1}",
+                   "compressed_rows": head["wl"].N, "ratio": head["wl"].ratio,
+                   "index_heads": head["wl"].H, "head_dim": head["wl"].D, "topk": head["wl"].topk,
+                   "scored_pairs_per_step": head["pairs"],
+                   "query_tokens_per_s": head["query_tokens_per_s"], "parallelism": "1 GPU"},
+        "roofline": roofline(head),
+        "kernels_ms": {c: v["avg_ms"] for c, v in head["kernels"].items()},
+        "secondary": [],
+    }
+    for r in sec:
+        wl = r["wl"]
+        entry = {"workload": r["workload"], "dtype": wl.dtype, "ms_per_step": r["ms_per_step"],
+                 "kernels_ms": {c: v["avg_ms"] for c, v in r["kernels"].items()},
+                 "roofline": roofline(r)}
+        if wl.T == 1:
+            rf = entry["roofline"]
+            entry.update({"value": rf["achieved"], "unit": "GB/s (decode scorer, K from HBM)",
+                          "end_to_end_GBps": rf["algorithmic_bytes_per_launch"] / (r["ms_per_step"] * 1e-3) / 1e9})
+        else:
+            entry.update({"value": r["pairs_per_s"], "unit": "pairs/s",
+                          "query_tokens_per_s": r["query_tokens_per_s"]})
+        line["secondary"].append(entry)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(HEADLINE)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -122,6 +122,37 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
                       const int32_t *pos, int64_t T, int64_t N, int ratio, float *scores,
                       void *stream);
 
+/*
+ * Per-kernel timing, for benchmarks and profiling.  While enabled, every kernel
+ * launch a call makes is bracketed by a pair of HIP events recorded on that
+ * call's stream, per class:
+ *   DS_KERNEL_SCORE          prefill scorer           (T > 1)
+ *   DS_KERNEL_SELECT         prefill per-token top-k  (T > 1)
+ *   DS_KERNEL_DECODE_SCORE   single-token scorer      (T == 1)
+ *   DS_KERNEL_DECODE_SELECT  single-token selection   (T == 1; both of its kernels)
+ * The pages' own evidence is end-to-end prompt throughput with bracketing
+ * controls ("How I turned one oversized DeepSeek optimization into three
+ * merged oMLX PRs", section "Turn review feedback into an experiment"); this
+ * splits a call's time into its kernels.
+ *
+ * ds_indexer_timing(ix, enable): enable != 0 starts recording, 0 stops.
+ *   Returns DS_OK or DS_ERR_INVALID_ARG (NULL handle).
+ * ds_indexer_timing_read(ix, ms, launches): waits for every recorded event,
+ *   writes the summed milliseconds and launch counts of each class into
+ *   ms[DS_KERNEL_CLASSES] and launches[DS_KERNEL_CLASSES] (host arrays), and
+ *   clears the record.  Returns DS_OK, DS_ERR_INVALID_ARG or DS_ERR_HIP.
+ */
+enum {
+    DS_KERNEL_SCORE = 0,
+    DS_KERNEL_SELECT = 1,
+    DS_KERNEL_DECODE_SCORE = 2,
+    DS_KERNEL_DECODE_SELECT = 3,
+    DS_KERNEL_CLASSES = 4
+};
+
+int ds_indexer_timing(ds_indexer *ix, int enable);
+int ds_indexer_timing_read(ds_indexer *ix, double *ms, int64_t *launches);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *ds_indexer_status_str(int status);
 

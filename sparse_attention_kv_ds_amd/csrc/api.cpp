@@ -9,6 +9,7 @@
 #include <limits.h>
 #include <new>
 #include <stdint.h>
+#include <vector>
 
 struct ds_indexer {
     int device;
@@ -20,6 +21,14 @@ struct ds_indexer {
     int *pcount;       // [decode partitions]
     uint64_t *pmin;    // [decode partitions]
     bool decode_ok;    // single-token path available (max_rows small enough)
+    // per-kernel timing (ds_indexer_timing)
+    struct Mark {
+        int cls;
+        hipEvent_t a, b;
+    };
+    bool timing = false;
+    std::vector<hipEvent_t> spare;
+    std::vector<Mark> marks;
 };
 
 namespace {
@@ -82,6 +91,40 @@ int check_call(const ds_indexer *ix, const void *q, const void *k, const float *
     if (T > ix->max_tokens || N > ix->max_rows)
         return DS_ERR_CAPACITY;
     return DS_OK;
+}
+
+hipEvent_t take_event(ds_indexer *ix)
+{
+    if (!ix->spare.empty()) {
+        hipEvent_t e = ix->spare.back();
+        ix->spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
+// Runs one launch step, bracketed by events of class `cls` while timing is on.
+template <class F>
+hipError_t timed(ds_indexer *ix, int cls, hipStream_t s, F &&launch)
+{
+    if (!ix->timing)
+        return launch();
+    hipEvent_t a = take_event(ix), b = take_event(ix);
+    if (!a || !b)
+        return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, s);
+    if (e == hipSuccess)
+        e = launch();
+    if (e == hipSuccess)
+        e = hipEventRecord(b, s);
+    if (e != hipSuccess) {
+        ix->spare.push_back(a);
+        ix->spare.push_back(b);
+        return e;
+    }
+    ix->marks.push_back({cls, a, b});
+    return hipSuccess;
 }
 
 dsi::Problem problem(const ds_indexer *ix, const void *q, const void *k, const float *w,
@@ -179,14 +222,22 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
     const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
     hipError_t e;
     if (T == 1 && ix->decode_ok) {
-        e = dsi::launch_decode_scorer(p, topk, ix->S, s);
+        e = timed(ix, DS_KERNEL_DECODE_SCORE, s,
+                  [&] { return dsi::launch_decode_scorer(p, topk, ix->S, s); });
         if (e == hipSuccess)
-            e = dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, decode_kp(N, topk),
-                                          ix->cand, ix->pcount, ix->pmin, out, s);
+            e = timed(ix, DS_KERNEL_DECODE_SELECT, s, [&] {
+                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk,
+                                                 decode_kp(N, topk), ix->cand, ix->pcount,
+                                                 ix->pmin, out, s);
+            });
     } else {
-        e = dsi::launch_prefill_scorer(p, topk, ix->S, ix->ldS, s);
+        e = timed(ix, DS_KERNEL_SCORE, s,
+                  [&] { return dsi::launch_prefill_scorer(p, topk, ix->S, ix->ldS, s); });
         if (e == hipSuccess)
-            e = dsi::launch_topk_stream(ix->S, ix->ldS, pos, (int)T, (int)N, ratio, topk, out, s);
+            e = timed(ix, DS_KERNEL_SELECT, s, [&] {
+                return dsi::launch_topk_stream(ix->S, ix->ldS, pos, (int)T, (int)N, ratio, topk,
+                                               out, s);
+            });
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
@@ -215,6 +266,39 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
+int ds_indexer_timing(ds_indexer *ix, int enable)
+{
+    if (!ix)
+        return DS_ERR_INVALID_ARG;
+    ix->timing = enable != 0;
+    return DS_OK;
+}
+
+int ds_indexer_timing_read(ds_indexer *ix, double *ms, int64_t *launches)
+{
+    if (!ix || !ms || !launches)
+        return DS_ERR_INVALID_ARG;
+    DeviceGuard g(ix->device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    for (int c = 0; c < DS_KERNEL_CLASSES; ++c) {
+        ms[c] = 0.0;
+        launches[c] = 0;
+    }
+    int st = DS_OK;
+    for (const auto &m : ix->marks) {
+        float t = 0.f;
+        if (hipEventSynchronize(m.b) != hipSuccess || hipEventElapsedTime(&t, m.a, m.b) != hipSuccess)
+            st = DS_ERR_HIP;
+        ms[m.cls] += t;
+        launches[m.cls] += 1;
+        ix->spare.push_back(m.a);
+        ix->spare.push_back(m.b);
+    }
+    ix->marks.clear();
+    return st;
+}
+
 void ds_indexer_destroy(ds_indexer *ix)
 {
     if (!ix)
@@ -222,6 +306,12 @@ void ds_indexer_destroy(ds_indexer *ix)
     {
         DeviceGuard g(ix->device);
         (void)hipDeviceSynchronize();
+        for (const auto &m : ix->marks) {
+            (void)hipEventDestroy(m.a);
+            (void)hipEventDestroy(m.b);
+        }
+        for (hipEvent_t e : ix->spare)
+            (void)hipEventDestroy(e);
         hipFree(ix->S);
         hipFree(ix->cand);
         hipFree(ix->pcount);

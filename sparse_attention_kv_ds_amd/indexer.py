@@ -24,9 +24,16 @@ DS_ERR_UNSUPPORTED = -2
 DS_ERR_CAPACITY = -3
 DS_ERR_HIP = -4
 DS_ERR_OOM = -5
+DS_KERNEL_SCORE = 0
+DS_KERNEL_SELECT = 1
+DS_KERNEL_DECODE_SCORE = 2
+DS_KERNEL_DECODE_SELECT = 3
+DS_KERNEL_CLASSES = 4
+KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select")
 
 EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
-           "ds_indexer_scores", "ds_indexer_status_str")
+           "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
+           "ds_indexer_timing_read")
 
 
 class IndexerError(RuntimeError):
@@ -52,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.ds_indexer_scores.argtypes = [P, P, P, P, P, I64, I64, I, P, P]
     lib.ds_indexer_status_str.restype = ctypes.c_char_p
     lib.ds_indexer_status_str.argtypes = [I]
+    lib.ds_indexer_timing.restype = I
+    lib.ds_indexer_timing.argtypes = [P, I]
+    lib.ds_indexer_timing_read.restype = I
+    lib.ds_indexer_timing_read.argtypes = [P, P, P]
     return lib
 
 
@@ -87,6 +98,18 @@ def ds_indexer_scores(handle, q, k, w, pos, T, N, ratio, scores, stream) -> int:
 
 def ds_indexer_status_str(status: int) -> str:
     return _lib.ds_indexer_status_str(status).decode()
+
+
+def ds_indexer_timing(handle, enable: int) -> int:
+    return _lib.ds_indexer_timing(handle, enable)
+
+
+def ds_indexer_timing_read(handle):
+    """Returns (status, ms[4], launches[4]) per kernel class."""
+    ms = (ctypes.c_double * DS_KERNEL_CLASSES)()
+    n = (ctypes.c_int64 * DS_KERNEL_CLASSES)()
+    st = _lib.ds_indexer_timing_read(handle, ms, n)
+    return st, list(ms), list(n)
 
 
 # --- torch-facing wrapper -------------------------------------------------------------
@@ -168,6 +191,18 @@ class Indexer:
         if st != DS_OK:
             raise IndexerError(st, "ds_indexer_score_topk")
         return out
+
+    def timing(self, enable: bool) -> None:
+        st = ds_indexer_timing(self.handle, 1 if enable else 0)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_timing")
+
+    def timing_read(self):
+        """{class name: (total ms, launches)} since the last read."""
+        st, ms, n = ds_indexer_timing_read(self.handle)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_timing_read")
+        return {name: (ms[i], n[i]) for i, name in enumerate(KERNEL_CLASS_NAMES)}
 
     def scores(self, q, k, w, pos, ratio: int, out=None):
         import torch

@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ds_indexer_create", "ds_indexer_score_topk",
                                            "ds_indexer_destroy", "ds_indexer_scores",
-                                           "ds_indexer_status_str"])
+                                           "ds_indexer_status_str", "ds_indexer_timing",
+                                           "ds_indexer_timing_read"])
 
 
 def test_every_declared_symbol_is_exported(ix):
@@ -55,7 +56,9 @@ def test_status_strings(ix):
 def test_header_constants_match_binding(ix):
     text = open(HEADER).read()
     for name in ("DS_F16", "DS_BF16", "DS_OK", "DS_ERR_INVALID_ARG", "DS_ERR_UNSUPPORTED",
-                 "DS_ERR_CAPACITY", "DS_ERR_HIP", "DS_ERR_OOM"):
+                 "DS_ERR_CAPACITY", "DS_ERR_HIP", "DS_ERR_OOM", "DS_KERNEL_SCORE",
+                 "DS_KERNEL_SELECT", "DS_KERNEL_DECODE_SCORE", "DS_KERNEL_DECODE_SELECT",
+                 "DS_KERNEL_CLASSES"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert m and int(m.group(1)) == getattr(ix, name), name
 
@@ -84,6 +87,8 @@ def test_calls_on_null_handle(ix):
     assert ix.ds_indexer_score_topk(None, 16, 16, 16, 16, 1, 1, 4, 1, 16, None) == -1
     assert ix.ds_indexer_scores(None, 16, 16, 16, 16, 1, 1, 4, 16, None) == -1
     ix.ds_indexer_destroy(None)  # accepted and ignored
+    assert ix.ds_indexer_timing(None, 1) == -1
+    assert ix.ds_indexer_timing_read(None)[0] == -1
 
 
 def test_product_path_never_touches_the_oracle():
