@@ -18,6 +18,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libds_indexer.so")
 SOURCES = ["api.cpp", "scorer.hip", "topk.hip"]
+# Extra flags per source.  The scorer is built without NaN semantics: its
+# inputs are finite by contract, and with NaNs honoured every ReLU (fmaxf)
+# costs an extra canonicalising instruction.
+# MFMA accumulators are kept in ordinary VGPRs (the epilogue reads them with
+# VALU instructions; in AGPRs every read would cost an extra move).
+EXTRA = {"scorer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,7 +35,7 @@ FLAGS = [
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

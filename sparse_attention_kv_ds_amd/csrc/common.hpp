@@ -99,6 +99,14 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Work-group barrier that orders LDS only: waits for this wave's LDS accesses,
+// then s_barrier.  Unlike __syncthreads it does not also wait for outstanding
+// global stores, which no other wave of the group reads.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int wave_max(int v)
 {
 #pragma unroll
@@ -110,6 +118,37 @@ __device__ __forceinline__ int wave_max(int v)
 __device__ __forceinline__ uint32_t readfirstlane(uint32_t v)
 {
     return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0 and
+// stores past the end are dropped by the hardware, so bounds become offsets
+// rather than branches.  (gfx9 descriptor word 3.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// an offset past the end of every resource built here (all are < 2 GiB), with
+// headroom so that offset + access size cannot wrap
+constexpr uint32_t kOffNone = 0x80000000u;
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// v + (the same register of lane l ^ 32): one cross-half swap, no LDS traffic
+__device__ __forceinline__ float add_other_half(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 } // namespace dsi

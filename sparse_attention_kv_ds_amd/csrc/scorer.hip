@@ -23,12 +23,18 @@ namespace dsi {
 
 namespace {
 
-constexpr int kPrefillWaves = 8;    // waves per prefill work-group
-constexpr int kChunkRows = 1024;    // compressed rows per prefill work-group
+constexpr int kPrefillWaves = 4;    // waves per prefill work-group
+constexpr int kChunkRows = 2048;    // compressed rows per prefill work-group (multiple of 64)
 
 // ---------------------------------------------------------------------------
 // prefill: blockIdx.x = tile of 64*WAVES (token, head) rows, blockIdx.y = chunk
-// of chunk_rows compressed rows.
+// of chunk_rows compressed rows (a multiple of the 64-row LDS stage).
+//
+// Per 64-row stage: 2 blocks of 32 rows.  Block b's MFMAs and block b-1's
+// epilogue are issued as one branch-free stretch of code, so the VALU work of
+// the epilogue runs while the matrix core is busy.  All bounds are handled by
+// buffer-resource ranges (rows past N read as 0, masked stores are dropped),
+// and the next stage's K loads are in flight during the whole stage.
 // ---------------------------------------------------------------------------
 template <int H, int D, int DT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
@@ -36,16 +42,18 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     const int32_t *__restrict__ pos, int T, int N, int ratio, int min_rows, int chunk_rows,
     float *__restrict__ S, long long ldS)
 {
-    constexpr int TPW = 64 / H;           // tokens per wave
-    constexpr int TPB = TPW * WAVES;      // tokens per work-group
-    constexpr int KS = D / 16;            // MFMA steps along D
-    constexpr int ROWB = D * 2 + 16;      // LDS bytes per K row (16-byte pad against bank conflicts)
-    constexpr int CPR = D / 8;            // 16-byte chunks per K row
-    constexpr int NCH = 32 * CPR;         // 16-byte chunks per 32-row tile
+    constexpr int TPW = 64 / H;       // tokens per wave
+    constexpr int TPB = TPW * WAVES;  // tokens per work-group
+    constexpr int KS = D / 16;        // MFMA steps along D
+    constexpr int SR = 64;            // K rows per LDS stage
+    constexpr int ROWB = D * 2 + 16;  // LDS bytes per K row (16-byte pad: no bank conflicts)
+    constexpr int CPR = D / 8;        // 16-byte chunks per K row
+    constexpr int NCH = SR * CPR;     // 16-byte chunks per stage
     constexpr int NTHR = WAVES * 64;
     constexpr int CPT = (NCH + NTHR - 1) / NTHR;
+    static_assert(NCH % NTHR == 0, "stage must split evenly over the work-group");
 
-    __shared__ __attribute__((aligned(16))) unsigned char kt[2][32 * ROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char kt[2][SR * ROWB];
     __shared__ int s_n[TPB];
 
     const int tid = threadIdx.x;
@@ -71,133 +79,171 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     if (j_chunk >= j_end)
         return; // the same decision in every thread of the work-group
 
-    int wn[TPW];
-    int wnmax = 0;
+    // tokens this lane stores: half-wave hf stores tokens hf, hf+2, ... of the
+    // wave (H >= 8) or tokens 2g + hf of each 8-token tile (H == 4)
+    constexpr int NST = H == 4 ? 8 : (TPW + 1) / 2;
+    int st_n[NST], st_tok[NST];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        wn[i] = s_n[wave * TPW + i];
-        wnmax = max(wnmax, wn[i]);
+    for (int e = 0; e < NST; ++e) {
+        int tk;
+        if constexpr (H == 4)
+            tk = (e >> 2) * 8 + 2 * (e & 3) + hf;
+        else
+            tk = 2 * e + hf;
+        st_tok[e] = wave * TPW + tk;
+        st_n[e] = tk < TPW ? s_n[wave * TPW + tk] : 0;
     }
 
-    // A fragments and head weights of this wave's 64 rows of the flattened Q
-    const long long row0 = (long long)(tok_base + wave * TPW) * H;
-    const long long rows_total = (long long)T * H;
+    const int t_here = min(TPB, T - tok_base);
+    const auto rq = make_rsrc(q + (long long)tok_base * H * D, (uint32_t)t_here * H * D * 2);
+    const auto rk = make_rsrc(k, (uint32_t)N * D * 2);
+    const auto rs = make_rsrc(S + (long long)tok_base * ldS, (uint32_t)(t_here * ldS * 4));
+
+    // A fragments (this wave's 64 rows of the flattened Q) and head weights
     u32x4 a[2][KS];
     float wr[2][16];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const long long r = row0 + mt * 32 + col;
+        const uint32_t r = wave * 64 + mt * 32 + col;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            if (wnmax > 0 && r < rows_total)
-                a[mt][kk] = *reinterpret_cast<const u32x4 *>(q + r * D + kk * 16 + 8 * hf);
-            else
-                a[mt][kk] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int kk = 0; kk < KS; ++kk)
+            a[mt][kk] = buf_load16(rq, (r * D + kk * 16 + 8 * hf) * 2);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const long long rr = row0 + mt * 32 + acc_row(i, lane);
-            wr[mt][i] = (wnmax > 0 && rr < rows_total) ? w[rr] : 0.f;
+            const long long rr = (long long)tok_base * H + wave * 64 + mt * 32 + acc_row(i, lane);
+            wr[mt][i] = rr < (long long)T * H ? w[rr] : 0.f;
         }
     }
 
     u32x4 stage[CPT];
-    auto load_tile = [&](int j0) {
+    auto load_stage = [&](int j0) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int ch = tid + c * NTHR;
-            const int j = j0 + ch / CPR;
-            if (ch < NCH && j < N)
-                stage[c] = *reinterpret_cast<const u32x4 *>(k + (long long)j * D + (ch % CPR) * 8);
-            else
-                stage[c] = u32x4{0u, 0u, 0u, 0u};
+            stage[c] = buf_load16(rk, ((uint32_t)(j0 + ch / CPR) * D + (ch % CPR) * 8) * 2);
         }
     };
-    auto store_tile = [&](int b) {
+    auto store_stage = [&](int b) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int ch = tid + c * NTHR;
-            if (ch < NCH)
-                *reinterpret_cast<u32x4 *>(&kt[b][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[c];
+            *reinterpret_cast<u32x4 *>(&kt[b][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[c];
         }
     };
 
-    load_tile(j_chunk);
-    store_tile(0);
+    // Lane-local partial sums of the epilogue: slot = token of the lane (see
+    // st_tok), two interleaved sums per slot for instruction-level parallelism.
+    constexpr int NSLOT = H == 4 ? 8 : TPW;
+    // accumulator (mt, i) -> slot
+    auto slot_of = [](int mt, int i) constexpr {
+        return H == 4 ? mt * 4 + (i >> 2) : (32 * mt + 8 * (i >> 2)) / H;
+    };
+
+    // ReLU, head weight and sum over each token's heads of the finished block
+    // `e0/e1`, done EPK accumulator registers of each tile at a time so that it
+    // can be spread between the MFMAs of the next block.
+    constexpr int EPK = 16 / KS;
+    auto reduce_part = [&](float (&part)[NSLOT][2], const f32x16 &e0, const f32x16 &e1, int kk) {
+#pragma unroll
+        for (int x = 0; x < EPK; ++x) {
+            const int i = kk * EPK + x;
+            part[slot_of(0, i)][i & 1] = fmaf(wr[0][i], fmaxf(e0[i], 0.f), part[slot_of(0, i)][i & 1]);
+        }
+#pragma unroll
+        for (int x = 0; x < EPK; ++x) {
+            const int i = kk * EPK + x;
+            part[slot_of(1, i)][i & 1] = fmaf(wr[1][i], fmaxf(e1[i], 0.f), part[slot_of(1, i)][i & 1]);
+        }
+    };
+    // finish the head sums and store s[t][jb + col]
+    auto store_part = [&](float (&part)[NSLOT][2], int jb) {
+        const int j = jb + col;
+#pragma unroll
+        for (int e = 0; e < NST; ++e) {
+            float v;
+            if constexpr (H == 4) {
+                v = part[e][0] + part[e][1]; // all 4 heads of the token are in this lane
+            } else {
+                // both half-waves hold a part of every token: add the halves
+                const float v0 = add_other_half(part[2 * e][0] + part[2 * e][1]);
+                v = v0;
+                if constexpr (TPW > 1) {
+                    const float v1 = add_other_half(part[2 * e + 1][0] + part[2 * e + 1][1]);
+                    v = hf ? v1 : v0;
+                }
+            }
+            const bool ok = (unsigned)j < (unsigned)st_n[e];
+            buf_store_f32(rs, ok ? (uint32_t)((st_tok[e] * ldS + j) * 4) : kOffNone, v);
+        }
+    };
+
+    // MFMAs of one 32-row block of K (LDS rows kb[0..31]) into c0/c1, with the
+    // epilogue of the previous block (e0/e1, rows je..je+31) interleaved: each
+    // MFMA is followed by its share of that VALU work, and sched_barrier keeps
+    // the compiler from regrouping them.
+    auto block_step = [&](const unsigned char *kb, f32x16 &c0, f32x16 &c1, const f32x16 &e0,
+                          const f32x16 &e1, int je) {
+        const unsigned char *bp = kb + col * ROWB + hf * 16;
+        float part[NSLOT][2];
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl)
+            part[sl][0] = part[sl][1] = 0.f;
+        c0 = f32x16{};
+        c1 = f32x16{};
+        u32x4 b = *reinterpret_cast<const u32x4 *>(bp);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            u32x4 bn = b;
+            if (kk + 1 < KS)
+                bn = *reinterpret_cast<const u32x4 *>(bp + (kk + 1) * 32);
+            c0 = mfma32<DT>(a[0][kk], b, c0);
+#pragma unroll
+            for (int x = 0; x < EPK; ++x) {
+                const int i = kk * EPK + x;
+                part[slot_of(0, i)][i & 1] =
+                    fmaf(wr[0][i], fmaxf(e0[i], 0.f), part[slot_of(0, i)][i & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            c1 = mfma32<DT>(a[1][kk], b, c1);
+#pragma unroll
+            for (int x = 0; x < EPK; ++x) {
+                const int i = kk * EPK + x;
+                part[slot_of(1, i)][i & 1] =
+                    fmaf(wr[1][i], fmaxf(e1[i], 0.f), part[slot_of(1, i)][i & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            b = bn;
+        }
+        store_part(part, je);
+    };
+
+    load_stage(j_chunk);
+    store_stage(0);
     __syncthreads();
 
+    f32x16 x0, x1, y0 = f32x16{}, y1 = f32x16{};
+    int jy = -(1 << 30); // block held in y (none yet: every store masked)
     int buf = 0;
-    for (int j0 = j_chunk; j0 < j_end; j0 += 32) {
-        const bool more = j0 + 32 < j_end;
-        if (more)
-            load_tile(j0 + 32);
-        if (j0 < wnmax) {
-            f32x16 acc0 = {}, acc1 = {};
-            const unsigned char *bp = &kt[buf][col * ROWB + hf * 16];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const u32x4 b = *reinterpret_cast<const u32x4 *>(bp + kk * 32);
-                acc0 = mfma32<DT>(a[0][kk], b, acc0);
-                acc1 = mfma32<DT>(a[1][kk], b, acc1);
-            }
-            const int j = j0 + col;
-            if constexpr (H >= 8) {
-                // the token of accumulator (mt, i) does not depend on the lane here
-                float part[TPW];
-#pragma unroll
-                for (int tk = 0; tk < TPW; ++tk)
-                    part[tk] = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tk0 = (8 * (i >> 2)) / H;
-                    const int tk1 = (32 + 8 * (i >> 2)) / H;
-                    part[tk0] = fmaf(wr[0][i], fmaxf(acc0[i], 0.f), part[tk0]);
-                    part[tk1] = fmaf(wr[1][i], fmaxf(acc1[i], 0.f), part[tk1]);
-                }
-#pragma unroll
-                for (int tk = 0; tk < TPW; ++tk)
-                    part[tk] += __shfl_xor(part[tk], 32);
-                // half-wave 0 stores even tokens, half-wave 1 odd ones
-#pragma unroll
-                for (int tk = 0; tk < TPW; tk += 2) {
-                    float v = part[tk];
-                    int nn = wn[tk];
-                    if constexpr (TPW > 1) {
-                        if (hf) {
-                            v = part[tk + 1];
-                            nn = wn[tk + 1];
-                        }
-                    } else {
-                        if (hf)
-                            nn = 0;
-                    }
-                    if (j < nn)
-                        S[(long long)(tok_base + wave * TPW + tk + hf) * ldS + j] = v;
-                }
-            } else {
-                // H == 4: token of (mt, i) = mt*8 + 2*(i/4) + half-wave; its 4
-                // heads sit in 4 consecutive registers of one lane
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float v = 0.f;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float x = mt ? acc1[4 * g + e] : acc0[4 * g + e];
-                            v = fmaf(wr[mt][4 * g + e], fmaxf(x, 0.f), v);
-                        }
-                        const int tk = mt * 8 + 2 * g + hf;
-                        if (j < s_n[wave * TPW + tk])
-                            S[(long long)(tok_base + wave * TPW + tk) * ldS + j] = v;
-                    }
-                }
-            }
-        }
-        if (more)
-            store_tile(buf ^ 1);
-        __syncthreads();
+    for (int js = j_chunk; js < j_end; js += SR) {
+        load_stage(js + SR); // past the end of K these read as 0; never used past j_end
+        const unsigned char *kb = kt[buf];
+        block_step(kb, x0, x1, y0, y1, jy);
+        block_step(kb + 32 * ROWB, y0, y1, x0, x1, js);
+        jy = js + 32;
+        store_stage(buf ^ 1);
+        lds_barrier();
         buf ^= 1;
+    }
+    // last block: its epilogue alone
+    {
+        float part[NSLOT][2];
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl)
+            part[sl][0] = part[sl][1] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            reduce_part(part, y0, y1, kk);
+        store_part(part, jy);
     }
 }
 
