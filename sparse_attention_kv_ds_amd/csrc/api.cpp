@@ -58,21 +58,17 @@ bool aligned(const void *p, uintptr_t a)
     return ((uintptr_t)p % a) == 0;
 }
 
-// candidates kept per decode partition: about twice the k best spread over the
-// partitions, at least 16, and at most what the merge holds
+// candidates kept per decode partition (a power of two): at least twice the
+// k best spread evenly over the partitions and at least 16, while the union of
+// all lists still fits the merge
 int decode_kp(int64_t N, int topk)
 {
     const int64_t P = (N + dsi::kDecodePart - 1) / dsi::kDecodePart;
-    int64_t kp = (2 * (int64_t)topk + P - 1) / P;
-    kp = (kp + 15) / 16 * 16;
-    if (kp < 16)
-        kp = 16;
-    if (kp > topk)
-        kp = topk;
-    if (kp > dsi::kDecodePart)
-        kp = dsi::kDecodePart;
-    if (P * kp > dsi::kDecodeUnion)
-        kp = dsi::kDecodeUnion / P;
+    int64_t kp = 16;
+    while (kp * P < 2 * (int64_t)topk && kp < dsi::kDecodePart)
+        kp *= 2;
+    while (kp > 1 && P * kp > dsi::kDecodeUnion)
+        kp /= 2;
     return (int)kp;
 }
 

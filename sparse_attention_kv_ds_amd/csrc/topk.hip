@@ -12,9 +12,10 @@
 // selected set is unique and no tie handling is needed anywhere.  Candidates
 // are appended to an LDS buffer in row order (ballot + mbcnt, no atomics), and
 // every compaction preserves that order, so the survivors come out ascending
-// without a final sort.  When the buffer fills, an exact k-th-key search
-// (bisection over the key bits, counted with ballots) shrinks it back to k
-// keys and raises the threshold.
+// without a final sort.  When the buffer fills, a threshold search shrinks it
+// and raises the running threshold; the final selection finds the exact k-th
+// key: bisection over the score bits until at most 64 candidates remain in the
+// boundary band, then one bitonic sort of that band across the lanes of a wave.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -36,6 +37,49 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     for (int o = 32; o > 0; o >>= 1)
         v = max(v, (uint32_t)__shfl_xor((int)v, o));
     return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m)
+{
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// (the readlane builtins return int: convert through uint32_t so that the low
+// word is never sign-extended into the high one)
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One key per lane, sorted descending across the wave (bitonic network).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t other = shfl_xor64(key, stride);
+            const bool lower = (lane & stride) == 0;
+            const bool desc = (lane & size) == 0; // direction of this lane's run
+            const bool take_max = lower == desc;
+            const uint64_t mx = other > key ? other : key;
+            const uint64_t mn = other > key ? key : other;
+            key = take_max ? mx : mn;
+        }
+    }
+    return key;
 }
 
 // ---------------------------------------------------------------------------
@@ -66,18 +110,48 @@ __device__ __forceinline__ int count_lo_ge(const uint32_t (&hi)[E], const uint32
     return r;
 }
 
-// Reduction of per-wave counts over the work-group: a caller-provided
-// reduction object so the same search code serves one wave or a whole block.
+// ---------------------------------------------------------------------------
+// Reductions over the participants of a selection: one wave, or a whole
+// work-group.  `band_kth` returns the r-th largest (1-based) of the <= 64 keys
+// whose high word lies in [v, u) -- gathered into LDS scratch, sorted by one
+// wave, and the answer made visible to every participant.
+// ---------------------------------------------------------------------------
 struct WaveReduce {
+    uint64_t *scratch; // 64 keys of LDS
     __device__ int sum(int wave_count) { return wave_count; }
     __device__ uint32_t umin(uint32_t v) { return wave_min_u32(v); }
     __device__ uint32_t umax(uint32_t v) { return wave_max_u32(v); }
+
+    template <int E>
+    __device__ uint64_t band_kth(const uint32_t (&hi)[E], const uint32_t (&lo)[E], int nsl,
+                                 uint32_t v, uint64_t u, int r)
+    {
+        const int lane = threadIdx.x & 63;
+        wave_lds_sync();
+        int nb = 0;
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            if (s < nsl) {
+                const bool in = hi[s] >= v && (uint64_t)hi[s] < u;
+                const uint64_t m = ballot(in);
+                if (in)
+                    scratch[nb + mbcnt(m)] = ((uint64_t)hi[s] << 32) | lo[s];
+                nb += popc(m);
+            }
+        }
+        wave_lds_sync();
+        const uint64_t key = lane < nb ? scratch[lane] : 0ull;
+        const uint64_t t = readlane64(wave_sort_desc(key), r - 1);
+        wave_lds_sync();
+        return t;
+    }
 };
 
 template <int NW>
 struct BlockReduce {
-    int *red;        // LDS [2][NW]
-    uint32_t *redu;  // LDS [2][NW]
+    int *red;          // LDS [2][NW]
+    uint32_t *redu;    // LDS [2][NW]
+    uint64_t *scratch; // LDS, 65 keys
     int phase;
     // Double-buffered slots: one barrier per reduction is enough, because a
     // wave can only overwrite a slot after every wave has passed the barrier
@@ -112,24 +186,90 @@ struct BlockReduce {
     }
     __device__ uint32_t umin(uint32_t v) { return ured<true>(v); }
     __device__ uint32_t umax(uint32_t v) { return ured<false>(v); }
+
+    template <int E>
+    __device__ uint64_t band_kth(const uint32_t (&hi)[E], const uint32_t (&lo)[E], int nsl,
+                                 uint32_t v, uint64_t u, int r)
+    {
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        int wc = 0;
+#pragma unroll
+        for (int s = 0; s < E; ++s)
+            if (s < nsl)
+                wc += popc(ballot(hi[s] >= v && (uint64_t)hi[s] < u));
+        if (lane == 0)
+            red[phase * NW + wave] = wc;
+        __syncthreads();
+        int nb = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int c = red[phase * NW + w];
+            nb += w < wave ? c : 0;
+            tot += c;
+        }
+        phase ^= 1;
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            if (s < nsl) {
+                const bool in = hi[s] >= v && (uint64_t)hi[s] < u;
+                const uint64_t m = ballot(in);
+                if (in)
+                    scratch[nb + mbcnt(m)] = ((uint64_t)hi[s] << 32) | lo[s];
+                nb += popc(m);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const uint64_t key = lane < tot ? scratch[lane] : 0ull;
+            const uint64_t t = readlane64(wave_sort_desc(key), r - 1);
+            if (lane == 0)
+                scratch[64] = t;
+        }
+        __syncthreads();
+        const uint64_t t = scratch[64];
+        __syncthreads(); // scratch may be reused right after
+        return t;
+    }
 };
 
-// Exact k-th largest key (1 <= k <= number of keys) among the keys held by the
-// participating lanes.  First the high word by bisection (largest v with at
-// least k keys whose high word is >= v), then, among the keys whose high word
-// is v, the low word the same way -- starting from the bits the candidates
-// have in common.
+// Threshold search over the keys held by the participants (`tot` valid keys,
+// k <= tot).  With slack > 0: returns L with k <= #{keys >= L} <= k + slack
+// (a bound, not necessarily a key).  With slack == 0: returns the k-th
+// largest key itself.
+//
+// Bisection on the high word (the score) keeps [v, u) with at least k keys at
+// or above v and fewer than k at or above u.  It stops early within the slack,
+// or (exact case) once the band [v, u) holds at most 64 keys, which are then
+// sorted.  Only a run of more than 64 equal scores across the boundary needs
+// the low word (the row), bisected from the bits those keys share.
 template <int E, class R>
-__device__ uint64_t kth_key(const uint32_t (&hi)[E], const uint32_t (&lo)[E], int nsl, int k, R &red)
+__device__ uint64_t select_bound(const uint32_t (&hi)[E], const uint32_t (&lo)[E], int nsl,
+                                 int tot, int k, int slack, R &red)
 {
     uint32_t v = 0;
+    uint64_t u = 1ull << 32;
+    int cv = tot; // #{keys with high word >= v}
+    int cu = 0;   // #{keys with high word >= u}
     for (int b = 31; b >= 0; --b) {
+        if (slack > 0 ? cv <= k + slack : cv - cu <= 64)
+            break;
         const uint32_t c = v | (1u << b);
-        if (red.sum(count_hi_ge<E>(hi, nsl, c)) >= k)
+        const int cc = red.sum(count_hi_ge<E>(hi, nsl, c));
+        if (cc >= k) {
             v = c;
+            cv = cc;
+        } else {
+            u = c;
+            cu = cc;
+        }
     }
-    const int ge = red.sum(count_hi_ge<E>(hi, nsl, v));
-    const int gt = v == 0xFFFFFFFFu ? 0 : red.sum(count_hi_ge<E>(hi, nsl, v + 1));
+    if (slack > 0 && cv <= k + slack)
+        return v ? ((uint64_t)v << 32) : 1ull;
+    if (cv - cu <= 64) // (valid keys have a nonzero high word: empty slots stay out of the band)
+        return red.template band_kth<E>(hi, lo, nsl, v ? v : 1u, u, k - cu);
+    // more than 64 equal scores straddle the boundary: rank them by row
+    const int need = k - cu; // here u == v + 1, and >= 2 keys share the high word v
     uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
     for (int s = 0; s < E; ++s)
@@ -139,39 +279,40 @@ __device__ uint64_t kth_key(const uint32_t (&hi)[E], const uint32_t (&lo)[E], in
         }
     lmin = red.umin(lmin);
     lmax = red.umax(lmax);
-    if (ge == k) // every key with high word v is kept; the smallest of them is the k-th
-        return ((uint64_t)v << 32) | lmin;
-    const int need = k - gt;
-    const uint32_t diff = lmin ^ lmax; // two or more distinct keys share v here
-    const int top = 31 - __builtin_clz(diff);
-    uint32_t u = lmax & ~((2u << top) - 1u);
+    const int top = 31 - __builtin_clz(lmin ^ lmax);
+    uint32_t w = lmax & ~((2u << top) - 1u);
     for (int b = top; b >= 0; --b) {
-        const uint32_t c = u | (1u << b);
+        const uint32_t c = w | (1u << b);
         if (red.sum(count_lo_ge<E>(hi, lo, nsl, v, c)) >= need)
-            u = c;
+            w = c;
     }
-    return ((uint64_t)v << 32) | u;
+    return ((uint64_t)v << 32) | w;
 }
 
 // ---------------------------------------------------------------------------
 // One wave's streaming selection state.  Keys enter the LDS buffer when they
-// beat the threshold `tau`; the buffer always holds every key that can still
-// be among the k best, in the order they arrived.
+// beat the threshold; the buffer always holds every key of the wave's stream
+// that can still be among the k best, in the order they arrived.
 // ---------------------------------------------------------------------------
 template <int MAXS>
 struct WaveSelect {
     static constexpr int CAP = MAXS * 64;
     uint64_t *buf; // LDS, CAP keys
     int k;
+    int slack;    // a streaming shrink keeps between k and k + slack keys
     int cnt;      // keys in buf (wave-uniform)
     uint64_t tau; // keys <= tau cannot be among the k best (wave-uniform)
 
-    __device__ void init(uint64_t *b, int kk, uint64_t t0)
+    // requires CAP >= k + 128 (select_slots guarantees more)
+    __device__ void init(uint64_t *b, int kk, uint64_t lower)
     {
         buf = b;
         k = kk;
+        // leave >= 128 free slots after every shrink, so each shrink makes room
+        slack = min(CAP / 4, CAP - 128 - kk);
+        slack = slack > 0 ? slack : 0;
         cnt = 0;
-        tau = t0;
+        tau = lower ? lower - 1 : 0;
     }
 
     // one key per lane (lanes with valid == false offer nothing)
@@ -185,11 +326,13 @@ struct WaveSelect {
             buf[cnt + mbcnt(m)] = key;
         cnt += popc(m);
         if (cnt > CAP - 64)
-            shrink();
+            shrink(slack);
     }
 
-    // keep exactly the k best keys of the buffer (requires cnt > k), in order
-    __device__ void shrink()
+    // keep only the keys >= a bound leaving between k and k + slack of them
+    // (exactly k when slack == 0), in order; the buffer's first 64 slots double
+    // as scratch for the band sort
+    __device__ void shrink(int sl)
     {
         wave_lds_sync();
         const int lane = threadIdx.x & 63;
@@ -204,14 +347,14 @@ struct WaveSelect {
             hi[s] = (uint32_t)(key >> 32);
             lo[s] = (uint32_t)key;
         }
-        WaveReduce red;
-        const uint64_t t = kth_key<MAXS>(hi, lo, nsl, k, red);
+        WaveReduce red{buf};
+        const uint64_t L = uniform64(select_bound<MAXS>(hi, lo, nsl, cnt, k, sl, red));
         int nc = 0;
 #pragma unroll
         for (int s = 0; s < MAXS; ++s) {
             if (s < nsl) {
                 const uint64_t key = ((uint64_t)hi[s] << 32) | lo[s];
-                const bool keep = key >= t;
+                const bool keep = key >= L;
                 const uint64_t m = ballot(keep);
                 if (keep)
                     buf[nc + mbcnt(m)] = key;
@@ -220,20 +363,31 @@ struct WaveSelect {
         }
         wave_lds_sync();
         cnt = nc;
-        tau = t;
+        tau = L - 1;
     }
 
+    // exactly the k best (requires at least k keys), in order
     __device__ void finish()
     {
         if (cnt > k)
-            shrink();
-        else
-            wave_lds_sync();
+            shrink(0);
+        wave_lds_sync();
     }
 };
 
+// smallest per-wave buffer (in 64-key slots) for selecting topk: room for topk,
+// a quarter more, and 128 free slots after a shrink
+int select_slots(int topk)
+{
+    for (int s : {4, 8, 16, 32})
+        if (s * 64 >= topk + topk / 4 + 128)
+            return s;
+    return 64;
+}
+
 // ---------------------------------------------------------------------------
-// prefill: one wave per token over its row S[t][0..n_t)
+// prefill: one wave per token over its row S[t][0..n_t); the next 512 scores
+// are always in flight while the current 512 are pushed.
 // ---------------------------------------------------------------------------
 template <int MAXS>
 __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restrict__ S, long long ldS,
@@ -259,18 +413,27 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
     sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, 0);
     const float *row = S + (long long)t * ldS;
     constexpr int U = 8;
+    float cur[U], nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = u * 64 + lane;
+        cur[u] = j < n ? row[j] : 0.f;
+    }
     for (int base = 0; base < n; base += U * 64) {
-        float v[U];
+        const int nb = base + U * 64;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = base + u * 64 + lane;
-            v[u] = j < n ? row[j] : 0.f;
+            const int j = nb + u * 64 + lane;
+            nxt[u] = j < n ? row[j] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + u * 64 + lane;
-            sel.push(make_key(v[u], (uint32_t)j), j < n);
+            sel.push(make_key(cur[u], (uint32_t)j), j < n);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            cur[u] = nxt[u];
     }
     sel.finish();
     for (int i = lane; i < topk; i += 64)
@@ -282,10 +445,9 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
 // partition lists its exact best kp keys in row order, with the smallest of
 // them (or 0 when the partition has no more than kp rows and lists them all).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int block_exclusive_scan256(int c, int *scan_lds)
+__device__ __forceinline__ int block_exclusive_scan(int c, int *scan)
 {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int inc = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -294,12 +456,12 @@ __device__ __forceinline__ int block_exclusive_scan256(int c, int *scan_lds)
             inc += y;
     }
     if (lane == 63)
-        scan_lds[wave] = inc;
+        scan[wave] = inc;
     __syncthreads();
-    int off = 0;
+    int off = inc - c;
     for (int w = 0; w < wave; ++w)
-        off += scan_lds[w];
-    return off + inc - c;
+        off += scan[w];
+    return off;
 }
 
 __global__ __launch_bounds__(256) void decode_partial_kernel(
@@ -308,7 +470,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 {
     __shared__ int red[2 * 4];
     __shared__ uint32_t redu[2 * 4];
-    __shared__ int scan_lds[4];
+    __shared__ uint64_t scratch[65];
+    __shared__ int scan[4];
     const int n = visible_rows(pos[0], ratio, N);
     if (n <= topk)
         return;
@@ -350,22 +513,22 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         }
         return;
     }
-    BlockReduce<4> br{red, redu, 0};
-    const uint64_t t = kth_key<4>(hi, lo, 4, kp, br);
+    BlockReduce<4> br{red, redu, scratch, 0};
+    const uint64_t L = select_bound<4>(hi, lo, 4, rows, kp, 0, br); // exactly the kp-th key
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        c += (((uint64_t)hi[e] << 32) | lo[e]) >= t;
-    int off = block_exclusive_scan256(c, scan_lds);
+        c += (((uint64_t)hi[e] << 32) | lo[e]) >= L;
+    int off = block_exclusive_scan(c, scan);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const uint64_t key = ((uint64_t)hi[e] << 32) | lo[e];
-        if (key >= t)
+        if (key >= L)
             dst[off++] = key;
     }
     if (tid == 0) {
         pcount[p] = kp;
-        pmin[p] = t;
+        pmin[p] = L;
     }
 }
 
@@ -375,6 +538,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // some partition listed only part of its rows and its smallest listed key is
 // above tU (it may hold unlisted rows above tU).  That case falls back to an
 // exact re-stream of those partitions' rows by one wave.
+// kp is a power of two.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeSlots = kDecodeUnion / kMergeThreads; // 16
@@ -389,6 +553,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     extern __shared__ uint64_t fb_buf[];
     __shared__ int red[2 * NW];
     __shared__ uint32_t redu[2 * NW];
+    __shared__ uint64_t scratch[65];
+    __shared__ int scan[NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -400,32 +566,32 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     }
     const int P = (n + kDecodePart - 1) / kDecodePart;
     const int U = P * kp;
-    const int nsl = (U + kMergeThreads - 1) / kMergeThreads;
+    const int E = (U + kMergeThreads - 1) / kMergeThreads; // <= kMergeSlots
+    const int lgkp = 31 - __builtin_clz(kp);
 
+    // thread i holds union elements [i*E, i*E + E): row order is element order
     uint32_t hi[kMergeSlots], lo[kMergeSlots];
+    int have = 0;
 #pragma unroll
     for (int s = 0; s < kMergeSlots; ++s) {
-        const int e = s * kMergeThreads + tid;
+        const int e = tid * E + s;
         uint64_t key = 0;
-        if (s < nsl && e < U && (e % kp) < pcount[e / kp])
+        if (s < E && e < U && (e & (kp - 1)) < pcount[e >> lgkp])
             key = cand[e];
         hi[s] = (uint32_t)(key >> 32);
         lo[s] = (uint32_t)key;
+        have += key != 0;
     }
-    BlockReduce<NW> br{red, redu, 0};
-    int total = 0;
-    {
-        int wc = 0;
+    BlockReduce<NW> br{red, redu, scratch, 0};
+    int wc = have;
 #pragma unroll
-        for (int s = 0; s < kMergeSlots; ++s)
-            if (s < nsl)
-                wc += popc(ballot(hi[s] != 0));
-        total = br.sum(wc);
-    }
+    for (int o = 32; o > 0; o >>= 1)
+        wc += __shfl_xor(wc, o);
+    const int total = br.sum(wc);
     bool fallback = total < topk;
     uint64_t tU = 0;
     if (!fallback) {
-        tU = kth_key<kMergeSlots>(hi, lo, nsl, topk, br);
+        tU = select_bound<kMergeSlots>(hi, lo, E, total, topk, 0, br); // the k-th key of the union
         bool fail = false;
         for (int p = tid; p < P; p += kMergeThreads) {
             const int rows = min(kDecodePart, n - p * kDecodePart);
@@ -434,38 +600,29 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
         fallback = br.sum(popc(ballot(fail))) > 0;
     }
     if (!fallback) {
-        // ordered compaction of the union's keys >= tU (exactly topk of them)
-        int base = 0;
+        int c = 0;
+#pragma unroll
+        for (int s = 0; s < kMergeSlots; ++s)
+            if (s < E)
+                c += (((uint64_t)hi[s] << 32) | lo[s]) >= tU;
+        int off = block_exclusive_scan(c, scan);
 #pragma unroll
         for (int s = 0; s < kMergeSlots; ++s) {
-            if (s < nsl) {
+            if (s < E) {
                 const uint64_t key = ((uint64_t)hi[s] << 32) | lo[s];
-                const bool keep = key >= tU;
-                const uint64_t m = ballot(keep);
-                if (lane == 0)
-                    red[br.phase * NW + wave] = popc(m);
-                __syncthreads();
-                int woff = 0, tot = 0;
-                for (int w = 0; w < NW; ++w) {
-                    const int c = red[br.phase * NW + w];
-                    woff += w < wave ? c : 0;
-                    tot += c;
-                }
-                br.phase ^= 1;
-                if (keep)
-                    out[base + woff + mbcnt(m)] = key_row(key);
-                base += tot;
+                if (key >= tU)
+                    out[off++] = key_row(key);
             }
         }
         return;
     }
     // exact fallback: one wave re-streams every partition in row order, the
     // listed keys of partitions whose list is known to be enough and all rows
-    // of the others, keeping only keys that can still beat tU
+    // of the others, keeping only keys that can still reach the top k
     if (wave != 0)
         return;
     WaveSelect<MAXS> sel;
-    sel.init(fb_buf, topk, tU ? tU - 1 : 0);
+    sel.init(fb_buf, topk, tU);
     for (int p = 0; p < P; ++p) {
         const int r0 = p * kDecodePart;
         const int rows = min(kDecodePart, n - r0);
@@ -491,20 +648,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
         out[i] = key_row(sel.buf[i]);
 }
 
-// smallest per-wave buffer (in 64-key slots) that leaves room for a full
-// chunk after every shrink and roughly doubles k
-int select_slots(int topk)
-{
-    for (int s : {4, 8, 16, 32, 64})
-        if (s * 64 >= 2 * topk + 64)
-            return s;
-    return 64;
-}
-
 template <int MAXS>
 hipError_t topk_stream_one(const float *S, long long ldS, const int32_t *pos, int T, int N,
                            int ratio, int topk, int32_t *out, hipStream_t st)
 {
+    // waves (tokens) per work-group: 64 KiB of LDS at most
     const int wpb = MAXS >= 64 ? 2 : 4;
     const size_t lds = (size_t)wpb * MAXS * 64 * sizeof(uint64_t);
     hipLaunchKernelGGL((topk_stream_kernel<MAXS>), dim3((T + wpb - 1) / wpb), dim3(wpb * 64), lds,
