@@ -35,7 +35,7 @@ namespace {
 
 constexpr int kMaxTopk = 2048;
 // single-token path: partitions of kDecodePart rows, at least 16 candidates each
-constexpr int64_t kDecodeMaxRows = (int64_t)dsi::kDecodeUnion / 16 * dsi::kDecodePart;
+constexpr int64_t kDecodeMaxRows = (int64_t)dsi::kDecodeMaxParts * dsi::kDecodePart;
 
 struct DeviceGuard {
     int prev = -1;
@@ -218,13 +218,13 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
     const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
     hipError_t e;
     if (T == 1 && ix->decode_ok) {
+        const int kp = decode_kp(N, topk);
         e = timed(ix, DS_KERNEL_DECODE_SCORE, s,
                   [&] { return dsi::launch_decode_scorer(p, topk, ix->S, s); });
         if (e == hipSuccess)
             e = timed(ix, DS_KERNEL_DECODE_SELECT, s, [&] {
-                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk,
-                                                 decode_kp(N, topk), ix->cand, ix->pcount,
-                                                 ix->pmin, out, s);
+                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, kp, ix->cand,
+                                                 ix->pcount, ix->pmin, out, s);
             });
     } else {
         e = timed(ix, DS_KERNEL_SCORE, s,

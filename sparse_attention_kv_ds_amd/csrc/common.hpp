@@ -120,6 +120,13 @@ __device__ __forceinline__ uint32_t readfirstlane(uint32_t v)
     return __builtin_amdgcn_readfirstlane(v);
 }
 
+// This wave's index in the work-group, as a value the compiler knows to be
+// the same in every lane (scalar registers, scalar control flow).
+__device__ __forceinline__ int wave_id()
+{
+    return (int)readfirstlane(threadIdx.x >> 6);
+}
+
 // Buffer resource over [base, base + bytes): loads past the end return 0 and
 // stores past the end are dropped by the hardware, so bounds become offsets
 // rather than branches.  (gfx9 descriptor word 3.)

@@ -16,8 +16,10 @@ struct Problem {
 
 // rows per decode-selection partition
 constexpr int kDecodePart = 1024;
-// largest candidate union the decode merge holds in registers (16 per thread)
+// largest candidate union the decode merge holds in registers (64 per thread)
 constexpr int kDecodeUnion = 16384;
+// most decode partitions: each lists at least 16 candidates
+constexpr int kDecodeMaxParts = kDecodeUnion / 16;
 
 bool scorer_supported(int H, int D, int dtype);
 
@@ -26,7 +28,8 @@ bool scorer_supported(int H, int D, int dtype);
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
                                  hipStream_t st);
 
-// Same for a single token (T == 1): K streamed across the whole GPU.
+// Same for a single token (T == 1): one work-group per kDecodePart-row
+// partition streams K; writes S[j] for j < n.
 hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st);
 
 // Per-token streaming top-k over S rows (one wave per token); skip path for
@@ -34,10 +37,15 @@ hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStr
 hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos, int T, int N,
                               int ratio, int topk, int32_t *out, hipStream_t st);
 
-// Single-token selection over S[0..n): per-partition candidates, then one merge.
+// Single-token selection over S[0..n): each kDecodePart-row partition lists
+// its exact best kp keys (in row order) in cand[p*kp ..], their number in
+// pcount[p] and the smallest of them in pmin[p] (0 when the partition's rows
+// all fit); one work-group then merges the lists into the exact top-k (with an
+// exact re-stream of S for partitions whose list may be short).  kp is a power
+// of two, ceil(N / kDecodePart) * kp <= kDecodeUnion.
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
-                                int kp, uint64_t *cand, int *pcount, uint64_t *pmin,
-                                int32_t *out, hipStream_t st);
+                                int kp, uint64_t *cand, int *pcount, uint64_t *pmin, int32_t *out,
+                                hipStream_t st);
 
 // p[0..n) = v
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st);

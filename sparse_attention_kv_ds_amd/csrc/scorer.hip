@@ -36,7 +36,7 @@ constexpr int kChunkRows = 2048;    // compressed rows per prefill work-group (m
 // buffer-resource ranges (rows past N read as 0, masked stores are dropped),
 // and the next stage's K loads are in flight during the whole stage.
 // ---------------------------------------------------------------------------
-template <int H, int D, int DT, int WAVES>
+template <int H, int D, int DT, int WAVES, int NSTG = 2, int BPF = 1, int SR = 64, int PRIO = 0>
 __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int T, int N, int ratio, int min_rows, int chunk_rows,
@@ -45,15 +45,17 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     constexpr int TPW = 64 / H;       // tokens per wave
     constexpr int TPB = TPW * WAVES;  // tokens per work-group
     constexpr int KS = D / 16;        // MFMA steps along D
-    constexpr int SR = 64;            // K rows per LDS stage
     constexpr int ROWB = D * 2 + 16;  // LDS bytes per K row (16-byte pad: no bank conflicts)
     constexpr int CPR = D / 8;        // 16-byte chunks per K row
     constexpr int NCH = SR * CPR;     // 16-byte chunks per stage
     constexpr int NTHR = WAVES * 64;
     constexpr int CPT = (NCH + NTHR - 1) / NTHR;
     static_assert(NCH % NTHR == 0, "stage must split evenly over the work-group");
+    static_assert(NSTG == 2 || NSTG == 3, "two or three LDS stages");
+    static_assert(BPF == 1 || BPF == 2, "B fragments read one or two steps ahead");
+    static_assert(SR % 64 == 0, "stages of whole pairs of 32-row blocks");
 
-    __shared__ __attribute__((aligned(16))) unsigned char kt[2][SR * ROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char kt[NSTG][SR * ROWB];
     __shared__ int s_n[TPB];
 
     const int tid = threadIdx.x;
@@ -190,12 +192,15 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
             part[sl][0] = part[sl][1] = 0.f;
         c0 = f32x16{};
         c1 = f32x16{};
-        u32x4 b = *reinterpret_cast<const u32x4 *>(bp);
+        u32x4 bq[KS];
+#pragma unroll
+        for (int kk = 0; kk < BPF; ++kk)
+            bq[kk] = *reinterpret_cast<const u32x4 *>(bp + kk * 32);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            u32x4 bn = b;
-            if (kk + 1 < KS)
-                bn = *reinterpret_cast<const u32x4 *>(bp + (kk + 1) * 32);
+            if (kk + BPF < KS)
+                bq[kk + BPF] = *reinterpret_cast<const u32x4 *>(bp + (kk + BPF) * 32);
+            const u32x4 b = bq[kk];
             c0 = mfma32<DT>(a[0][kk], b, c0);
 #pragma unroll
             for (int x = 0; x < EPK; ++x) {
@@ -212,27 +217,57 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
                     fmaf(wr[1][i], fmaxf(e1[i], 0.f), part[slot_of(1, i)][i & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            b = bn;
         }
         store_part(part, je);
     };
 
-    load_stage(j_chunk);
-    store_stage(0);
-    __syncthreads();
-
     f32x16 x0, x1, y0 = f32x16{}, y1 = f32x16{};
     int jy = -(1 << 30); // block held in y (none yet: every store masked)
-    int buf = 0;
-    for (int js = j_chunk; js < j_end; js += SR) {
-        load_stage(js + SR); // past the end of K these read as 0; never used past j_end
-        const unsigned char *kb = kt[buf];
-        block_step(kb, x0, x1, y0, y1, jy);
-        block_step(kb + 32 * ROWB, y0, y1, x0, x1, js);
-        jy = js + 32;
-        store_stage(buf ^ 1);
-        lds_barrier();
-        buf ^= 1;
+    if constexpr (NSTG == 2) {
+        // stage s+1 is loaded into registers during stage s and stored at its end
+        load_stage(j_chunk);
+        store_stage(0);
+        __syncthreads();
+        int buf = 0;
+        for (int js = j_chunk; js < j_end; js += SR) {
+            load_stage(js + SR); // past the end of K these read as 0; never used past j_end
+            const unsigned char *kb = kt[buf];
+            if constexpr (PRIO)
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int pr = 0; pr < SR / 64; ++pr) {
+                block_step(kb + 64 * pr * ROWB, x0, x1, y0, y1, jy);
+                block_step(kb + (64 * pr + 32) * ROWB, y0, y1, x0, x1, js + 64 * pr);
+                jy = js + 64 * pr + 32;
+            }
+            if constexpr (PRIO)
+                __builtin_amdgcn_s_setprio(0);
+            store_stage(buf ^ 1);
+            lds_barrier();
+            buf ^= 1;
+        }
+    } else {
+        // three buffers: stage s+2 is loaded during stage s and stored at the
+        // start of stage s+1, a whole stage after its loads were issued
+        load_stage(j_chunk);
+        store_stage(0);
+        load_stage(j_chunk + SR);
+        __syncthreads();
+        int cur = 0;
+        for (int js = j_chunk; js < j_end; js += SR) {
+            const int nxt = cur == NSTG - 1 ? 0 : cur + 1;
+            store_stage(nxt);         // stage js + SR (loaded one stage ago)
+            load_stage(js + 2 * SR);  // past the end of K these read as 0
+            const unsigned char *kb = kt[cur];
+#pragma unroll
+            for (int pr = 0; pr < SR / 64; ++pr) {
+                block_step(kb + 64 * pr * ROWB, x0, x1, y0, y1, jy);
+                block_step(kb + (64 * pr + 32) * ROWB, y0, y1, x0, x1, js + 64 * pr);
+                jy = js + 64 * pr + 32;
+            }
+            lds_barrier();
+            cur = nxt;
+        }
     }
     // last block: its epilogue alone
     {
@@ -248,83 +283,131 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decode (T == 1): every wave owns the token's H heads (as 64 rows, zero
-// padded) and walks the 32-row blocks of K with a grid-wide stride, loading B
-// fragments straight from global memory one block ahead.
+// decode (T == 1): work-groups of 4 waves, one 32-row block of K per wave.
+// Decode is bound by the K stream.  Each wave fetches its block with loads
+// that each read 1 KiB of consecutive rows and go straight into the wave's
+// LDS staging area (no registers in between), then reads the block back as
+// MFMA B fragments; a per-row XOR swizzle of the 16-byte chunks keeps those
+// fragment reads free of bank conflicts.  (Loading the fragments directly
+// would read 32 bytes from each of 32 rows per instruction, which the memory
+// system serves markedly slower.)  Many small work-groups stream best.  The
+// query and weights are fetched by the whole work-group alongside the first
+// K loads and shared through LDS.  No load waits for pos: K rows past the
+// visible count are fetched and dropped (the caller passes the rows that
+// exist, so at decode nearly all are visible).
 // ---------------------------------------------------------------------------
+constexpr int kDecWaves = 4;
+// K loads marked non-temporal: every byte of K is read once per call
+constexpr int kStreamAux = 2;
+
+// LDS slot (16-byte units) of chunk c of row r in a K staging area of rows of
+// CPR 16-byte chunks: the chunk index is XORed with a function of the row so
+// that the 16 rows read by 16 lanes of one fragment load fall in 16 different
+// bank groups.  The map is its own inverse within a row.
+template <int CPR>
+__device__ __forceinline__ int stage_slot(int r, int c)
+{
+    return r * CPR + (c ^ ((r / (16 / CPR)) % CPR));
+}
+
 template <int H, int D, int DT>
-__global__ __launch_bounds__(256) void decode_scorer_kernel(
+__global__ __launch_bounds__(kDecWaves * 64) void decode_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int N, int ratio, int min_rows, float *__restrict__ S)
 {
     constexpr int KS = D / 16;
     constexpr int MT = H > 32 ? 2 : 1;
-    const int lane = threadIdx.x & 63;
+    constexpr int ROWB = D * 2 + 16;         // LDS bytes per query row (16-byte pad)
+    constexpr int QCH = MT * 32 * (D / 8);   // 16-byte chunks of the padded query
+    constexpr int NT = kDecWaves * 64;
+    constexpr int QPT = (QCH + NT - 1) / NT; // chunks per thread
+    constexpr int CPR = D / 8;               // 16-byte chunks per K row
+    static_assert(32 * CPR == 64 * KS, "one 1 KiB load per MFMA step of a block");
+    __shared__ __attribute__((aligned(16))) unsigned char qs[MT * 32 * ROWB];
+    __shared__ float ws[MT * 32];
+    __shared__ u32x4 kst[kDecWaves * 32 * CPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = wave_id();
     const int col = lane & 31;
     const int hf = lane >> 5;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nw = gridDim.x * 4;
+    const int32_t p0 = pos[0];
+    const int r0 = blockIdx.x * (kDecWaves * 32);
+    const int wrow = r0 + wave * 32;
+    u32x4 *ks = kst + wave * 32 * CPR;
 
-    const int n = visible_rows(pos[0], ratio, N);
-    if (n <= min_rows)
-        return;
-    const int nblk = (n + 31) / 32;
-    if (gw >= nblk)
-        return;
+    // query rows (heads past H read as 0) and weights
+    const auto rq = make_rsrc(q, (uint32_t)(H * D * 2));
+    u32x4 qv[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int c = tid + i * NT;
+        qv[i] = buf_load16(rq, c < QCH ? (uint32_t)c * 16 : kOffNone);
+    }
+    const auto rw = make_rsrc(w, (uint32_t)(H * 4));
+    const float wv = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rw, tid < MT * 32 ? tid * 4 : kOffNone, 0, 0));
+    // this wave's K block into LDS: load i fills slots [64 i, 64 i + 64) lane
+    // by lane, each lane fetching the chunk that belongs in its slot (rows
+    // past N read as 0)
+    const auto rk = make_rsrc(k, (uint32_t)N * D * 2);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        const int g = i * 64 + lane, r = g / CPR;
+        const int c = (g % CPR) ^ ((r / (16 / CPR)) % CPR);
+        const uint32_t off = ((uint32_t)(wrow + r) * CPR + c) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void *)(ks + i * 64), 16, off, 0, 0, kStreamAux);
+    }
 
-    u32x4 a[MT][KS];
+    const int n = visible_rows(p0, ratio, N);
+    if (n <= min_rows || r0 >= n)
+        return; // same for the whole work-group
+
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int c = tid + i * NT;
+        if (c < QCH)
+            *reinterpret_cast<u32x4 *>(&qs[(c / (D / 8)) * ROWB + (c % (D / 8)) * 16]) = qv[i];
+    }
+    if (tid < MT * 32)
+        ws[tid] = wv;
+    lds_barrier();
     float wr[MT][16];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int h = mt * 32 + col;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            a[mt][kk] = h < H ? *reinterpret_cast<const u32x4 *>(q + h * D + kk * 16 + 8 * hf)
-                              : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int hh = mt * 32 + acc_row(i, lane);
-            wr[mt][i] = hh < H ? w[hh] : 0.f;
-        }
-    }
+        for (int i = 0; i < 16; ++i)
+            wr[mt][i] = ws[mt * 32 + acc_row(i, lane)];
 
-    u32x4 b[KS], bn[KS];
-    auto load_b = [&](int blk, u32x4(&dst)[KS]) {
-        const int j = blk * 32 + col;
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): the staged block has landed
+    wave_lds_sync();
+    const unsigned char *ap = qs + col * ROWB + hf * 16;
+    f32x16 acc[MT];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            dst[kk] = j < N ? *reinterpret_cast<const u32x4 *>(k + (long long)j * D + kk * 16 + 8 * hf)
-                            : u32x4{0u, 0u, 0u, 0u};
-    };
-    load_b(gw, b);
-    for (int blk = gw; blk < nblk; blk += nw) {
-        const int nxt = blk + nw;
-        if (nxt < nblk)
-            load_b(nxt, bn);
-        f32x16 acc[MT];
+    for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        const u32x4 bk = ks[stage_slot<CPR>(col, 2 * kk + hf)]; // row col, elements 16 kk + 8 hf ..
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-                acc[mt] = mfma32<DT>(a[mt][kk], b[kk], acc[mt]);
-        }
-        float s = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                s = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), s);
-        s += __shfl_xor(s, 32);
-        const int j = blk * 32 + col;
-        if (hf == 0 && j < n)
-            S[j] = s;
-        if (nxt < nblk) {
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-                b[kk] = bn[kk];
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(ap + mt * 32 * ROWB + kk * 32);
+            acc[mt] = mfma32<DT>(a, bk, acc[mt]);
         }
     }
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            s0 = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), s0);
+            s1 = fmaf(wr[mt][i + 1], fmaxf(acc[mt][i + 1], 0.f), s1);
+        }
+    const float s = add_other_half(s0 + s1);
+    const auto rs = make_rsrc(S, (uint32_t)n * 4);
+    buf_store_f32(rs, hf == 0 ? (uint32_t)(wrow + col) * 4 : kOffNone, s); // rows >= n dropped
 }
 
 __global__ void fill_kernel(float *__restrict__ p, long long n, float v)
@@ -349,11 +432,9 @@ hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, 
 template <int H, int D, int DT>
 hipError_t decode_one(const Problem &p, int min_rows, float *S, hipStream_t st)
 {
-    const int nblk = (p.N + 31) / 32;
-    int blocks = (nblk + 3) / 4;
-    if (blocks > 512)
-        blocks = 512;
-    hipLaunchKernelGGL((decode_scorer_kernel<H, D, DT>), dim3(blocks), dim3(256), 0, st,
+    constexpr int ROWS = kDecWaves * 32; // per work-group
+    hipLaunchKernelGGL((decode_scorer_kernel<H, D, DT>), dim3((p.N + ROWS - 1) / ROWS),
+                       dim3(kDecWaves * 64), 0, st,
                        (const uint16_t *)p.q, (const uint16_t *)p.k, p.w, p.pos, p.N, p.ratio,
                        min_rows, S);
     return hipGetLastError();

@@ -1,0 +1,422 @@
+// select.hpp -- selection primitives shared by the top-k kernels (gfx950).
+//
+// Keys are the unique 64-bit (score, row) keys of common.hpp.  The primitives
+// count keys held in registers with ballots (no atomics), find a threshold by
+// bisection over the score bits, finish the exact k-th key by ranking the
+// <= 64 keys left in the boundary band, and keep a wave's streaming candidate
+// buffer in LDS in arrival (row) order.
+#pragma once
+
+#include "common.hpp"
+
+namespace dsi {
+namespace {
+
+// Wave-wide reductions on the VALU alone (DPP row shuffles, then the gfx950
+// row and half swaps): every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op)
+{
+    v = op(v, dpp<0xB1>(v));  // quad_perm [1,0,3,2]: lane ^ 1
+    v = op(v, dpp<0x4E>(v));  // quad_perm [2,3,0,1]: lane ^ 2
+    v = op(v, dpp<0x141>(v)); // row_half_mirror: the other quad of each 8
+    v = op(v, dpp<0x140>(v)); // row_mirror: the other 8 of each row of 16
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(r[0], r[1]);       // rows 0/1 and 2/3 combined
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(h[0], h[1]);    // the two halves combined
+}
+
+struct OpMin {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct OpMax {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct OpAdd {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    return readfirstlane(wave_reduce(v, OpMin{}));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    return readfirstlane(wave_reduce(v, OpMax{}));
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+    return (int)readfirstlane(wave_reduce((uint32_t)v, OpAdd{}));
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// (the readlane builtins return int: convert through uint32_t so that the low
+// word is never sign-extended into the high one)
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// ---------------------------------------------------------------------------
+// Counting over keys held in registers, split in high/low words.  Empty slots
+// hold key 0, which never counts because every value tested is >= 1.
+// ---------------------------------------------------------------------------
+// Lane masks of x[s] >= c for four slots, computed back to back into four
+// scalar register pairs (written as one block so that the compares are not
+// serialised through a single mask register by the scalar counts after them).
+__device__ __forceinline__ void ge_masks4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                          uint32_t c, uint64_t &m0, uint64_t &m1, uint64_t &m2,
+                                          uint64_t &m3)
+{
+    asm volatile("v_cmp_ge_u32_e64 %0, %4, %8\n\t"
+                 "v_cmp_ge_u32_e64 %1, %5, %8\n\t"
+                 "v_cmp_ge_u32_e64 %2, %6, %8\n\t"
+                 "v_cmp_ge_u32_e64 %3, %7, %8"
+                 : "=&s"(m0), "=&s"(m1), "=&s"(m2), "=&s"(m3) // (written before c is last read)
+                 : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "s"(c));
+}
+
+// #{keys with high word >= c} over all E slots of the wave (empty slots hold
+// 0 and c >= 1, so they never count)
+template <int E>
+__device__ __forceinline__ int count_hi_ge(const uint32_t (&hi)[E], uint32_t c)
+{
+    int r = 0;
+#pragma unroll
+    for (int s = 0; s < E; s += 4) {
+        if (s + 4 <= E) {
+            uint64_t m0, m1, m2, m3;
+            ge_masks4(hi[s], hi[s + 1], hi[s + 2], hi[s + 3], c, m0, m1, m2, m3);
+            r += popc(m0) + popc(m1) + popc(m2) + popc(m3);
+        } else {
+            for (int t = s; t < E; ++t)
+                r += popc(ballot(hi[t] >= c));
+        }
+    }
+    return r;
+}
+
+template <int E, class LO>
+__device__ __forceinline__ int count_lo_ge(const uint32_t (&hi)[E], const LO &lo, uint32_t v,
+                                           uint32_t c)
+{
+    int r = 0;
+#pragma unroll
+    for (int s = 0; s < E; ++s)
+        r += popc(ballot(hi[s] == v && lo[s] >= c));
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions over the participants of a selection: one wave, or a whole
+// work-group.  Every result is the same in all lanes (scalar registers).
+// ---------------------------------------------------------------------------
+struct WaveReduce {
+    __device__ __forceinline__ int sum(int wave_count) { return wave_count; }
+    __device__ __forceinline__ void minmax(uint32_t &mn, uint32_t &mx)
+    {
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+    }
+    __device__ __forceinline__ uint32_t umin(uint32_t v) { return wave_min_u32(v); }
+    __device__ __forceinline__ uint32_t umax(uint32_t v) { return wave_max_u32(v); }
+};
+
+template <int NW>
+struct BlockReduce {
+    static constexpr int kWords = 2 * NW * 2; // LDS ints the caller provides
+    int *red;  // LDS [2][NW][2]
+    int phase; // double-buffered slots: one barrier per reduction is enough,
+               // because a wave can only overwrite a slot after every wave has
+               // passed the barrier of the next reduction, i.e. after every wave
+               // finished reading it
+    __device__ __forceinline__ int *mine() { return red + (phase * NW + wave_id()) * 2; }
+    __device__ __forceinline__ const int *col(int w) const { return red + (phase * NW + w) * 2; }
+
+    __device__ __forceinline__ int sum(int wave_count)
+    {
+        if ((threadIdx.x & 63) == 0)
+            mine()[0] = wave_count;
+        lds_barrier();
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            s += col(w)[0];
+        phase ^= 1;
+        return (int)readfirstlane(s);
+    }
+    __device__ __forceinline__ void minmax(uint32_t &mn, uint32_t &mx)
+    {
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+        if ((threadIdx.x & 63) == 0) {
+            mine()[0] = (int)mn;
+            mine()[1] = (int)mx;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            mn = min(mn, (uint32_t)col(w)[0]);
+            mx = max(mx, (uint32_t)col(w)[1]);
+        }
+        mn = readfirstlane(mn);
+        mx = readfirstlane(mx);
+        phase ^= 1;
+    }
+    template <bool MIN>
+    __device__ __forceinline__ uint32_t ured(uint32_t v)
+    {
+        v = MIN ? wave_min_u32(v) : wave_max_u32(v);
+        if ((threadIdx.x & 63) == 0)
+            mine()[0] = (int)v;
+        lds_barrier();
+        uint32_t r = (uint32_t)col(0)[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            r = MIN ? min(r, (uint32_t)col(w)[0]) : max(r, (uint32_t)col(w)[0]);
+        phase ^= 1;
+        return readfirstlane(r);
+    }
+    __device__ __forceinline__ uint32_t umin(uint32_t v) { return ured<true>(v); }
+    __device__ __forceinline__ uint32_t umax(uint32_t v) { return ured<false>(v); }
+};
+
+// The largest (MAX) or smallest key whose high word lies in [v, u), v >= 1.
+template <bool MAX, int E, class LO, class R>
+__device__ __forceinline__ uint64_t band_extreme(const uint32_t (&hi)[E], const LO &lo, uint32_t v,
+                                                 uint64_t u, R &red)
+{
+    uint32_t h = MAX ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+    for (int s = 0; s < E; ++s)
+        if (hi[s] >= v && (uint64_t)hi[s] < u)
+            h = MAX ? max(h, hi[s]) : min(h, hi[s]);
+    h = MAX ? red.umax(h) : red.umin(h);
+    uint32_t l = MAX ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+    for (int s = 0; s < E; ++s)
+        if (hi[s] == h)
+            l = MAX ? max(l, (uint32_t)lo[s]) : min(l, (uint32_t)lo[s]);
+    l = MAX ? red.umax(l) : red.umin(l);
+    return ((uint64_t)h << 32) | l;
+}
+
+// Threshold search over the keys held by the participants (`tot` valid keys,
+// k <= tot; empty slots hold key 0).  With slack > 0: returns L with
+// k <= #{keys >= L} <= k + slack (a bound, not necessarily a key).  With
+// slack == 0: returns the k-th largest key itself.
+//
+// The search starts from the bits that the smallest and largest high words
+// (scores) share, then bisects the high word keeping [v, u) with at least k
+// keys at or above v and fewer than k at or above u.  It stops early within
+// the slack, or (exact case) as soon as the k-th key is the largest or the
+// smallest of the band [v, u), which one reduction then finds.  Only equal
+// scores across the boundary need the low word (the row), bisected from the
+// bits those keys share.
+template <int E, class LO, class R>
+__device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const LO &lo, int tot,
+                                                int k, int slack, R &red)
+{
+    if (slack > 0 && tot <= k + slack)
+        return 1ull;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int s = 0; s < E; ++s)
+        if (hi[s] != 0u) {
+            mn = min(mn, hi[s]);
+            mx = max(mx, hi[s]);
+        }
+    red.minmax(mn, mx);
+    // every key's high word is in [v, u), v <= mn, mx < u
+    const int top = mn == mx ? -1 : 31 - __builtin_clz(mn ^ mx);
+    const uint32_t span = top < 0 ? 1u : (2u << top); // 0 when top == 31 (whole range)
+    const uint32_t v0 = top < 0 ? mn : (mn & ~(span - 1u));
+    uint32_t v = v0;
+    uint64_t u = (uint64_t)v0 + (span ? span : (1ull << 32));
+    int cv = tot; // #{keys with high word >= v}
+    int cu = 0;   // #{keys with high word >= u}
+#pragma unroll 1
+    for (int b = top; b >= 0; --b) {
+        if (slack > 0 ? cv <= k + slack : (k - cu == 1 || k == cv))
+            break;
+        const uint32_t c = v | (1u << b);
+        const int cc = red.sum(count_hi_ge<E>(hi, c));
+        if (cc >= k) {
+            v = c;
+            cv = cc;
+        } else {
+            u = c;
+            cu = cc;
+        }
+    }
+    if (slack > 0 && cv <= k + slack)
+        return (uint64_t)v << 32; // v >= mn >= 1
+    const uint32_t vb = v ? v : 1u; // (empty slots stay out of the band)
+    if (k - cu == 1) // the k-th key is the largest in the band
+        return band_extreme<true>(hi, lo, vb, u, red);
+    if (k == cv) // ... or the smallest
+        return band_extreme<false>(hi, lo, vb, u, red);
+    // equal scores straddle the boundary: rank them by row
+    const int need = k - cu; // here u == v + 1, and >= 3 keys share the high word v
+    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+#pragma unroll
+    for (int s = 0; s < E; ++s)
+        if (hi[s] == v) {
+            lmin = min(lmin, (uint32_t)lo[s]);
+            lmax = max(lmax, (uint32_t)lo[s]);
+        }
+    red.minmax(lmin, lmax);
+    const int ltop = 31 - __builtin_clz(lmin ^ lmax);
+    uint32_t w = lmax & ~((2u << ltop) - 1u);
+#pragma unroll 1
+    for (int b = ltop; b >= 0; --b) {
+        const uint32_t c = w | (1u << b);
+        if (red.sum(count_lo_ge<E, LO>(hi, lo, v, c)) >= need)
+            w = c;
+    }
+    return ((uint64_t)v << 32) | w;
+}
+
+// Low words of a wave's LDS key buffer, read on demand: slot s of this lane,
+// at a constant offset from the lane's first key.
+struct LdsLow {
+    const uint64_t *mine; // buf + lane
+    __device__ uint32_t operator[](int s) const { return (uint32_t)mine[s * 64]; }
+};
+
+template <int MAXS>
+struct WaveSelect {
+    static constexpr int CAP = MAXS * 64;
+    // the largest buffers keep only the high words in registers during a
+    // shrink and read the low words from LDS where a decision needs them
+    static constexpr bool kLowInLds = MAXS > 32;
+    uint64_t *buf; // LDS, CAP keys
+    int k;
+    int slack;    // a streaming shrink keeps between k and k + slack keys
+    int cnt;      // keys in buf (wave-uniform)
+    uint64_t tau; // keys <= tau cannot be among the k best (wave-uniform)
+
+    // requires CAP >= k + 128 (select_slots guarantees more)
+    __device__ __forceinline__ void init(uint64_t *b, int kk, uint64_t lower)
+    {
+        buf = b;
+        k = kk;
+        // leave >= 128 free slots after every shrink, so each shrink makes room
+        slack = min(CAP / 4, CAP - 128 - kk);
+        slack = slack > 0 ? slack : 0;
+        cnt = 0;
+        tau = lower ? lower - 1 : 0;
+    }
+
+    // one key per lane (lanes with valid == false offer nothing)
+    __device__ __forceinline__ void push(uint64_t key, bool valid)
+    {
+        const bool pass = valid && key > tau;
+        const uint64_t m = ballot(pass);
+        if (m == 0)
+            return;
+        if (pass)
+            buf[cnt + mbcnt(m)] = key;
+        cnt += popc(m);
+        if (cnt > CAP - 64)
+            shrink(slack);
+    }
+
+    // keep only the keys >= a bound leaving between k and k + slack of them
+    // (exactly k when slack == 0), in order.  The compaction is in place: a
+    // kept key moves to an index no larger than its own, and one wave's LDS
+    // accesses stay in program order.
+    __device__ __forceinline__ void shrink(int sl)
+    {
+        wave_lds_sync();
+        const int lane = threadIdx.x & 63;
+        const int nsl = (cnt + 63) >> 6;
+        uint32_t hi[MAXS];
+        uint32_t lo_r[kLowInLds ? 1 : MAXS];
+        const uint64_t *mine = buf + lane; // slot s at constant offset s * 64
+        const int rem = cnt - lane;        // slot s holds a key iff s * 64 < rem
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            uint64_t key = 0;
+            if (s * 64 < rem)
+                key = mine[s * 64];
+            hi[s] = (uint32_t)(key >> 32);
+            if constexpr (!kLowInLds)
+                lo_r[s] = (uint32_t)key;
+        }
+        WaveReduce red;
+        uint64_t L;
+        // (every slot is looked at: empty ones hold key 0, which never counts)
+        if constexpr (kLowInLds)
+            L = uniform64(select_bound<MAXS>(hi, LdsLow{mine}, cnt, k, sl, red));
+        else
+            L = uniform64(select_bound<MAXS>(hi, lo_r, cnt, k, sl, red));
+        int nc = 0;
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            if (s < nsl) {
+                uint32_t lw;
+                if constexpr (kLowInLds)
+                    lw = (uint32_t)mine[s * 64];
+                else
+                    lw = lo_r[s];
+                const uint64_t key = ((uint64_t)hi[s] << 32) | lw;
+                const bool keep = hi[s] != 0u && key >= L; // (hi == 0: no key)
+                const uint64_t m = ballot(keep);
+                if (keep)
+                    buf[nc + mbcnt(m)] = key;
+                nc += popc(m);
+            }
+        }
+        wave_lds_sync();
+        cnt = nc;
+        tau = L - 1;
+    }
+
+    // exactly the k best (requires at least k keys), in order
+    __device__ __forceinline__ void finish()
+    {
+        if (cnt > k)
+            shrink(0);
+        wave_lds_sync();
+    }
+};
+
+__device__ __forceinline__ int block_exclusive_scan(int c, int *scan)
+{
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o)
+            inc += y;
+    }
+    if (lane == 63)
+        scan[wave] = inc;
+    __syncthreads();
+    int off = inc - c;
+    for (int w = 0; w < wave; ++w)
+        off += scan[w];
+    return off;
+}
+
+} // namespace
+} // namespace dsi
