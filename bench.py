@@ -15,14 +15,19 @@ call, 8 distinct K buffers rotated so every call reads HBM rather than the
 256 MB last-level cache), and times the CPU oracle on a bounded token sample of
 the headline workload.
 
-Per-kernel durations come from HIP events the library records around each of
-its launches on the call's stream (ds_indexer_timing), inside the timed region.
+The step time is taken over K calls with nothing else on the stream.  The
+per-kernel durations come from a second timed pass of K calls in which the
+library records HIP events around each of its launches on the call's stream
+(ds_indexer_timing); those markers themselves leave the GPU idle between
+kernels, so that pass's step time is reported apart.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only prefill32k|prefill64k|decode1m   (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --summarize-pmc DIR                      (fold rocprofv3 counter CSVs)
        python bench.py --summarize-trace DIR                    (kernel table of a rocprofv3 trace)
+       python bench.py --record-traffic WL FETCH WRITE CFETCH CWRITE
+                       (HBM bytes per launch of WL's dominant kernel from counter runs)
 """
 from __future__ import annotations
 
@@ -96,12 +101,7 @@ def time_workload(name: str, steps: int, warmup: int):
                for i in range(DECODE_K_BUFFERS - 1)]
     out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
     ix = Indexer(wl.H, wl.D, wl.dtype, wl.topk, wl.T, wl.N, device=0)
-    try:
-        for i in range(warmup):
-            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
-        torch.cuda.synchronize(dev)
-        ix.timing(True)
-        ix.timing_read()
+    def timed_steps():
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize(dev)
@@ -110,17 +110,30 @@ def time_workload(name: str, steps: int, warmup: int):
             ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
         t1.record()
         torch.cuda.synchronize(dev)
-        ms = t0.elapsed_time(t1) / steps
+        return t0.elapsed_time(t1) / steps
+
+    try:
+        for i in range(warmup):
+            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
+        # the step time without per-kernel markers (each marker pair leaves the
+        # GPU idle for microseconds between kernels) ...
+        ms = timed_steps()
+        # ... then the same steps again with the library's per-kernel HIP events
+        # on the call's stream, for the kernel durations
+        ix.timing(True)
+        ix.timing_read()
+        ms_marked = timed_steps()
         per = ix.timing_read()
         ix.timing(False)
     finally:
         ix.close()
     kernels = {c: {"avg_ms": v[0] / v[1], "launches": v[1]} for c, v in per.items() if v[1]}
     pairs = visible_pairs(wl)
-    res = {"workload": name, "ms_per_step": ms, "pairs": pairs, "tokens": wl.T,
+    res = {"workload": name, "ms_per_step": ms, "ms_per_step_with_markers": ms_marked,
+           "pairs": pairs, "tokens": wl.T,
            "pairs_per_s": pairs / (ms * 1e-3), "query_tokens_per_s": wl.T / (ms * 1e-3),
            "kernels": kernels, "wl": wl}
-    log(f"[bench] {name}: {ms * 1e3:.1f} us/step, "
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step ({ms_marked * 1e3:.1f} with kernel markers), "
         + ", ".join(f"{c} {v['avg_ms'] * 1e3:.1f} us" for c, v in kernels.items()))
     return res
 
@@ -226,6 +239,62 @@ def summarize_pmc(directory: str):
     print(json.dumps(out, indent=1))
 
 
+def _pmc_table(directory: str):
+    """{kernel name: {counter: average per dispatch}} from rocprofv3 counter CSVs."""
+    acc = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
+                per = acc.setdefault(key, {})
+                did = r.get("Dispatch_Id", "0")
+                per[did] = per.get(did, 0.0) + float(r.get("Counter_Value", 0.0))
+    out = {}
+    for (name, ctr), per in acc.items():
+        out.setdefault(name, {})[ctr] = sum(per.values()) / len(per)
+    return out
+
+
+DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
+            "prefill32k": ("score", "prefill_scorer_kernel"),
+            "prefill64k": ("score", "prefill_scorer_kernel")}
+
+
+def record_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch: str, copy_write: str):
+    """HBM bytes per launch of the workload's dominant kernel from FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
+    reads for the plain 512 MiB copy of --copy-calibration; stored in
+    profiles/traffic_counters.json with the hash of the kernel's sources."""
+    cls, needle = DOMINANT[workload]
+    expect_kib = 512 * 1024.0
+
+    def pick(directory, counter, match):
+        tab = _pmc_table(directory)
+        cands = [(n, v[counter]) for n, v in tab.items() if counter in v and match(n)]
+        if not cands:
+            raise SystemExit(f"no {counter} for the kernel in {directory}")
+        return max(cands, key=lambda x: x[1])
+
+    _, cf = pick(copy_fetch, "FETCH_SIZE", lambda n: True)
+    _, cw = pick(copy_write, "WRITE_SIZE", lambda n: True)
+    kname, f = pick(fetch_dir, "FETCH_SIZE", lambda n: needle in n)
+    _, wr = pick(write_dir, "WRITE_SIZE", lambda n: needle in n)
+    ff, wf = expect_kib / cf, expect_kib / cw
+    rec = {"kernel": kname, "source_hash": source_hash(cls),
+           "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": wr,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": ff, "write_scale": wf,
+           "hbm_bytes_per_launch": (f * ff + wr * wf) * 1024.0}
+    data = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    data[f"{cls}:{workload}"] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def summarize_trace(directory: str):
     """Per-kernel calls and durations (us) from a rocprofv3 --kernel-trace run
     (its SQLite database, or its *kernel_stats.csv)."""
@@ -262,6 +331,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc")
     ap.add_argument("--summarize-trace")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -269,6 +340,9 @@ def main():
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return 0
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (the indexer kernels shard over "
@@ -300,6 +374,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "ms_per_step_with_markers": head["ms_per_step_with_markers"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -318,6 +393,7 @@ def main():
     for r in sec:
         wl = r["wl"]
         entry = {"workload": r["workload"], "dtype": wl.dtype, "ms_per_step": r["ms_per_step"],
+                 "ms_per_step_with_markers": r["ms_per_step_with_markers"],
                  "kernels_ms": {c: v["avg_ms"] for c, v in r["kernels"].items()},
                  "roofline": roofline(r)}
         if wl.T == 1:
