@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kPartWaves * 64) void decode_partition_kernel(
 // some partition listed only part of its rows and its smallest listed key is
 // above tU (it may hold unlisted rows above tU).  That case falls back to an
 // exact re-stream of those partitions' rows by one wave.
-// Thread i holds union elements [i*E, i*E + E), so thread order is row order.
-// kp is a power of two.
+// Union element e sits in slot e / NT of thread e % NT: every load reads
+// consecutive keys, and element order is row order.  kp is a power of two.
 // ---------------------------------------------------------------------------
 template <int MAXS, int MS, int NT>
 __global__ __launch_bounds__(NT) void decode_merge_kernel(
@@ -170,22 +170,19 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     constexpr int PPT = (kDecodeMaxParts + NT - 1) / NT;
     extern __shared__ uint64_t fb_buf[];
     __shared__ int red[BlockReduce<NW>::kWords];
-    __shared__ int scan[NW];
+    __shared__ int tab[MS][NW]; // kept keys per slot and wave
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int32_t p0 = pos[0];
     const int Pmax = (N + kDecodePart - 1) / kDecodePart;
-    const int Umax = Pmax * kp;
-    const int E = (Umax + NT - 1) / NT; // <= MS
+    const int Umax = Pmax * kp; // <= MS * NT
 
     // every load is issued before the visible count is known (one round trip)
     uint64_t key[MS];
 #pragma unroll
-    for (int s = 0; s < MS; ++s) {
-        const int e = tid * E + s;
-        key[s] = s < E && e < Umax ? cand[e] : 0ull;
-    }
+    for (int s = 0; s < MS; ++s)
+        key[s] = s * NT + tid < Umax ? cand[s * NT + tid] : 0ull;
     int my_pc[PPT];
     uint64_t my_pm[PPT];
 #pragma unroll
@@ -206,8 +203,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     int have = 0;
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
-        const int e = tid * E + s;
-        const bool in = s < E && e < U && key[s] != 0ull; // (unused list slots hold 0)
+        const bool in = s * NT + tid < U && key[s] != 0ull; // (unused list slots hold 0)
         hi[s] = in ? (uint32_t)(key[s] >> 32) : 0u;
         lo[s] = in ? (uint32_t)key[s] : 0u;
         have += in;
@@ -230,19 +226,29 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
         fallback = br.sum(popc(ballot(fail))) > 0;
     }
     if (!fallback) {
-        int c = 0;
-#pragma unroll
-        for (int s = 0; s < MS; ++s)
-            if (s < E)
-                c += (((uint64_t)hi[s] << 32) | lo[s]) >= tU;
-        int off = block_exclusive_scan(c, scan);
+        // output position of a kept key: kept keys of earlier slots, then of
+        // earlier waves in its slot, then of lower lanes
+        uint64_t m[MS];
 #pragma unroll
         for (int s = 0; s < MS; ++s) {
-            if (s < E) {
-                const uint64_t k = ((uint64_t)hi[s] << 32) | lo[s];
-                if (k >= tU)
-                    out[off++] = key_row(k);
+            m[s] = ballot(hi[s] != 0u && (((uint64_t)hi[s] << 32) | lo[s]) >= tU);
+            if (lane == 0)
+                tab[s][wave] = popc(m[s]);
+        }
+        lds_barrier();
+        int base = 0;
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+            int before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int c = tab[s][w];
+                before += w < wave ? c : 0;
+                all += c;
             }
+            if ((m[s] >> lane) & 1)
+                out[base + before + mbcnt(m[s])] = key_row(((uint64_t)hi[s] << 32) | lo[s]);
+            base += all;
         }
         return;
     }
