@@ -17,9 +17,10 @@ the headline workload.
 
 The step time is taken over K calls with nothing else on the stream.  The
 per-kernel durations come from a second timed pass of K calls in which the
-library records HIP events around each of its launches on the call's stream
-(ds_indexer_timing); those markers themselves leave the GPU idle between
-kernels, so that pass's step time is reported apart.
+library has each of its kernels record HIP events from its own dispatch
+(ds_indexer_timing: start of the first kernel of a step, end of the last, on
+the call's stream); launches that carry events are dispatched more slowly, so
+that pass's step time is reported apart.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only prefill32k|prefill64k|decode1m   (one workload, for profilers)
@@ -115,11 +116,11 @@ def time_workload(name: str, steps: int, warmup: int):
     try:
         for i in range(warmup):
             ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
-        # the step time without per-kernel markers (each marker pair leaves the
-        # GPU idle for microseconds between kernels) ...
+        # the step time without per-kernel events (launches that record them are
+        # dispatched more slowly) ...
         ms = timed_steps()
-        # ... then the same steps again with the library's per-kernel HIP events
-        # on the call's stream, for the kernel durations
+        # ... then the same steps again with the kernels recording HIP events from
+        # their own dispatch, for the kernel durations
         ix.timing(True)
         ix.timing_read()
         ms_marked = timed_steps()

@@ -100,27 +100,32 @@ hipEvent_t take_event(ds_indexer *ix)
     return hipEventCreate(&e) == hipSuccess ? e : nullptr;
 }
 
-// Runs one launch step, bracketed by events of class `cls` while timing is on.
+// Runs one launch step; while timing is on, its kernels record a pair of
+// events of class `cls` from their own dispatch (start of the first kernel,
+// end of the last).
 template <class F>
-hipError_t timed(ds_indexer *ix, int cls, hipStream_t s, F &&launch)
+hipError_t timed(ds_indexer *ix, int cls, F &&launch)
 {
     if (!ix->timing)
-        return launch();
-    hipEvent_t a = take_event(ix), b = take_event(ix);
-    if (!a || !b)
+        return launch(nullptr);
+    dsi::Timing tm;
+    tm.start = take_event(ix);
+    tm.stop = take_event(ix);
+    if (!tm.start || !tm.stop) {
+        if (tm.start)
+            ix->spare.push_back(tm.start);
+        if (tm.stop)
+            ix->spare.push_back(tm.stop);
         return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(a, s);
-    if (e == hipSuccess)
-        e = launch();
-    if (e == hipSuccess)
-        e = hipEventRecord(b, s);
-    if (e != hipSuccess) {
-        ix->spare.push_back(a);
-        ix->spare.push_back(b);
-        return e;
     }
-    ix->marks.push_back({cls, a, b});
-    return hipSuccess;
+    const hipError_t e = launch(&tm);
+    if (e == hipSuccess && tm.started && tm.stopped) {
+        ix->marks.push_back({cls, tm.start, tm.stop});
+    } else { // nothing launched (or a failure): the events were not used
+        ix->spare.push_back(tm.start);
+        ix->spare.push_back(tm.stop);
+    }
+    return e;
 }
 
 dsi::Problem problem(const ds_indexer *ix, const void *q, const void *k, const float *w,
@@ -219,20 +224,22 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
     hipError_t e;
     if (T == 1 && ix->decode_ok) {
         const int kp = decode_kp(N, topk);
-        e = timed(ix, DS_KERNEL_DECODE_SCORE, s,
-                  [&] { return dsi::launch_decode_scorer(p, topk, ix->S, s); });
+        e = timed(ix, DS_KERNEL_DECODE_SCORE, [&](dsi::Timing *tm) {
+            return dsi::launch_decode_scorer(p, topk, ix->S, s, tm);
+        });
         if (e == hipSuccess)
-            e = timed(ix, DS_KERNEL_DECODE_SELECT, s, [&] {
+            e = timed(ix, DS_KERNEL_DECODE_SELECT, [&](dsi::Timing *tm) {
                 return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, kp, ix->cand,
-                                                 ix->pcount, ix->pmin, out, s);
+                                                 ix->pcount, ix->pmin, out, s, tm);
             });
     } else {
-        e = timed(ix, DS_KERNEL_SCORE, s,
-                  [&] { return dsi::launch_prefill_scorer(p, topk, ix->S, ix->ldS, s); });
+        e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
+            return dsi::launch_prefill_scorer(p, topk, ix->S, ix->ldS, s, tm);
+        });
         if (e == hipSuccess)
-            e = timed(ix, DS_KERNEL_SELECT, s, [&] {
+            e = timed(ix, DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
                 return dsi::launch_topk_stream(ix->S, ix->ldS, pos, (int)T, (int)N, ratio, topk,
-                                               out, s);
+                                               out, s, tm);
             });
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;

@@ -1,10 +1,44 @@
 // internal.hpp -- host-side launchers of the indexer kernels (not part of the C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dsi {
+
+// Optional kernel timing.  When `start` / `stop` are set, the first kernel of
+// a launcher call records `start` as it begins and the last records `stop` as
+// it ends, from the kernels' own dispatch (no extra marker on the stream);
+// `started` / `stopped` tell whether that happened (no kernel may run).
+struct Timing {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+    bool started = false;
+    bool stopped = false;
+};
+
+// Launch `kernel` on `st`, converting each argument to the kernel's parameter
+// type; with `tm`, record its events on this launch (`first` / `last`: this
+// launch opens / closes the timed step).
+template <class... P, class... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                         Timing *tm, bool first, bool last, A &&...args)
+{
+    hipEvent_t e0 = tm && first ? tm->start : nullptr;
+    hipEvent_t e1 = tm && last ? tm->stop : nullptr;
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u,
+                              static_cast<P>(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, st, static_cast<P>(args)...);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && tm) {
+        tm->started |= e0 != nullptr;
+        tm->stopped |= e1 != nullptr;
+    }
+    return e;
+}
 
 struct Problem {
     const void *q;       // [T][H][D] raw fp16/bf16 bits
@@ -26,16 +60,18 @@ bool scorer_supported(int H, int D, int dtype);
 // Scores of every token with more than min_rows visible rows, written to
 // S[t * ldS + j] for j < n_t (other entries untouched).
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
-                                 hipStream_t st);
+                                 hipStream_t st, Timing *tm = nullptr);
 
 // Same for a single token (T == 1): one work-group per kDecodePart-row
 // partition streams K; writes S[j] for j < n.
-hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st);
+hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st,
+                                Timing *tm = nullptr);
 
 // Per-token streaming top-k over S rows (one wave per token); skip path for
 // tokens whose visible rows all fit.
 hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos, int T, int N,
-                              int ratio, int topk, int32_t *out, hipStream_t st);
+                              int ratio, int topk, int32_t *out, hipStream_t st,
+                              Timing *tm = nullptr);
 
 // Single-token selection over S[0..n): each kDecodePart-row partition lists
 // its exact best kp keys (in row order) in cand[p*kp ..], their number in
@@ -45,7 +81,7 @@ hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos,
 // of two, ceil(N / kDecodePart) * kp <= kDecodeUnion.
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
                                 int kp, uint64_t *cand, int *pcount, uint64_t *pmin, int32_t *out,
-                                hipStream_t st);
+                                hipStream_t st, Timing *tm = nullptr);
 
 // p[0..n) = v
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st);

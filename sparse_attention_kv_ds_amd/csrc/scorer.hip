@@ -418,26 +418,23 @@ __global__ void fill_kernel(float *__restrict__ p, long long n, float v)
 }
 
 template <int H, int D, int DT>
-hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, hipStream_t st)
+hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, hipStream_t st,
+                       Timing *tm)
 {
     constexpr int TPB = (64 / H) * kPrefillWaves;
     const dim3 grid((p.T + TPB - 1) / TPB, (p.N + kChunkRows - 1) / kChunkRows);
-    hipLaunchKernelGGL((prefill_scorer_kernel<H, D, DT, kPrefillWaves>), grid,
-                       dim3(kPrefillWaves * 64), 0, st, (const uint16_t *)p.q,
-                       (const uint16_t *)p.k, p.w, p.pos, p.T, p.N, p.ratio, min_rows,
-                       kChunkRows, S, ldS);
-    return hipGetLastError();
+    return launch_kernel(prefill_scorer_kernel<H, D, DT, kPrefillWaves>, grid,
+                         dim3(kPrefillWaves * 64), 0, st, tm, true, true, p.q, p.k, p.w, p.pos,
+                         p.T, p.N, p.ratio, min_rows, kChunkRows, S, ldS);
 }
 
 template <int H, int D, int DT>
-hipError_t decode_one(const Problem &p, int min_rows, float *S, hipStream_t st)
+hipError_t decode_one(const Problem &p, int min_rows, float *S, hipStream_t st, Timing *tm)
 {
     constexpr int ROWS = kDecWaves * 32; // per work-group
-    hipLaunchKernelGGL((decode_scorer_kernel<H, D, DT>), dim3((p.N + ROWS - 1) / ROWS),
-                       dim3(kDecWaves * 64), 0, st,
-                       (const uint16_t *)p.q, (const uint16_t *)p.k, p.w, p.pos, p.N, p.ratio,
-                       min_rows, S);
-    return hipGetLastError();
+    return launch_kernel(decode_scorer_kernel<H, D, DT>, dim3((p.N + ROWS - 1) / ROWS),
+                         dim3(kDecWaves * 64), 0, st, tm, true, true, p.q, p.k, p.w, p.pos, p.N,
+                         p.ratio, min_rows, S);
 }
 
 // (H, D, dtype) -> instantiation
@@ -455,15 +452,16 @@ hipError_t dispatch(int H, int D, int dt, A... args)
 }
 
 template <int H, int D, int DT> struct PrefillF {
-    static hipError_t run(const Problem &p, int m, float *S, long long ld, hipStream_t st)
+    static hipError_t run(const Problem &p, int m, float *S, long long ld, hipStream_t st,
+                          Timing *tm)
     {
-        return prefill_one<H, D, DT>(p, m, S, ld, st);
+        return prefill_one<H, D, DT>(p, m, S, ld, st, tm);
     }
 };
 template <int H, int D, int DT> struct DecodeF {
-    static hipError_t run(const Problem &p, int m, float *S, hipStream_t st)
+    static hipError_t run(const Problem &p, int m, float *S, hipStream_t st, Timing *tm)
     {
-        return decode_one<H, D, DT>(p, m, S, st);
+        return decode_one<H, D, DT>(p, m, S, st, tm);
     }
 };
 
@@ -477,18 +475,19 @@ bool scorer_supported(int H, int D, int dtype)
 }
 
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
-                                 hipStream_t st)
+                                 hipStream_t st, Timing *tm)
 {
     if (p.T <= 0 || p.N <= 0)
         return hipSuccess;
-    return dispatch<PrefillF>(p.H, p.D, p.dtype, p, min_rows, S, ldS, st);
+    return dispatch<PrefillF>(p.H, p.D, p.dtype, p, min_rows, S, ldS, st, tm);
 }
 
-hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st)
+hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st,
+                                Timing *tm)
 {
     if (p.T <= 0 || p.N <= 0)
         return hipSuccess;
-    return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, st);
+    return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, st, tm);
 }
 
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st)

@@ -287,69 +287,71 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
 
 template <int MAXS>
 hipError_t topk_stream_one(const float *S, long long ldS, const int32_t *pos, int T, int N,
-                           int ratio, int topk, int32_t *out, hipStream_t st)
+                           int ratio, int topk, int32_t *out, hipStream_t st, Timing *tm)
 {
     // waves (tokens) per work-group: 64 KiB of LDS at most
     const int wpb = MAXS >= 64 ? 2 : 4;
     const size_t lds = (size_t)wpb * MAXS * 64 * sizeof(uint64_t);
-    hipLaunchKernelGGL((topk_stream_kernel<MAXS>), dim3((T + wpb - 1) / wpb), dim3(wpb * 64), lds,
-                       st, S, ldS, pos, T, N, ratio, topk, out);
-    return hipGetLastError();
+    return launch_kernel(topk_stream_kernel<MAXS>, dim3((T + wpb - 1) / wpb), dim3(wpb * 64), lds,
+                         st, tm, true, true, S, ldS, pos, T, N, ratio, topk, out);
 }
 
 template <int MAXS>
 hipError_t merge_one(const float *S, const int32_t *pos, int N, int ratio, int topk, int kp,
                      const uint64_t *cand, const int *pcount, const uint64_t *pmin, int32_t *out,
-                     hipStream_t st)
+                     hipStream_t st, Timing *tm, bool first)
 {
     const size_t lds = (size_t)MAXS * 64 * sizeof(uint64_t);
     const long long U = (long long)((N + kDecodePart - 1) / kDecodePart) * kp;
     // four waves: a search step's count and its barrier cost about the same
     constexpr int NT = 256;
     if (U <= 16 * NT)
-        hipLaunchKernelGGL((decode_merge_kernel<MAXS, 16, NT>), dim3(1), dim3(NT), lds, st, S, pos,
-                           N, ratio, topk, kp, cand, pcount, pmin, out);
-    else
-        hipLaunchKernelGGL((decode_merge_kernel<MAXS, kDecodeUnion / NT, NT>), dim3(1), dim3(NT),
-                           lds, st, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
-    return hipGetLastError();
+        return launch_kernel(decode_merge_kernel<MAXS, 16, NT>, dim3(1), dim3(NT), lds, st, tm,
+                             first, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
+    return launch_kernel(decode_merge_kernel<MAXS, kDecodeUnion / NT, NT>, dim3(1), dim3(NT), lds,
+                         st, tm, first, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
 }
 
 } // namespace
 
 hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos, int T, int N,
-                              int ratio, int topk, int32_t *out, hipStream_t st)
+                              int ratio, int topk, int32_t *out, hipStream_t st, Timing *tm)
 {
     if (T <= 0)
         return hipSuccess;
     switch (select_slots(topk)) {
-    case 4: return topk_stream_one<4>(S, ldS, pos, T, N, ratio, topk, out, st);
-    case 8: return topk_stream_one<8>(S, ldS, pos, T, N, ratio, topk, out, st);
-    case 16: return topk_stream_one<16>(S, ldS, pos, T, N, ratio, topk, out, st);
-    case 32: return topk_stream_one<32>(S, ldS, pos, T, N, ratio, topk, out, st);
-    default: return topk_stream_one<64>(S, ldS, pos, T, N, ratio, topk, out, st);
+    case 4: return topk_stream_one<4>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
+    case 8: return topk_stream_one<8>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
+    case 16: return topk_stream_one<16>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
+    case 32: return topk_stream_one<32>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
+    default: return topk_stream_one<64>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
     }
 }
 
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
                                 int kp, uint64_t *cand, int *pcount, uint64_t *pmin, int32_t *out,
-                                hipStream_t st)
+                                hipStream_t st, Timing *tm)
 {
+    bool first = true; // the merge opens the timed step when there is no partition stage
     if (N > 0) {
         const int parts = (N + kDecodePart - 1) / kDecodePart;
-        hipLaunchKernelGGL(decode_partition_kernel, dim3((parts + kPartWaves - 1) / kPartWaves),
-                           dim3(kPartWaves * 64), 0, st, S, pos, N, ratio, topk, kp, cand, pcount,
-                           pmin);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_kernel(decode_partition_kernel,
+                                           dim3((parts + kPartWaves - 1) / kPartWaves),
+                                           dim3(kPartWaves * 64), 0, st, tm, true, false, S, pos,
+                                           N, ratio, topk, kp, cand, pcount, pmin);
         if (e != hipSuccess)
             return e;
+        first = false;
     }
     switch (select_slots(topk)) {
-    case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st);
-    case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st);
-    case 16: return merge_one<16>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st);
-    case 32: return merge_one<32>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st);
-    default: return merge_one<64>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st);
+    case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+    case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+    case 16:
+        return merge_one<16>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+    case 32:
+        return merge_one<32>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+    default:
+        return merge_one<64>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
     }
 }
 

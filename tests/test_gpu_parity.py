@@ -329,3 +329,34 @@ def test_decode1m_full_size(lib, orc):
     assert n == 262144
     check_tolerant(out[0], sc[0], osc[0], n, wl.topk, "decode1m")
     check_all_tokens(out, sc, d["pos"], wl.ratio, wl.N, wl.topk, "decode1m")
+
+
+def test_timing_markers_do_not_change_results(lib):
+    """Per-kernel HIP events (ds_indexer_timing): every launch class is counted once per
+    call, durations are positive, and the outputs are the same with markers on or off."""
+    say("timing markers: prefill and decode calls")
+    rng = np.random.default_rng(77)
+    H, D, topk = 8, 64, 32
+    for T, N, p0 in ((40, 600, 2000), (1, 5000, 4 * 5000 - 1)):
+        q, k, w, _ = rand_int_case(rng, T, N, H, D, -4, 4, 4, 1, "f16")
+        pos = np.arange(p0, p0 + T, dtype=np.int32)
+        ix = lib.Indexer(H, D, "f16", topk, T, N, device=0)
+        try:
+            plain = gpu_run(lib, q, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk, ix=ix)
+            ix.timing(True)
+            ix.timing_read()
+            marked = gpu_run(lib, q, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk, ix=ix)
+            per = ix.timing_read()
+            ix.timing(False)
+            after = gpu_run(lib, q, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk, ix=ix)
+            silent = ix.timing_read()
+        finally:
+            ix.close()
+        assert np.array_equal(plain, marked) and np.array_equal(plain, after)
+        classes = ("decode_score", "decode_select") if T == 1 else ("score", "select")
+        for c, (ms, n) in per.items():
+            if c in classes:
+                assert n == 1 and ms > 0.0, (c, ms, n)
+            else:
+                assert n == 0, (c, n)
+        assert all(n == 0 for _, n in silent.values())
