@@ -22,7 +22,8 @@ library has each of its kernels record HIP events from its own dispatch
 the call's stream); launches that carry events are dispatched more slowly, so
 that pass's step time is reported apart.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W = 200: the
+                       GPU needs some tens of milliseconds of work to reach its full clock)
        python bench.py --only prefill32k|prefill64k|decode1m   (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --summarize-pmc DIR                      (fold rocprofv3 counter CSVs)
@@ -330,7 +331,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=[HEADLINE, *SECONDARY])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
