@@ -113,23 +113,34 @@ __device__ __forceinline__ int count_hi_ge(const uint32_t (&hi)[E], uint32_t c)
     return r;
 }
 
-template <int E, class LO>
-__device__ __forceinline__ int count_lo_ge(const uint32_t (&hi)[E], const LO &lo, uint32_t v,
-                                           uint32_t c)
-{
-    int r = 0;
-#pragma unroll
-    for (int s = 0; s < E; ++s)
-        r += popc(ballot(hi[s] == v && lo[s] >= c));
-    return r;
-}
-
 // ---------------------------------------------------------------------------
 // Reductions over the participants of a selection: one wave, or a whole
 // work-group.  Every result is the same in all lanes (scalar registers).
 // ---------------------------------------------------------------------------
 struct WaveReduce {
     __device__ __forceinline__ int sum(int wave_count) { return wave_count; }
+    // Low word of the r-th (1-based) key with high word v in participant order:
+    // slot 0 of lanes 0..63, then slot 1, ... (r is at most the number of such keys)
+    template <int E, class LO>
+    __device__ __forceinline__ uint32_t nth(const uint32_t (&hi)[E], const LO &lo, uint32_t v,
+                                            int r)
+    {
+        const int lane = threadIdx.x & 63;
+        uint32_t res = 0;
+        int before = 0;
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            const uint64_t m = ballot(hi[s] == v);
+            const int c = popc(m);
+            const int q = r - before; // rank within this slot
+            if (q >= 1 && q <= c) {
+                const uint64_t hit = ballot(((m >> lane) & 1) && mbcnt(m) == q - 1);
+                res = __builtin_amdgcn_readlane((uint32_t)lo[s], (int)__builtin_ctzll(hit));
+            }
+            before += c;
+        }
+        return res;
+    }
     __device__ __forceinline__ void minmax(uint32_t &mn, uint32_t &mx)
     {
         mn = wave_min_u32(mn);
@@ -143,6 +154,7 @@ template <int NW>
 struct BlockReduce {
     static constexpr int kWords = 2 * NW * 2; // LDS ints the caller provides
     int *red;  // LDS [2][NW][2]
+    int *tab;  // LDS [E][NW] for nth<E>
     int phase; // double-buffered slots: one barrier per reduction is enough,
                // because a wave can only overwrite a slot after every wave has
                // passed the barrier of the next reduction, i.e. after every wave
@@ -196,6 +208,47 @@ struct BlockReduce {
     }
     __device__ __forceinline__ uint32_t umin(uint32_t v) { return ured<true>(v); }
     __device__ __forceinline__ uint32_t umax(uint32_t v) { return ured<false>(v); }
+
+    // As WaveReduce::nth, in the order slot, then wave, then lane.
+    template <int E, class LO>
+    __device__ __forceinline__ uint32_t nth(const uint32_t (&hi)[E], const LO &lo, uint32_t v,
+                                            int r)
+    {
+        const int lane = threadIdx.x & 63;
+        const int wave = wave_id();
+        uint64_t m[E];
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            m[s] = ballot(hi[s] == v);
+            if (lane == 0)
+                tab[s * NW + wave] = popc(m[s]);
+        }
+        lds_barrier();
+        int base = 0;
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            int before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int c = tab[s * NW + w];
+                before += w < wave ? c : 0;
+                all += c;
+            }
+            const int q = (int)readfirstlane(r - base - before); // rank within this wave's slot
+            if (q >= 1 && q <= popc(m[s])) {
+                const uint64_t hit = ballot(((m[s] >> lane) & 1) && mbcnt(m[s]) == q - 1);
+                const uint32_t x =
+                    __builtin_amdgcn_readlane((uint32_t)lo[s], (int)__builtin_ctzll(hit));
+                if (lane == 0)
+                    red[phase * NW * 2] = (int)x; // one writer in the whole group
+            }
+            base += all;
+        }
+        lds_barrier();
+        const uint32_t res = readfirstlane((uint32_t)red[phase * NW * 2]);
+        phase ^= 1;
+        return res;
+    }
 };
 
 // The largest (MAX) or smallest key whose high word lies in [v, u), v >= 1.
@@ -273,25 +326,11 @@ __device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const 
         return band_extreme<true>(hi, lo, vb, u, red);
     if (k == cv) // ... or the smallest
         return band_extreme<false>(hi, lo, vb, u, red);
-    // equal scores straddle the boundary: rank them by row
+    // equal scores straddle the boundary: among the keys with score v, the one
+    // with the need-th lowest row -- the participants hold their keys in row
+    // order, so it is the need-th such key in that order
     const int need = k - cu; // here u == v + 1, and >= 3 keys share the high word v
-    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
-#pragma unroll
-    for (int s = 0; s < E; ++s)
-        if (hi[s] == v) {
-            lmin = min(lmin, (uint32_t)lo[s]);
-            lmax = max(lmax, (uint32_t)lo[s]);
-        }
-    red.minmax(lmin, lmax);
-    const int ltop = 31 - __builtin_clz(lmin ^ lmax);
-    uint32_t w = lmax & ~((2u << ltop) - 1u);
-#pragma unroll 1
-    for (int b = ltop; b >= 0; --b) {
-        const uint32_t c = w | (1u << b);
-        if (red.sum(count_lo_ge<E, LO>(hi, lo, v, c)) >= need)
-            w = c;
-    }
-    return ((uint64_t)v << 32) | w;
+    return ((uint64_t)v << 32) | red.template nth<E, LO>(hi, lo, v, need);
 }
 
 // Low words of a wave's LDS key buffer, read on demand: slot s of this lane,

@@ -58,31 +58,65 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
             o[i] = i < n ? i : -1;
         return;
     }
-    WaveSelect<MAXS> sel;
-    sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, 0);
     const float *row = S + (long long)t * ldS;
-    constexpr int U = 8;
-    float cur[U], nxt[U];
+    const auto rr = make_rsrc(row, (uint32_t)n * 4); // (reads past n_t return 0)
+    // Starting threshold from a sample of the row (16 runs of 64 consecutive
+    // rows, evenly spaced): a bound L that about r sampled keys reach, r chosen
+    // so that about 1.5 k keys of the whole row are expected to reach L -- most
+    // of the row is then dropped at the first compare and the buffer rarely
+    // fills.  The result does not depend on the estimate: when fewer than k keys
+    // of the row reach L, the row is streamed again from threshold 0.
+    uint64_t lower = 0;
+    constexpr int NS = 16 * 64; // sample size, 16 keys per lane
+    if (n >= 4 * NS) {
+        uint32_t hi[16], lo[16];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int j = u * 64 + lane;
-        cur[u] = j < n ? row[j] : 0.f;
+        for (int s = 0; s < 16; ++s) {
+            const int j = (int)((long long)s * (n - 64) / 15) + lane;
+            const uint64_t key = make_key(
+                __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)j * 4, 0, 0)),
+                (uint32_t)j);
+            hi[s] = (uint32_t)(key >> 32);
+            lo[s] = (uint32_t)key;
+        }
+        const int r = min(NS, (int)((long long)topk * NS * 3 / (2LL * n)) + 8);
+        WaveReduce red;
+        lower = uniform64(select_bound<16>(hi, lo, NS, r, r / 4 + 1, red));
     }
-    for (int base = 0; base < n; base += U * 64) {
-        const int nb = base + U * 64;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = nb + u * 64 + lane;
-            nxt[u] = j < n ? row[j] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = base + u * 64 + lane;
-            sel.push(make_key(cur[u], (uint32_t)j), j < n);
-        }
+    WaveSelect<MAXS> sel;
+    // 32 scores per lane in flight while the previous 32 are pushed
+    constexpr int U = 32;
+#pragma unroll 1
+    for (;;) {
+        sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, lower);
+        float cur[U], nxt[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            cur[u] = nxt[u];
+            cur[u] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
+#pragma unroll 1
+        for (int base = 0; base < n; base += U * 64) {
+            const int nb = base + U * 64;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = nb + u * 64 + lane;
+                nxt[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rr, j < n ? (uint32_t)j * 4 : kOffNone, 0, 0));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = base + u * 64 + lane;
+                sel.push(make_key(cur[u], (uint32_t)j), j < n);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                cur[u] = nxt[u];
+        }
+        // (after a shrink the buffer holds >= k keys; without one it holds
+        // every key that reached the starting threshold)
+        if (sel.cnt >= topk || lower == 0)
+            break;
+        lower = 0;
     }
     sel.finish();
     for (int i = lane; i < topk; i += 64)
@@ -208,7 +242,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
         lo[s] = in ? (uint32_t)key[s] : 0u;
         have += in;
     }
-    BlockReduce<NW> br{red, 0};
+    BlockReduce<NW> br{red, &tab[0][0], 0};
     const int total = br.sum(wave_sum(have));
     bool fallback = total < topk;
     uint64_t tU = 0;

@@ -360,3 +360,23 @@ def test_timing_markers_do_not_change_results(lib):
             else:
                 assert n == 0, (c, n)
         assert all(n == 0 for _, n in silent.values())
+
+
+def test_sampled_threshold_restart(lib, orc):
+    """Rows long enough for the sampled starting threshold, built so that the sample
+    overestimates it: every sampled row (a multiple of the sampling step) has the top
+    score, so fewer than k rows of the whole row reach the estimate and the row must
+    be streamed again from threshold 0.  Bit-exact against the oracle either way."""
+    say("sampled threshold restart: n = 4096..8192, sampled rows carry the top score")
+    H, D, topk, ratio = 4, 32, 512, 1
+    for N in (4096, 6000, 8192):
+        step = N // 1024
+        k = np.zeros((N, D), dtype=np.float64)
+        j = np.arange(N)
+        k[:, 0] = np.where(j % step == 0, 4, j % 3)
+        q = np.zeros((3, H, D), dtype=np.float64)
+        q[:, :, 0] = 1
+        w = np.ones((3, H), dtype=np.float32)
+        pos = np.array([N - 1, N - 2, N + 5], dtype=np.int32)
+        exact_case(lib, orc, synth.to_bits(q, "f16"), synth.to_bits(k, "f16"), w, pos, H=H, D=D,
+                   dtype="f16", ratio=ratio, topk=topk, where=f"restart N={N}")
