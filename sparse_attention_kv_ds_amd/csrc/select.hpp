@@ -93,14 +93,17 @@ __device__ __forceinline__ void ge_masks4(uint32_t x0, uint32_t x1, uint32_t x2,
                  : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "s"(c));
 }
 
-// #{keys with high word >= c} over all E slots of the wave (empty slots hold
-// 0 and c >= 1, so they never count)
+// #{keys with high word >= c} over the wave's slots; slots at or past nsl (a
+// uniform bound, in steps of 4) are skipped, and empty slots hold 0 while
+// c >= 1, so they never count
 template <int E>
-__device__ __forceinline__ int count_hi_ge(const uint32_t (&hi)[E], uint32_t c)
+__device__ __forceinline__ int count_hi_ge(const uint32_t (&hi)[E], int nsl, uint32_t c)
 {
     int r = 0;
 #pragma unroll
     for (int s = 0; s < E; s += 4) {
+        if (s >= nsl)
+            break;
         if (s + 4 <= E) {
             uint64_t m0, m1, m2, m3;
             ge_masks4(hi[s], hi[s + 1], hi[s + 2], hi[s + 3], c, m0, m1, m2, m3);
@@ -272,7 +275,7 @@ __device__ __forceinline__ uint64_t band_extreme(const uint32_t (&hi)[E], const 
 }
 
 // Threshold search over the keys held by the participants (`tot` valid keys,
-// k <= tot; empty slots hold key 0).  With slack > 0: returns L with
+// k <= tot; empty slots hold key 0; slots at or past nsl are all empty).  With slack > 0: returns L with
 // k <= #{keys >= L} <= k + slack (a bound, not necessarily a key).  With
 // slack == 0: returns the k-th largest key itself.
 //
@@ -284,8 +287,8 @@ __device__ __forceinline__ uint64_t band_extreme(const uint32_t (&hi)[E], const 
 // scores across the boundary need the low word (the row), bisected from the
 // bits those keys share.
 template <int E, class LO, class R>
-__device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const LO &lo, int tot,
-                                                int k, int slack, R &red)
+__device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const LO &lo, int nsl,
+                                                int tot, int k, int slack, R &red)
 {
     if (slack > 0 && tot <= k + slack)
         return 1ull;
@@ -310,7 +313,7 @@ __device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const 
         if (slack > 0 ? cv <= k + slack : (k - cu == 1 || k == cv))
             break;
         const uint32_t c = v | (1u << b);
-        const int cc = red.sum(count_hi_ge<E>(hi, c));
+        const int cc = red.sum(count_hi_ge<E>(hi, nsl, c));
         if (cc >= k) {
             v = c;
             cv = cc;
@@ -352,30 +355,42 @@ struct WaveSelect {
     int cnt;      // keys in buf (wave-uniform)
     uint64_t tau; // keys <= tau cannot be among the k best (wave-uniform)
 
-    // requires CAP >= k + 128 (select_slots guarantees more)
-    __device__ __forceinline__ void init(uint64_t *b, int kk, uint64_t lower)
+    // Keys arrive in batches of at most `batch` (a multiple of 64) between
+    // make_room() calls; requires CAP >= k + batch + 64.
+    __device__ __forceinline__ void init(uint64_t *b, int kk, uint64_t lower, int batch)
     {
         buf = b;
         k = kk;
-        // leave >= 128 free slots after every shrink, so each shrink makes room
-        slack = min(CAP / 4, CAP - 128 - kk);
+        // every shrink leaves room for a whole batch
+        slack = min(CAP / 4, CAP - batch - kk);
         slack = slack > 0 ? slack : 0;
         cnt = 0;
         tau = lower ? lower - 1 : 0;
     }
 
-    // one key per lane (lanes with valid == false offer nothing)
-    __device__ __forceinline__ void push(uint64_t key, bool valid)
+    // before a batch of up to `incoming` keys
+    __device__ __forceinline__ void make_room(int incoming)
+    {
+        if (cnt > CAP - incoming)
+            shrink(slack);
+    }
+
+    // one key per lane (lanes with valid == false offer nothing); appends the
+    // keys above the threshold, in lane order, without checking for room
+    __device__ __forceinline__ void append(uint64_t key, bool valid)
     {
         const bool pass = valid && key > tau;
         const uint64_t m = ballot(pass);
-        if (m == 0)
-            return;
         if (pass)
             buf[cnt + mbcnt(m)] = key;
         cnt += popc(m);
-        if (cnt > CAP - 64)
-            shrink(slack);
+    }
+
+    // a batch of one key per lane
+    __device__ __forceinline__ void push(uint64_t key, bool valid)
+    {
+        make_room(64);
+        append(key, valid);
     }
 
     // keep only the keys >= a bound leaving between k and k + slack of them
@@ -404,9 +419,9 @@ struct WaveSelect {
         uint64_t L;
         // (every slot is looked at: empty ones hold key 0, which never counts)
         if constexpr (kLowInLds)
-            L = uniform64(select_bound<MAXS>(hi, LdsLow{mine}, cnt, k, sl, red));
+            L = uniform64(select_bound<MAXS>(hi, LdsLow{mine}, nsl, cnt, k, sl, red));
         else
-            L = uniform64(select_bound<MAXS>(hi, lo_r, cnt, k, sl, red));
+            L = uniform64(select_bound<MAXS>(hi, lo_r, nsl, cnt, k, sl, red));
         int nc = 0;
 #pragma unroll
         for (int s = 0; s < MAXS; ++s) {

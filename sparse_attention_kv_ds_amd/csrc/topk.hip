@@ -24,15 +24,20 @@ namespace dsi {
 
 namespace {
 
-// smallest per-wave buffer (in 64-key slots) for selecting topk: room for topk,
-// a quarter more, and 128 free slots after a shrink
-int select_slots(int topk)
+// smallest per-wave buffer (in 64-key slots) for selecting topk from batches
+// of `batch` keys: room for topk, a quarter more, and a batch after a shrink
+int select_slots(int topk, int batch)
 {
     for (int s : {4, 8, 16, 32})
-        if (s * 64 >= topk + topk / 4 + 128)
+        if (s * 64 >= topk + topk / 4 + batch + 64)
             return s;
     return 64;
 }
+
+// scores per lane in flight in the prefill stream, and the keys per batch
+// (one room check per batch keeps the appends free of the shrink)
+constexpr int kStreamU = 16;
+constexpr int kStreamBatch = kStreamU * 64;
 
 // ---------------------------------------------------------------------------
 // prefill: one wave per token over its row S[t][0..n_t); the next 512 scores
@@ -60,6 +65,14 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
     }
     const float *row = S + (long long)t * ldS;
     const auto rr = make_rsrc(row, (uint32_t)n * 4); // (reads past n_t return 0)
+    // The next U scores per lane are always in flight while the current U are
+    // appended; the first U are fetched before the sample below is used.
+    constexpr int U = kStreamU;
+    float cur[U], nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        cur[u] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
     // Starting threshold from a sample of the row (16 runs of 64 consecutive
     // rows, evenly spaced): a bound L that about r sampled keys reach, r chosen
     // so that about 1.5 k keys of the whole row are expected to reach L -- most
@@ -81,19 +94,12 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
         }
         const int r = min(NS, (int)((long long)topk * NS * 3 / (2LL * n)) + 8);
         WaveReduce red;
-        lower = uniform64(select_bound<16>(hi, lo, NS, r, r / 4 + 1, red));
+        lower = uniform64(select_bound<16>(hi, lo, 16, NS, r, r / 4 + 1, red));
     }
     WaveSelect<MAXS> sel;
-    // 32 scores per lane in flight while the previous 32 are pushed
-    constexpr int U = 32;
 #pragma unroll 1
     for (;;) {
-        sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, lower);
-        float cur[U], nxt[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            cur[u] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
+        sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, lower, kStreamBatch);
 #pragma unroll 1
         for (int base = 0; base < n; base += U * 64) {
             const int nb = base + U * 64;
@@ -103,10 +109,11 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
                 nxt[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                     rr, j < n ? (uint32_t)j * 4 : kOffNone, 0, 0));
             }
+            sel.make_room(kStreamBatch);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * 64 + lane;
-                sel.push(make_key(cur[u], (uint32_t)j), j < n);
+                sel.append(make_key(cur[u], (uint32_t)j), j < n);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -117,6 +124,10 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
         if (sel.cnt >= topk || lower == 0)
             break;
         lower = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            cur[u] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
     }
     sel.finish();
     for (int i = lane; i < topk; i += 64)
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kPartWaves * 64) void decode_partition_kernel(
     uint64_t t = 1ull; // every valid key is >= 1
     if (rows > kp) {
         WaveReduce red;
-        t = select_bound<E>(hi, lo, rows, kp, 0, red); // the kp-th best key
+        t = select_bound<E>(hi, lo, E, rows, kp, 0, red); // the kp-th best key
     }
     uint64_t *list = cand + (size_t)p * kp;
     int nc = 0;
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     bool fallback = total < topk;
     uint64_t tU = 0;
     if (!fallback) {
-        tU = select_bound<MS>(hi, lo, total, topk, 0, br); // the k-th key of the union
+        tU = select_bound<MS>(hi, lo, MS, total, topk, 0, br); // the k-th key of the union
         bool fail = false;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     if (wave != 0)
         return;
     WaveSelect<MAXS> sel;
-    sel.init(fb_buf, topk, tU);
+    sel.init(fb_buf, topk, tU, 64);
     // one 64-key chunk per step (a single push site keeps the kernel small)
     int p = 0, i = 0;
 #pragma unroll 1
@@ -353,7 +364,7 @@ hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos,
 {
     if (T <= 0)
         return hipSuccess;
-    switch (select_slots(topk)) {
+    switch (select_slots(topk, kStreamBatch)) {
     case 4: return topk_stream_one<4>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
     case 8: return topk_stream_one<8>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
     case 16: return topk_stream_one<16>(S, ldS, pos, T, N, ratio, topk, out, st, tm);
@@ -377,7 +388,7 @@ hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int r
             return e;
         first = false;
     }
-    switch (select_slots(topk)) {
+    switch (select_slots(topk, 64)) {
     case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
     case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
     case 16:
