@@ -150,6 +150,38 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// 16 bytes per lane from r at byte offset off straight into LDS: lane l's
+// bytes land at lds + 16 l (lds must be the same in every lane).  The load is
+// counted by vmcnt and its data is in LDS once that count says it completed.
+// AUX: cache policy bits of the load (e.g. 2 = non-temporal).
+template <int AUX = 0>
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             off, 0, 0, AUX);
+}
+
+// s_waitcnt with only vmcnt <= n (n < 64): waits until at most n vector
+// memory instructions of this wave are outstanding (they complete in order)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// LDS slot (16-byte units) of chunk c of row r in a staging area of rows of
+// CPR 16-byte chunks (CPR = 4, 8 or 16), no padding: the chunk index is XORed
+// with a function of the row so that the 16 rows read by 16 consecutive lanes
+// of one MFMA fragment load fall in 16 different bank groups.  The map is its
+// own inverse within a row, so the chunk held by slot position p of row r is
+// p ^ (the same function of r).
+template <int CPR>
+__device__ __forceinline__ int stage_slot(int r, int c)
+{
+    return r * CPR + (c ^ ((r / (16 / CPR)) % CPR));
+}
+
 // v + (the same register of lane l ^ 32): one cross-half swap, no LDS traffic
 __device__ __forceinline__ float add_other_half(float v)
 {

@@ -25,18 +25,26 @@ namespace {
 
 constexpr int kPrefillWaves = 4;    // waves per prefill work-group
 constexpr int kChunkRows = 2048;    // compressed rows per prefill work-group (multiple of 64)
+constexpr int kStageRows = 64;      // K rows per LDS stage (two 32-row blocks)
 
 // ---------------------------------------------------------------------------
 // prefill: blockIdx.x = tile of 64*WAVES (token, head) rows, blockIdx.y = chunk
 // of chunk_rows compressed rows (a multiple of the 64-row LDS stage).
 //
+// K moves through two LDS stages of 64 rows.  The loads go straight from
+// memory into LDS (buffer loads with the LDS bit: no registers, no LDS write
+// instructions), unpadded, with the 16-byte chunks of each row swizzled so that
+// the MFMA fragment reads are free of bank conflicts; every lane's fragment
+// addresses are computed once.  The loads of stage s+1 are issued as stage s
+// starts; at its end each wave waits for its own loads (vmcnt, not counting the
+// score stores issued since) and one barrier publishes them to the group.
+//
 // Per 64-row stage: 2 blocks of 32 rows.  Block b's MFMAs and block b-1's
 // epilogue are issued as one branch-free stretch of code, so the VALU work of
-// the epilogue runs while the matrix core is busy.  All bounds are handled by
-// buffer-resource ranges (rows past N read as 0, masked stores are dropped),
-// and the next stage's K loads are in flight during the whole stage.
+// the epilogue runs while the matrix core is busy.  Rows past N read as 0 and
+// masked score stores are dropped (buffer-resource ranges).
 // ---------------------------------------------------------------------------
-template <int H, int D, int DT, int WAVES, int NSTG = 2, int BPF = 1, int SR = 64, int PRIO = 0>
+template <int H, int D, int DT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int T, int N, int ratio, int min_rows, int chunk_rows,
@@ -45,22 +53,21 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     constexpr int TPW = 64 / H;       // tokens per wave
     constexpr int TPB = TPW * WAVES;  // tokens per work-group
     constexpr int KS = D / 16;        // MFMA steps along D
-    constexpr int ROWB = D * 2 + 16;  // LDS bytes per K row (16-byte pad: no bank conflicts)
     constexpr int CPR = D / 8;        // 16-byte chunks per K row
-    constexpr int NCH = SR * CPR;     // 16-byte chunks per stage
-    constexpr int NTHR = WAVES * 64;
-    constexpr int CPT = (NCH + NTHR - 1) / NTHR;
-    static_assert(NCH % NTHR == 0, "stage must split evenly over the work-group");
-    static_assert(NSTG == 2 || NSTG == 3, "two or three LDS stages");
-    static_assert(BPF == 1 || BPF == 2, "B fragments read one or two steps ahead");
-    static_assert(SR % 64 == 0, "stages of whole pairs of 32-row blocks");
+    constexpr int SR = kStageRows;
+    constexpr int STAGE_B = SR * D * 2;            // bytes of one stage
+    constexpr int LPW = SR * CPR / 64 / WAVES;     // 1 KiB LDS loads per wave per stage
+    static_assert(SR * CPR % (64 * WAVES) == 0, "stage must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) unsigned char kt[NSTG][SR * ROWB];
+    // the two stages are separate arrays so that the compiler can tell that
+    // the loads into one do not touch the fragment reads of the other
+    __shared__ __attribute__((aligned(1024))) unsigned char kt0[STAGE_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char kt1[STAGE_B];
     __shared__ int s_n[TPB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int col = lane & 31;
     const int hf = lane >> 5;
     const int tok_base = blockIdx.x * TPB;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 
     // visible rows of the tile's tokens; 0 for tokens past T and for tokens
     // that need no scoring (all their rows fit)
-    for (int i = tid; i < TPB; i += NTHR) {
+    for (int i = tid; i < TPB; i += WAVES * 64) {
         const int t = tok_base + i;
         const int n = t < T ? visible_rows(pos[t], ratio, N) : 0;
         s_n[i] = n > min_rows ? n : 0;
@@ -80,6 +87,25 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     const int j_end = min(j_chunk + chunk_rows, nmax);
     if (j_chunk >= j_end)
         return; // the same decision in every thread of the work-group
+
+    // K stage loads: load i of this wave fills LDS slots [64 (wave*LPW + i), +64)
+    // lane by lane; the lane fetches the chunk that belongs in its slot
+    const auto rk = make_rsrc(k, (uint32_t)N * D * 2);
+    uint32_t kvoff[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int s = (wave * LPW + i) * 64 + lane;
+        const int r = s / CPR;
+        const int c = (s % CPR) ^ ((r / (16 / CPR)) % CPR);
+        kvoff[i] = (uint32_t)(r * CPR + c) * 16;
+    }
+    auto load_stage = [&](int j0, unsigned char *kt) {
+        const uint32_t base = (uint32_t)j0 * D * 2;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            buf_load16_lds(rk, kt + (wave * LPW + i) * 1024, base + kvoff[i]);
+    };
+    load_stage(j_chunk, kt0);
 
     // tokens this lane stores: half-wave hf stores tokens hf, hf+2, ... of the
     // wave (H >= 8) or tokens 2g + hf of each 8-token tile (H == 4)
@@ -98,7 +124,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 
     const int t_here = min(TPB, T - tok_base);
     const auto rq = make_rsrc(q + (long long)tok_base * H * D, (uint32_t)t_here * H * D * 2);
-    const auto rk = make_rsrc(k, (uint32_t)N * D * 2);
+    const auto rw = make_rsrc(w + (long long)tok_base * H, (uint32_t)t_here * H * 4);
     const auto rs = make_rsrc(S + (long long)tok_base * ldS, (uint32_t)(t_here * ldS * 4));
 
     // A fragments (this wave's 64 rows of the flattened Q) and head weights
@@ -111,27 +137,17 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
         for (int kk = 0; kk < KS; ++kk)
             a[mt][kk] = buf_load16(rq, (r * D + kk * 16 + 8 * hf) * 2);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const long long rr = (long long)tok_base * H + wave * 64 + mt * 32 + acc_row(i, lane);
-            wr[mt][i] = rr < (long long)T * H ? w[rr] : 0.f;
-        }
+        for (int i = 0; i < 16; ++i)
+            wr[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rw, (uint32_t)(wave * 64 + mt * 32 + acc_row(i, lane)) * 4, 0, 0));
     }
 
-    u32x4 stage[CPT];
-    auto load_stage = [&](int j0) {
+    // this lane's B fragment byte offsets within a 32-row block: row col,
+    // chunk 2 kk + hf (elements 16 kk + 8 hf ..)
+    uint32_t boff[KS];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int ch = tid + c * NTHR;
-            stage[c] = buf_load16(rk, ((uint32_t)(j0 + ch / CPR) * D + (ch % CPR) * 8) * 2);
-        }
-    };
-    auto store_stage = [&](int b) {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int ch = tid + c * NTHR;
-            *reinterpret_cast<u32x4 *>(&kt[b][(ch / CPR) * ROWB + (ch % CPR) * 16]) = stage[c];
-        }
-    };
+    for (int kk = 0; kk < KS; ++kk)
+        boff[kk] = (uint32_t)stage_slot<CPR>(col, 2 * kk + hf) * 16;
 
     // Lane-local partial sums of the epilogue: slot = token of the lane (see
     // st_tok), two interleaved sums per slot for instruction-level parallelism.
@@ -142,8 +158,8 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     };
 
     // ReLU, head weight and sum over each token's heads of the finished block
-    // `e0/e1`, done EPK accumulator registers of each tile at a time so that it
-    // can be spread between the MFMAs of the next block.
+    // `e0/e1`, EPK accumulator registers of each tile at a time so that it can
+    // be spread between the MFMAs of the next block.
     constexpr int EPK = 16 / KS;
     auto reduce_part = [&](float (&part)[NSLOT][2], const f32x16 &e0, const f32x16 &e1, int kk) {
 #pragma unroll
@@ -179,28 +195,25 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
         }
     };
 
-    // MFMAs of one 32-row block of K (LDS rows kb[0..31]) into c0/c1, with the
-    // epilogue of the previous block (e0/e1, rows je..je+31) interleaved: each
-    // MFMA is followed by its share of that VALU work, and sched_barrier keeps
-    // the compiler from regrouping them.
+    // MFMAs of one 32-row block of K (LDS rows at kb) into c0/c1,
+    // with the epilogue of the previous block (e0/e1, rows je..je+31)
+    // interleaved: each MFMA is followed by its share of that VALU work, and
+    // sched_barrier keeps the compiler from regrouping them.
     auto block_step = [&](const unsigned char *kb, f32x16 &c0, f32x16 &c1, const f32x16 &e0,
                           const f32x16 &e1, int je) {
-        const unsigned char *bp = kb + col * ROWB + hf * 16;
         float part[NSLOT][2];
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl)
             part[sl][0] = part[sl][1] = 0.f;
         c0 = f32x16{};
         c1 = f32x16{};
-        u32x4 bq[KS];
-#pragma unroll
-        for (int kk = 0; kk < BPF; ++kk)
-            bq[kk] = *reinterpret_cast<const u32x4 *>(bp + kk * 32);
+        u32x4 bq[2];
+        bq[0] = *reinterpret_cast<const u32x4 *>(kb + boff[0]);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            if (kk + BPF < KS)
-                bq[kk + BPF] = *reinterpret_cast<const u32x4 *>(bp + (kk + BPF) * 32);
-            const u32x4 b = bq[kk];
+            if (kk + 1 < KS)
+                bq[(kk + 1) & 1] = *reinterpret_cast<const u32x4 *>(kb + boff[kk + 1]);
+            const u32x4 b = bq[kk & 1];
             c0 = mfma32<DT>(a[0][kk], b, c0);
 #pragma unroll
             for (int x = 0; x < EPK; ++x) {
@@ -221,53 +234,38 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
         store_part(part, je);
     };
 
+    // end of a stage: this wave's loads of the next stage have landed (the
+    // 2 NST score stores issued after them may still be in flight), then
+    // every wave's have
+    auto stage_done = [&]() {
+        wait_vmcnt<2 * NST>();
+        lds_barrier();
+    };
+
     f32x16 x0, x1, y0 = f32x16{}, y1 = f32x16{};
     int jy = -(1 << 30); // block held in y (none yet: every store masked)
-    if constexpr (NSTG == 2) {
-        // stage s+1 is loaded into registers during stage s and stored at its end
-        load_stage(j_chunk);
-        store_stage(0);
-        __syncthreads();
-        int buf = 0;
-        for (int js = j_chunk; js < j_end; js += SR) {
-            load_stage(js + SR); // past the end of K these read as 0; never used past j_end
-            const unsigned char *kb = kt[buf];
-            if constexpr (PRIO)
-                __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int pr = 0; pr < SR / 64; ++pr) {
-                block_step(kb + 64 * pr * ROWB, x0, x1, y0, y1, jy);
-                block_step(kb + (64 * pr + 32) * ROWB, y0, y1, x0, x1, js + 64 * pr);
-                jy = js + 64 * pr + 32;
-            }
-            if constexpr (PRIO)
-                __builtin_amdgcn_s_setprio(0);
-            store_stage(buf ^ 1);
-            lds_barrier();
-            buf ^= 1;
-        }
-    } else {
-        // three buffers: stage s+2 is loaded during stage s and stored at the
-        // start of stage s+1, a whole stage after its loads were issued
-        load_stage(j_chunk);
-        store_stage(0);
-        load_stage(j_chunk + SR);
-        __syncthreads();
-        int cur = 0;
-        for (int js = j_chunk; js < j_end; js += SR) {
-            const int nxt = cur == NSTG - 1 ? 0 : cur + 1;
-            store_stage(nxt);         // stage js + SR (loaded one stage ago)
-            load_stage(js + 2 * SR);  // past the end of K these read as 0
-            const unsigned char *kb = kt[cur];
-#pragma unroll
-            for (int pr = 0; pr < SR / 64; ++pr) {
-                block_step(kb + 64 * pr * ROWB, x0, x1, y0, y1, jy);
-                block_step(kb + (64 * pr + 32) * ROWB, y0, y1, x0, x1, js + 64 * pr);
-                jy = js + 64 * pr + 32;
-            }
-            lds_barrier();
-            cur = nxt;
-        }
+    wait_vmcnt<0>();     // stage 0, the query rows and the weights
+    __syncthreads();
+    // two stages per iteration, so that every LDS offset is a constant
+    for (int js = j_chunk;;) {
+        if (js + SR < j_end)
+            load_stage(js + SR, kt1);
+        block_step(kt0, x0, x1, y0, y1, jy);
+        block_step(kt0 + 32 * D * 2, y0, y1, x0, x1, js);
+        jy = js + 32;
+        stage_done();
+        js += SR;
+        if (js >= j_end)
+            break;
+        if (js + SR < j_end)
+            load_stage(js + SR, kt0);
+        block_step(kt1, x0, x1, y0, y1, jy);
+        block_step(kt1 + 32 * D * 2, y0, y1, x0, x1, js);
+        jy = js + 32;
+        stage_done();
+        js += SR;
+        if (js >= j_end)
+            break;
     }
     // last block: its epilogue alone
     {
@@ -299,16 +297,6 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 constexpr int kDecWaves = 4;
 // K loads marked non-temporal: every byte of K is read once per call
 constexpr int kStreamAux = 2;
-
-// LDS slot (16-byte units) of chunk c of row r in a K staging area of rows of
-// CPR 16-byte chunks: the chunk index is XORed with a function of the row so
-// that the 16 rows read by 16 lanes of one fragment load fall in 16 different
-// bank groups.  The map is its own inverse within a row.
-template <int CPR>
-__device__ __forceinline__ int stage_slot(int r, int c)
-{
-    return r * CPR + (c ^ ((r / (16 / CPR)) % CPR));
-}
 
 template <int H, int D, int DT>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_scorer_kernel(
@@ -357,13 +345,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_scorer_kernel(
         const int g = i * 64 + lane, r = g / CPR;
         const int c = (g % CPR) ^ ((r / (16 / CPR)) % CPR);
         const uint32_t off = ((uint32_t)(wrow + r) * CPR + c) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void *)(ks + i * 64), 16, off, 0, 0, kStreamAux);
+        buf_load16_lds<kStreamAux>(rk, ks + i * 64, off);
     }
 
     const int n = visible_rows(p0, ratio, N);
-    if (n <= min_rows || r0 >= n)
-        return; // same for the whole work-group
+    if (n <= min_rows || r0 >= n) {
+        wait_vmcnt<0>(); // no load into this group's LDS outlives it
+        return;          // same for the whole work-group
+    }
 
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
@@ -381,7 +370,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_scorer_kernel(
         for (int i = 0; i < 16; ++i)
             wr[mt][i] = ws[mt * 32 + acc_row(i, lane)];
 
-    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): the staged block has landed
+    wait_vmcnt<0>(); // the staged block has landed
     wave_lds_sync();
     const unsigned char *ap = qs + col * ROWB + hf * 16;
     f32x16 acc[MT];
