@@ -39,12 +39,12 @@ constexpr int kStageRows = 64;      // K rows per LDS stage (two 32-row blocks)
 // starts; at its end each wave waits for its own loads (vmcnt, not counting the
 // score stores issued since) and one barrier publishes them to the group.
 //
-// Per 64-row stage: 2 blocks of 32 rows.  Block b's MFMAs and block b-1's
-// epilogue are issued as one branch-free stretch of code, so the VALU work of
-// the epilogue runs while the matrix core is busy.  Rows past N read as 0 and
-// masked score stores are dropped (buffer-resource ranges).
+// Per 64-row stage: 2 blocks of 32 rows, each its 16 MFMAs then its epilogue
+// (one accumulator pair per wave keeps the kernel at three waves per SIMD, so
+// that other waves' MFMAs cover each wave's epilogue).  Rows past N read as 0
+// and masked score stores are dropped (buffer-resource ranges).
 // ---------------------------------------------------------------------------
-template <int H, int D, int DT, int WAVES>
+template <int H, int D, int DT, int WAVES, int SR>
 __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int T, int N, int ratio, int min_rows, int chunk_rows,
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     constexpr int TPB = TPW * WAVES;  // tokens per work-group
     constexpr int KS = D / 16;        // MFMA steps along D
     constexpr int CPR = D / 8;        // 16-byte chunks per K row
-    constexpr int SR = kStageRows;
+    static_assert(SR % 64 == 0, "stages of whole pairs of 32-row blocks");
     constexpr int STAGE_B = SR * D * 2;            // bytes of one stage
     constexpr int LPW = SR * CPR / 64 / WAVES;     // 1 KiB LDS loads per wave per stage
     static_assert(SR * CPR % (64 * WAVES) == 0, "stage must split evenly over the waves");
@@ -157,24 +157,31 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
         return H == 4 ? mt * 4 + (i >> 2) : (32 * mt + 8 * (i >> 2)) / H;
     };
 
-    // ReLU, head weight and sum over each token's heads of the finished block
-    // `e0/e1`, EPK accumulator registers of each tile at a time so that it can
-    // be spread between the MFMAs of the next block.
-    constexpr int EPK = 16 / KS;
-    auto reduce_part = [&](float (&part)[NSLOT][2], const f32x16 &e0, const f32x16 &e1, int kk) {
+    // One 32-row block of K (LDS rows at kb, compressed rows jb..jb+31): the
+    // MFMAs into c0/c1, then ReLU, head weight and the sum over each token's
+    // heads, and the store of s[t][jb + col].  The VALU work of one wave's
+    // epilogue runs while the other waves of its SIMD keep the matrix core
+    // busy (three waves fit: one accumulator pair per wave).
+    auto block = [&](const unsigned char *kb, int jb) {
+        f32x16 c0 = f32x16{}, c1 = f32x16{};
+        u32x4 bq[2];
+        bq[0] = *reinterpret_cast<const u32x4 *>(kb + boff[0]);
 #pragma unroll
-        for (int x = 0; x < EPK; ++x) {
-            const int i = kk * EPK + x;
-            part[slot_of(0, i)][i & 1] = fmaf(wr[0][i], fmaxf(e0[i], 0.f), part[slot_of(0, i)][i & 1]);
+        for (int kk = 0; kk < KS; ++kk) {
+            if (kk + 1 < KS)
+                bq[(kk + 1) & 1] = *reinterpret_cast<const u32x4 *>(kb + boff[kk + 1]);
+            c0 = mfma32<DT>(a[0][kk], bq[kk & 1], c0);
+            c1 = mfma32<DT>(a[1][kk], bq[kk & 1], c1);
         }
+        float part[NSLOT][2];
 #pragma unroll
-        for (int x = 0; x < EPK; ++x) {
-            const int i = kk * EPK + x;
-            part[slot_of(1, i)][i & 1] = fmaf(wr[1][i], fmaxf(e1[i], 0.f), part[slot_of(1, i)][i & 1]);
+        for (int sl = 0; sl < NSLOT; ++sl)
+            part[sl][0] = part[sl][1] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            part[slot_of(0, i)][i & 1] = fmaf(wr[0][i], fmaxf(c0[i], 0.f), part[slot_of(0, i)][i & 1]);
+            part[slot_of(1, i)][i & 1] = fmaf(wr[1][i], fmaxf(c1[i], 0.f), part[slot_of(1, i)][i & 1]);
         }
-    };
-    // finish the head sums and store s[t][jb + col]
-    auto store_part = [&](float (&part)[NSLOT][2], int jb) {
         const int j = jb + col;
 #pragma unroll
         for (int e = 0; e < NST; ++e) {
@@ -195,88 +202,41 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
         }
     };
 
-    // MFMAs of one 32-row block of K (LDS rows at kb) into c0/c1,
-    // with the epilogue of the previous block (e0/e1, rows je..je+31)
-    // interleaved: each MFMA is followed by its share of that VALU work, and
-    // sched_barrier keeps the compiler from regrouping them.
-    auto block_step = [&](const unsigned char *kb, f32x16 &c0, f32x16 &c1, const f32x16 &e0,
-                          const f32x16 &e1, int je) {
-        float part[NSLOT][2];
+    // the blocks of one stage (rows js.. in LDS at kt)
+    auto run_stage = [&](const unsigned char *kt, int js) {
 #pragma unroll
-        for (int sl = 0; sl < NSLOT; ++sl)
-            part[sl][0] = part[sl][1] = 0.f;
-        c0 = f32x16{};
-        c1 = f32x16{};
-        u32x4 bq[2];
-        bq[0] = *reinterpret_cast<const u32x4 *>(kb + boff[0]);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            if (kk + 1 < KS)
-                bq[(kk + 1) & 1] = *reinterpret_cast<const u32x4 *>(kb + boff[kk + 1]);
-            const u32x4 b = bq[kk & 1];
-            c0 = mfma32<DT>(a[0][kk], b, c0);
-#pragma unroll
-            for (int x = 0; x < EPK; ++x) {
-                const int i = kk * EPK + x;
-                part[slot_of(0, i)][i & 1] =
-                    fmaf(wr[0][i], fmaxf(e0[i], 0.f), part[slot_of(0, i)][i & 1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            c1 = mfma32<DT>(a[1][kk], b, c1);
-#pragma unroll
-            for (int x = 0; x < EPK; ++x) {
-                const int i = kk * EPK + x;
-                part[slot_of(1, i)][i & 1] =
-                    fmaf(wr[1][i], fmaxf(e1[i], 0.f), part[slot_of(1, i)][i & 1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int b = 0; b < SR / 32; ++b) {
+            if (b > 0 && js + 32 * b >= j_end)
+                break; // the rest of the last stage is past every token's rows
+            block(kt + 32 * b * D * 2, js + 32 * b);
         }
-        store_part(part, je);
     };
-
     // end of a stage: this wave's loads of the next stage have landed (the
-    // 2 NST score stores issued after them may still be in flight), then
-    // every wave's have
+    // score stores issued after them, NST per block, may still be in flight),
+    // then every wave's have
     auto stage_done = [&]() {
-        wait_vmcnt<2 * NST>();
+        wait_vmcnt<SR / 32 * NST>();
         lds_barrier();
     };
 
-    f32x16 x0, x1, y0 = f32x16{}, y1 = f32x16{};
-    int jy = -(1 << 30); // block held in y (none yet: every store masked)
-    wait_vmcnt<0>();     // stage 0, the query rows and the weights
+    wait_vmcnt<0>(); // stage 0, the query rows and the weights
     __syncthreads();
     // two stages per iteration, so that every LDS offset is a constant
     for (int js = j_chunk;;) {
         if (js + SR < j_end)
             load_stage(js + SR, kt1);
-        block_step(kt0, x0, x1, y0, y1, jy);
-        block_step(kt0 + 32 * D * 2, y0, y1, x0, x1, js);
-        jy = js + 32;
+        run_stage(kt0, js);
         stage_done();
         js += SR;
         if (js >= j_end)
             break;
         if (js + SR < j_end)
             load_stage(js + SR, kt0);
-        block_step(kt1, x0, x1, y0, y1, jy);
-        block_step(kt1 + 32 * D * 2, y0, y1, x0, x1, js);
-        jy = js + 32;
+        run_stage(kt1, js);
         stage_done();
         js += SR;
         if (js >= j_end)
             break;
-    }
-    // last block: its epilogue alone
-    {
-        float part[NSLOT][2];
-#pragma unroll
-        for (int sl = 0; sl < NSLOT; ++sl)
-            part[sl][0] = part[sl][1] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            reduce_part(part, y0, y1, kk);
-        store_part(part, jy);
     }
 }
 
@@ -412,7 +372,7 @@ hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, 
 {
     constexpr int TPB = (64 / H) * kPrefillWaves;
     const dim3 grid((p.T + TPB - 1) / TPB, (p.N + kChunkRows - 1) / kChunkRows);
-    return launch_kernel(prefill_scorer_kernel<H, D, DT, kPrefillWaves>, grid,
+    return launch_kernel(prefill_scorer_kernel<H, D, DT, kPrefillWaves, kStageRows>, grid,
                          dim3(kPrefillWaves * 64), 0, st, tm, true, true, p.q, p.k, p.w, p.pos,
                          p.T, p.N, p.ratio, min_rows, kChunkRows, S, ldS);
 }
