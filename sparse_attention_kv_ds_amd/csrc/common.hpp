@@ -46,8 +46,8 @@ __device__ __forceinline__ int visible_rows(int32_t pos, int ratio, int n_rows)
 {
     if (pos < 0)
         return 0;
-    long long n = ((long long)pos + 1) / ratio;
-    return n < n_rows ? (int)n : n_rows;
+    const uint32_t n = ((uint32_t)pos + 1u) / (uint32_t)ratio; // pos + 1 <= 2^31: no overflow
+    return n < (uint32_t)n_rows ? (int)n : n_rows;
 }
 
 // Unique, totally ordered selection key of (score, row): a larger key is a
@@ -168,6 +168,12 @@ __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(n >= 0 && n < 64, "vmcnt has 6 bits");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// s_waitcnt with only lgkmcnt(0): this wave's LDS accesses have completed
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
 }
 
 // LDS slot (16-byte units) of chunk c of row r in a staging area of rows of

@@ -241,122 +241,174 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decode (T == 1): work-groups of 4 waves, one 32-row block of K per wave.
-// Decode is bound by the K stream.  Each wave fetches its block with loads
-// that each read 1 KiB of consecutive rows and go straight into the wave's
-// LDS staging area (no registers in between), then reads the block back as
-// MFMA B fragments; a per-row XOR swizzle of the 16-byte chunks keeps those
-// fragment reads free of bank conflicts.  (Loading the fragments directly
-// would read 32 bytes from each of 32 rows per instruction, which the memory
-// system serves markedly slower.)  Many small work-groups stream best.  The
-// query and weights are fetched by the whole work-group alongside the first
-// K loads and shared through LDS.  No load waits for pos: K rows past the
-// visible count are fetched and dropped (the caller passes the rows that
-// exist, so at decode nearly all are visible).
+// decode (T == 1): work-groups of WAVES waves; each wave scores NB consecutive
+// 32-row blocks of K.  Decode is bound by the K stream, so the kernel keeps as
+// many K bytes in flight per CU as LDS allows, all the time: every K block
+// goes straight from memory into one of two LDS slots of its wave (buffer
+// loads with the LDS bit, non-temporal: each byte is read once per call); as
+// soon as block b has landed, the wave copies its MFMA fragments into
+// registers and reuses the slot for block b+2, then computes block b while
+// b+1 and b+2 are in flight.  The query rows are staged once per work-group
+// in LDS.  The 16-byte chunks of every staged row are swizzled so that the
+// fragment reads are free of bank conflicts.  (Loading MFMA fragments straight
+// into registers would read 32 bytes from each of 32 rows per instruction,
+// which the memory system serves markedly slower.)  No load waits for pos: K
+// rows past the visible count are fetched and dropped (the caller passes the
+// rows that exist, so at decode nearly all are visible).
 // ---------------------------------------------------------------------------
-constexpr int kDecWaves = 4;
 // K loads marked non-temporal: every byte of K is read once per call
 constexpr int kStreamAux = 2;
 
-template <int H, int D, int DT>
-__global__ __launch_bounds__(kDecWaves * 64) void decode_scorer_kernel(
+template <int H, int D, int DT, int WAVES, int NB>
+__global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int N, int ratio, int min_rows, float *__restrict__ S)
 {
     constexpr int KS = D / 16;
-    constexpr int MT = H > 32 ? 2 : 1;
-    constexpr int ROWB = D * 2 + 16;         // LDS bytes per query row (16-byte pad)
-    constexpr int QCH = MT * 32 * (D / 8);   // 16-byte chunks of the padded query
-    constexpr int NT = kDecWaves * 64;
-    constexpr int QPT = (QCH + NT - 1) / NT; // chunks per thread
-    constexpr int CPR = D / 8;               // 16-byte chunks per K row
-    static_assert(32 * CPR == 64 * KS, "one 1 KiB load per MFMA step of a block");
-    __shared__ __attribute__((aligned(16))) unsigned char qs[MT * 32 * ROWB];
-    __shared__ float ws[MT * 32];
-    __shared__ u32x4 kst[kDecWaves * 32 * CPR];
+    constexpr int MT = H > 32 ? 2 : 1;       // 32-head tiles of the query
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int BLK_B = 32 * D * 2;        // bytes of one 32-row block
+    constexpr int KPB = BLK_B / 1024;        // 1 KiB loads per K block
+    constexpr int QL = MT * 32 * CPR / 64;   // 1 KiB loads of the query, whole group
+    constexpr int QLW = (QL + WAVES - 1) / WAVES;
+    static_assert(BLK_B % 1024 == 0, "whole 1 KiB loads per block");
+    static_assert(NB >= 1 && KPB + 2 < 64, "vmcnt has 6 bits");
+    // the two slots are separate arrays so that the compiler can tell that the
+    // loads into one do not touch the fragment reads of the other
+    __shared__ __attribute__((aligned(1024))) unsigned char qs[QLW * WAVES * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char kst0[WAVES * BLK_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char kst1[WAVES * BLK_B];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int col = lane & 31;
     const int hf = lane >> 5;
     const int32_t p0 = pos[0];
-    const int r0 = blockIdx.x * (kDecWaves * 32);
-    const int wrow = r0 + wave * 32;
-    u32x4 *ks = kst + wave * 32 * CPR;
+    const int r0 = blockIdx.x * (WAVES * NB * 32);
+    const int wrow = r0 + wave * NB * 32;
+    unsigned char *const ks[2] = {kst0 + wave * BLK_B, kst1 + wave * BLK_B};
 
-    // query rows (heads past H read as 0) and weights
-    const auto rq = make_rsrc(q, (uint32_t)(H * D * 2));
-    u32x4 qv[QPT];
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-        const int c = tid + i * NT;
-        qv[i] = buf_load16(rq, c < QCH ? (uint32_t)c * 16 : kOffNone);
-    }
+    // head weights of this lane's accumulator rows (4 consecutive heads per
+    // load; heads past H read as 0)
     const auto rw = make_rsrc(w, (uint32_t)(H * 4));
-    const float wv = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rw, tid < MT * 32 ? tid * 4 : kOffNone, 0, 0));
-    // this wave's K block into LDS: load i fills slots [64 i, 64 i + 64) lane
-    // by lane, each lane fetching the chunk that belongs in its slot (rows
-    // past N read as 0)
-    const auto rk = make_rsrc(k, (uint32_t)N * D * 2);
+    u32x4 wv[MT][4];
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-        const int g = i * 64 + lane, r = g / CPR;
-        const int c = (g % CPR) ^ ((r / (16 / CPR)) % CPR);
-        const uint32_t off = ((uint32_t)(wrow + r) * CPR + c) * 16;
-        buf_load16_lds<kStreamAux>(rk, ks + i * 64, off);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            wv[mt][g] = buf_load16(rw, (uint32_t)(mt * 32 + acc_row(4 * g, lane)) * 4);
+    // the query rows, swizzled (heads past H read as 0)
+    const auto rq = make_rsrc(q, (uint32_t)(H * D * 2));
+#pragma unroll
+    for (int i = 0; i < QLW; ++i) {
+        const int li = wave * QLW + i;
+        const int sl = li * 64 + lane, r = sl / CPR;
+        const int c = (sl % CPR) ^ ((r / (16 / CPR)) % CPR);
+        if (li < QL)
+            buf_load16_lds(rq, qs + li * 1024, (uint32_t)(r * CPR + c) * 16);
     }
+    // K block b of this wave into slot b % 2: load i fills the slot's 16-byte
+    // units [64 i, 64 i + 64) lane by lane, each lane fetching the chunk that
+    // belongs in its unit (rows past N read as 0)
+    const auto rk = make_rsrc(k, (uint32_t)N * D * 2);
+    uint32_t koff[KPB];
+#pragma unroll
+    for (int i = 0; i < KPB; ++i) {
+        const int sl = i * 64 + lane, r = sl / CPR;
+        const int c = (sl % CPR) ^ ((r / (16 / CPR)) % CPR);
+        koff[i] = ((uint32_t)(wrow + r) * CPR + c) * 16;
+    }
+    auto load_block = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < KPB; ++i)
+            buf_load16_lds<kStreamAux>(rk, ks[b & 1] + i * 1024, koff[i] + (uint32_t)b * BLK_B);
+    };
+    load_block(0);
+    if (NB > 1)
+        load_block(1);
 
     const int n = visible_rows(p0, ratio, N);
     if (n <= min_rows || r0 >= n) {
         wait_vmcnt<0>(); // no load into this group's LDS outlives it
         return;          // same for the whole work-group
     }
-
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-        const int c = tid + i * NT;
-        if (c < QCH)
-            *reinterpret_cast<u32x4 *>(&qs[(c / (D / 8)) * ROWB + (c % (D / 8)) * 16]) = qv[i];
-    }
-    if (tid < MT * 32)
-        ws[tid] = wv;
+    // the weights and the query (issued before every K load) have landed
+    // here and in every wave
+    wait_vmcnt<(NB > 1 ? 2 : 1) * KPB>();
     lds_barrier();
+    u32x4 a[MT][KS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            a[mt][kk] = *reinterpret_cast<const u32x4 *>(
+                qs + (mt * 32 * CPR + stage_slot<CPR>(col, 2 * kk + hf)) * 16);
     float wr[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            wr[mt][i] = ws[mt * 32 + acc_row(i, lane)];
-
-    wait_vmcnt<0>(); // the staged block has landed
-    wave_lds_sync();
-    const unsigned char *ap = qs + col * ROWB + hf * 16;
-    f32x16 acc[MT];
+            wr[mt][i] = __uint_as_float(wv[mt][i >> 2][i & 3]);
+    uint32_t boff[KS]; // row col, elements 16 kk + 8 hf ..
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        const u32x4 bk = ks[stage_slot<CPR>(col, 2 * kk + hf)]; // row col, elements 16 kk + 8 hf ..
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const u32x4 a = *reinterpret_cast<const u32x4 *>(ap + mt * 32 * ROWB + kk * 32);
-            acc[mt] = mfma32<DT>(a, bk, acc[mt]);
-        }
-    }
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            s0 = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), s0);
-            s1 = fmaf(wr[mt][i + 1], fmaxf(acc[mt][i + 1], 0.f), s1);
-        }
-    const float s = add_other_half(s0 + s1);
+    for (int kk = 0; kk < KS; ++kk)
+        boff[kk] = (uint32_t)stage_slot<CPR>(col, 2 * kk + hf) * 16;
     const auto rs = make_rsrc(S, (uint32_t)n * 4);
-    buf_store_f32(rs, hf == 0 ? (uint32_t)(wrow + col) * 4 : kOffNone, s); // rows >= n dropped
+    // wait until block b has landed: issued after it are block b+1 (if any)
+    // and the score stores of blocks b-2 and b-1 (those that exist)
+    auto wait_block = [&](int b) {
+        const int st = b < 2 ? b : 2;
+        if (b + 1 < NB) {
+            if (st == 0)
+                wait_vmcnt<KPB>();
+            else if (st == 1)
+                wait_vmcnt<KPB + 1>();
+            else
+                wait_vmcnt<KPB + 2>();
+        } else {
+            if (st == 0)
+                wait_vmcnt<0>();
+            else if (st == 1)
+                wait_vmcnt<1>();
+            else
+                wait_vmcnt<2>();
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        wait_block(b);
+        wave_lds_sync();
+        u32x4 bk[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            bk[kk] = *reinterpret_cast<const u32x4 *>(ks[b & 1] + boff[kk]);
+        if (b + 2 < NB) {
+            // the slot's fragments are in registers: reuse it for block b+2
+            wait_lgkmcnt0();
+            wave_lds_sync();
+            load_block(b + 2);
+        }
+        f32x16 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = mfma32<DT>(a[mt][kk], bk[kk], acc[mt]);
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                s0 = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), s0);
+                s1 = fmaf(wr[mt][i + 1], fmaxf(acc[mt][i + 1], 0.f), s1);
+            }
+        const float sc = add_other_half(s0 + s1);
+        // rows >= n dropped
+        buf_store_f32(rs, hf == 0 ? (uint32_t)(wrow + b * 32 + col) * 4 : kOffNone, sc);
+    }
 }
 
 __global__ void fill_kernel(float *__restrict__ p, long long n, float v)
@@ -377,13 +429,16 @@ hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, 
                          p.T, p.N, p.ratio, min_rows, kChunkRows, S, ldS);
 }
 
+constexpr int kDecWaves = 4;  // waves per decode work-group
+constexpr int kDecBlocks = 4; // 32-row K blocks per decode wave
+
 template <int H, int D, int DT>
 hipError_t decode_one(const Problem &p, int min_rows, float *S, hipStream_t st, Timing *tm)
 {
-    constexpr int ROWS = kDecWaves * 32; // per work-group
-    return launch_kernel(decode_scorer_kernel<H, D, DT>, dim3((p.N + ROWS - 1) / ROWS),
-                         dim3(kDecWaves * 64), 0, st, tm, true, true, p.q, p.k, p.w, p.pos, p.N,
-                         p.ratio, min_rows, S);
+    constexpr int ROWS = kDecWaves * kDecBlocks * 32; // per work-group
+    return launch_kernel(decode_scorer_kernel<H, D, DT, kDecWaves, kDecBlocks>,
+                         dim3((p.N + ROWS - 1) / ROWS), dim3(kDecWaves * 64), 0, st, tm, true,
+                         true, p.q, p.k, p.w, p.pos, p.N, p.ratio, min_rows, S);
 }
 
 // (H, D, dtype) -> instantiation
