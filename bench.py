@@ -26,8 +26,12 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W
                        GPU needs some tens of milliseconds of work to reach its full clock)
        python bench.py --only prefill32k|prefill64k|decode1m   (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
+       python bench.py --ceilings                               (vendor GEMM and plain-copy
+                       rates with the workloads' value distributions)
        python bench.py --summarize-pmc DIR                      (fold rocprofv3 counter CSVs)
        python bench.py --summarize-trace DIR                    (kernel table of a rocprofv3 trace)
+       python bench.py --summarize-mfma DIR                     (clock and MFMA use per kernel
+                       from a rocprofv3 counter run)
        python bench.py --record-traffic WL FETCH WRITE CFETCH CWRITE
                        (HBM bytes per launch of WL's dominant kernel from counter runs)
 """
@@ -225,6 +229,57 @@ def copy_calibration(mib: int = 512, reps: int = 3):
                       "reps": reps}))
 
 
+def ceilings(reps: int = 20):
+    """Reference rates on this GPU with the workloads' value distributions:
+    a vendor (hipBLASLt, through torch.matmul) dense 8192^3 GEMM on
+    integer-valued fp16 operands and on Gaussian fp16 / bf16 operands (the
+    matrix cores draw more power on random mantissas and the clock drops),
+    and a plain device copy of 64 MiB (torch copy_ over 8 rotating buffer
+    pairs, so that every pass reads and writes HBM).  Times are events around back-to-back
+    launches on one stream."""
+    import torch
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(0)
+    n = 8192
+    out = {}
+
+    def timed(fn, k):
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize(dev)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(k):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / k * 1e-3
+
+    cases = {
+        "gemm_f16_integers": lambda: torch.randint(-4, 5, (n, n), device=dev, generator=g).to(torch.float16),
+        "gemm_f16_gaussian": lambda: (torch.randn(n, n, device=dev, generator=g) / 128 ** 0.5).to(torch.float16),
+        "gemm_bf16_gaussian": lambda: (torch.randn(n, n, device=dev, generator=g) / 128 ** 0.5).to(torch.bfloat16),
+    }
+    for name, make in cases.items():
+        x, y = make(), make()
+        # warm the clock with some tens of ms of work, then time
+        t = timed(lambda i: torch.matmul(x, y), reps)
+        t = timed(lambda i: torch.matmul(x, y), reps)
+        tf = 2.0 * n ** 3 / t / 1e12
+        out[name] = {"tflops": tf, "frac_of_2500": tf / PEAK_MFMA_TFLOPS["f16"]}
+        log(f"[ceilings] {name}: {tf:.0f} TFLOP/s ({tf / PEAK_MFMA_TFLOPS['f16'] * 100:.1f} % of 2.5 PFLOP/s)")
+        del x, y
+    src = [torch.randn(32 * 2 ** 20, device=dev, generator=g).to(torch.float16) for _ in range(8)]
+    dst = [torch.empty_like(src[0]) for _ in range(8)]
+    t = timed(lambda i: dst[i % 8].copy_(src[(i + 3) % 8]), 8 * reps)
+    gbs = 2 * 64 * 2 ** 20 / t / 1e9
+    out["copy_64MiB"] = {"GBps_read_plus_write": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "us": t * 1e6}
+    log(f"[ceilings] device copy of 64 MiB (torch copy_, 8 rotating buffer pairs): {t * 1e6:.1f} us, "
+        f"{gbs:.0f} GB/s read + write ({gbs / PEAK_HBM_GBS * 100:.1f} % of 8 TB/s)")
+    print(json.dumps(out))
+
+
 def summarize_pmc(directory: str):
     """Average per-dispatch counter values per kernel from rocprofv3 counter CSVs."""
     rows = []
@@ -243,6 +298,43 @@ def summarize_pmc(directory: str):
         vals = list(per.values())
         out.setdefault(name, {})[ctr] = {"dispatches": len(vals), "avg": sum(vals) / len(vals)}
     print(json.dumps(out, indent=1))
+
+
+def summarize_mfma(directory: str):
+    """Clock and matrix-core use per dispatch of the scorer kernels from a
+    rocprofv3 counter run with GRBM_GUI_ACTIVE (summed over the 8 XCDs),
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) and the MFMA op
+    counters (units of 512 flops): clock = GUI-active cycles per XCD / the
+    dispatch's duration; busy = MFMA-busy cycles per SIMD / GUI-active cycles
+    per XCD; flops from the op counters; rate = flops / duration."""
+    import statistics
+    per = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                d = per.setdefault(key, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                d["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    rows = {}
+    for (name, _), d in per.items():
+        if "GRBM_GUI_ACTIVE" not in d or "SQ_VALU_MFMA_BUSY_CYCLES" not in d or d["dur_ns"] <= 0:
+            continue
+        gui = d["GRBM_GUI_ACTIVE"] / 8.0
+        mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        rows.setdefault(name, []).append({
+            "dur_us": d["dur_ns"] / 1e3, "clock_ghz": gui / d["dur_ns"],
+            "mfma_busy": d["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / gui if gui else 0.0,
+            "tflops": mops * 512.0 / (d["dur_ns"] * 1e-9) / 1e12,
+            "coexec": d.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / max(d["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0)})
+    print("| kernel | dispatches | median duration us | clock GHz | MFMA busy | MFMA TFLOP/s (counted ops) | VALU co-issued with MFMA |")
+    print("|---|---|---|---|---|---|---|")
+    for name, v in sorted(rows.items()):
+        if not any(x["mfma_busy"] > 0 for x in v):
+            continue
+        med = {k: statistics.median(x[k] for x in v) for k in v[0]}
+        print(f"| `{name[:90]}` | {len(v)} | {med['dur_us']:.1f} | {med['clock_ghz']:.2f} | "
+              f"{med['mfma_busy'] * 100:.1f} % | {med['tflops']:.0f} | {med['coexec'] * 100:.0f} % of busy cycles |")
 
 
 def _pmc_table(directory: str):
@@ -335,8 +427,10 @@ def main():
     ap.add_argument("--only", choices=[HEADLINE, *SECONDARY])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceilings", action="store_true")
     ap.add_argument("--summarize-pmc")
     ap.add_argument("--summarize-trace")
+    ap.add_argument("--summarize-mfma")
     ap.add_argument("--record-traffic", nargs=5,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     args = ap.parse_args()
@@ -346,6 +440,9 @@ def main():
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return 0
     if args.record_traffic:
         record_traffic(*args.record_traffic)
@@ -357,6 +454,9 @@ def main():
         return 2
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.ceilings:
+        ceilings()
         return 0
 
     import torch
