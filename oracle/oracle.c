@@ -1,5 +1,7 @@
 /*
- * oracle.c -- plain, slow CPU oracle for the lightning-indexer score + top-k.
+ * oracle.c -- plain, slow CPU oracle for the lightning-indexer score + top-k,
+ * and for the sparse attention that consumes the selected rows (second half
+ * of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
  * the benchmark's CPU-baseline leg may load this library.  The GPU product
@@ -330,6 +332,258 @@ int oracle_score_topk(const uint16_t *q, const uint16_t *k, const float *w, cons
         if (jobs[th].status != ORACLE_OK)
             status = jobs[th].status;
     free(kd);
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
+}
+
+/* ======================================================================== *
+ * Sparse attention over the selected rows (the consumer of the indices).
+ *
+ * The pages describe the consumer as compressed attention that concatenates
+ * local key/value state with pooled (compressed) key/value state and runs
+ * ordinary dense attention over the result; the native kernel takes the
+ * pooled indices ("How I turned one oversized DeepSeek optimization into
+ * three merged oMLX PRs", section "1. Route ratio-128 prefill through native
+ * attention"), and the pooled rows a token uses are the ones its indexer
+ * selected ("How I made DeepSeek 12x faster on a Mac Studio", opening of
+ * section "1: the kernels").
+ *
+ * For token t at absolute position pos_t and attention head h:
+ *
+ *   rows R(t) = local rows p = max(0, pos_t - window + 1) .. min(pos_t, L-1)
+ *               of the raw cache (none when pos_t < 0 or window == 0),
+ *             + pooled rows j = idx[t][i] for every entry i with idx >= 0
+ *               (entries < 0 are padding; an entry >= N is an error)
+ *   s_r       = scale * sum_d q[t,h,d] * key_r[d]
+ *   o[t,h,:]  = sum_r  exp(s_r - max_r s) / sum_r' exp(s_r' - max s) * value_r
+ *             = 0 when R(t) is empty.
+ *
+ * Keys and values are shared by all heads.  Everything is decoded exactly
+ * to double and computed in double; nothing is blocked or reordered: per
+ * (token, head) it scores every row of R(t), takes the largest score, forms
+ * the weights and sums.
+ * ======================================================================== */
+
+typedef struct {
+    const uint16_t *q;        /* [T][HA][DK] */
+    const double *kp, *vp;    /* [N][DK], [N][DV] decoded */
+    const double *kl, *vl;    /* [L][DK], [L][DV] decoded */
+    const int32_t *idx, *pos; /* [T][topk], [T] */
+    int64_t T, N, L;
+    int HA, DK, DV, topk, window, dtype;
+    double scale;
+    const int64_t *tokens;
+    int64_t n_out;
+    double *out;              /* [n_out][HA][DV] */
+    int nthreads, tid, status;
+} attn_job;
+
+static void *run_attn_job(void *arg)
+{
+    attn_job *jb = (attn_job *)arg;
+    const int HA = jb->HA, DK = jb->DK, DV = jb->DV;
+    const int64_t cap = (int64_t)jb->topk + (jb->window > 0 ? jb->window : 0);
+    const double **krow = (const double **)malloc(sizeof(double *) * (size_t)(cap > 0 ? cap : 1));
+    const double **vrow = (const double **)malloc(sizeof(double *) * (size_t)(cap > 0 ? cap : 1));
+    double *s = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+    double *qh = (double *)malloc(sizeof(double) * (size_t)DK);
+    int64_t i;
+    jb->status = ORACLE_OK;
+    if (!krow || !vrow || !s || !qh) {
+        jb->status = ORACLE_ERR_NOMEM;
+        goto done;
+    }
+    for (i = jb->tid; i < jb->n_out; i += jb->nthreads) {
+        const int64_t t = jb->tokens ? jb->tokens[i] : i;
+        const int64_t p = jb->pos[t];
+        int64_t nr = 0, r, lo, hi;
+        int h, d, e;
+        /* the row set R(t): local rows first, then the listed pooled rows */
+        if (p >= 0 && jb->window > 0) {
+            lo = p - jb->window + 1;
+            if (lo < 0)
+                lo = 0;
+            hi = p < jb->L - 1 ? p : jb->L - 1;
+            for (r = lo; r <= hi; ++r) {
+                krow[nr] = jb->kl + r * DK;
+                vrow[nr] = jb->vl + r * DV;
+                ++nr;
+            }
+        }
+        for (e = 0; e < jb->topk; ++e) {
+            const int32_t j = jb->idx[t * jb->topk + e];
+            if (j < 0)
+                continue;
+            if (j >= jb->N) {
+                jb->status = ORACLE_ERR_ARG;
+                goto done;
+            }
+            krow[nr] = jb->kp + (int64_t)j * DK;
+            vrow[nr] = jb->vp + (int64_t)j * DV;
+            ++nr;
+        }
+        for (h = 0; h < HA; ++h) {
+            double *o = jb->out + (i * HA + h) * DV;
+            double m = -INFINITY, z = 0.0;
+            for (d = 0; d < DK; ++d) {
+                qh[d] = decode(jb->q[(t * HA + h) * DK + d], jb->dtype);
+                if (!isfinite(qh[d])) {
+                    jb->status = ORACLE_ERR_NONFINITE;
+                    goto done;
+                }
+            }
+            for (d = 0; d < DV; ++d)
+                o[d] = 0.0;
+            if (nr == 0)
+                continue;
+            for (r = 0; r < nr; ++r) {
+                double x = 0.0;
+                for (d = 0; d < DK; ++d)
+                    x += qh[d] * krow[r][d];
+                s[r] = jb->scale * x;
+                if (s[r] > m)
+                    m = s[r];
+            }
+            for (r = 0; r < nr; ++r) {
+                s[r] = exp(s[r] - m);
+                z += s[r];
+            }
+            for (r = 0; r < nr; ++r) {
+                const double a = s[r] / z;
+                for (d = 0; d < DV; ++d)
+                    o[d] += a * vrow[r][d];
+            }
+        }
+    }
+done:
+    free(krow);
+    free(vrow);
+    free(s);
+    free(qh);
+    return NULL;
+}
+
+static double *decode_all(const uint16_t *bits, int64_t n, int dtype, int *status)
+{
+    int64_t i;
+    double *x = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!x) {
+        *status = ORACLE_ERR_NOMEM;
+        return NULL;
+    }
+    for (i = 0; i < n; ++i) {
+        x[i] = decode(bits[i], dtype);
+        if (!isfinite(x[i])) {
+            *status = ORACLE_ERR_NONFINITE;
+            free(x);
+            return NULL;
+        }
+    }
+    return x;
+}
+
+/*
+ * Sparse attention for the tokens listed in `tokens` (or all T when NULL, in
+ * which case n_out must equal T).
+ *
+ *   q    [T][HA][DK]  raw fp16 (dtype 1) or bf16 (dtype 2) bits
+ *   kp   [N][DK], vp [N][DV]   pooled key / value rows, same dtype
+ *   kl   [L][DK], vl [L][DV]   raw (local) key / value rows by absolute position
+ *   idx  [T][topk] int32: pooled rows of each token, -1 = padding
+ *   pos  [T] int32 absolute positions
+ *   out  [n_out][HA][DV] double
+ *
+ * Returns ORACLE_OK, ORACLE_ERR_ARG, ORACLE_ERR_NONFINITE or ORACLE_ERR_NOMEM.
+ */
+int oracle_sparse_attention(const uint16_t *q, const uint16_t *kp, const uint16_t *vp,
+                            const uint16_t *kl, const uint16_t *vl, const int32_t *idx,
+                            const int32_t *pos, int64_t T, int64_t N, int64_t L, int HA, int DK,
+                            int DV, int topk, int window, double scale, int dtype,
+                            const int64_t *tokens, int64_t n_out, double *out, int threads)
+{
+    double *kpd = NULL, *vpd = NULL, *kld = NULL, *vld = NULL;
+    attn_job *jobs = NULL;
+    pthread_t *tids = NULL;
+    int *started = NULL;
+    int64_t i;
+    int th, status = ORACLE_OK;
+
+    if (T < 0 || N < 0 || L < 0 || HA < 1 || DK < 1 || DV < 1 || topk < 0 || window < 0 ||
+        n_out < 0 || !isfinite(scale))
+        return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+        return ORACLE_ERR_ARG;
+    if (!tokens && n_out != T)
+        return ORACLE_ERR_ARG;
+    if (n_out > 0 && (!q || !pos || !out || (topk > 0 && !idx)))
+        return ORACLE_ERR_ARG;
+    if ((N > 0 && (!kp || !vp)) || (L > 0 && (!kl || !vl)))
+        return ORACLE_ERR_ARG;
+    for (i = 0; i < n_out; ++i)
+        if (tokens && (tokens[i] < 0 || tokens[i] >= T))
+            return ORACLE_ERR_ARG;
+    if (threads < 1)
+        threads = 1;
+    kpd = decode_all(kp, N * DK, dtype, &status);
+    if (kpd)
+        vpd = decode_all(vp, N * DV, dtype, &status);
+    if (vpd)
+        kld = decode_all(kl, L * DK, dtype, &status);
+    if (kld)
+        vld = decode_all(vl, L * DV, dtype, &status);
+    if (!vld)
+        goto out;
+    jobs = (attn_job *)calloc((size_t)threads, sizeof(attn_job));
+    tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    started = (int *)calloc((size_t)threads, sizeof(int));
+    if (!jobs || !tids || !started) {
+        status = ORACLE_ERR_NOMEM;
+        goto out;
+    }
+    for (th = 0; th < threads; ++th) {
+        attn_job *jb = &jobs[th];
+        jb->q = q;
+        jb->kp = kpd;
+        jb->vp = vpd;
+        jb->kl = kld;
+        jb->vl = vld;
+        jb->idx = idx;
+        jb->pos = pos;
+        jb->T = T;
+        jb->N = N;
+        jb->L = L;
+        jb->HA = HA;
+        jb->DK = DK;
+        jb->DV = DV;
+        jb->topk = topk;
+        jb->window = window;
+        jb->dtype = dtype;
+        jb->scale = scale;
+        jb->tokens = tokens;
+        jb->n_out = n_out;
+        jb->out = out;
+        jb->nthreads = threads;
+        jb->tid = th;
+    }
+    for (th = 1; th < threads; ++th)
+        started[th] = pthread_create(&tids[th], NULL, run_attn_job, &jobs[th]) == 0;
+    run_attn_job(&jobs[0]);
+    for (th = 1; th < threads; ++th) {
+        if (started[th])
+            pthread_join(tids[th], NULL);
+        else
+            run_attn_job(&jobs[th]);
+    }
+    for (th = 0; th < threads; ++th)
+        if (jobs[th].status != ORACLE_OK)
+            status = jobs[th].status;
+out:
+    free(kpd);
+    free(vpd);
+    free(kld);
+    free(vld);
     free(jobs);
     free(tids);
     free(started);

@@ -7,8 +7,9 @@ imports this module.
 The oracle computes, for each query token, the lightning-indexer score of
 every causally visible compressed row in double precision, sorts all of them
 by (score descending, row ascending), keeps the first min(n_t, topk), and
-returns those rows in ascending order padded with -1 (the definition is
-written out at the top of oracle.c, with its sources).
+returns those rows in ascending order padded with -1; and the sparse
+attention of each token over its local raw rows plus its selected pooled
+rows (both definitions are written out in oracle.c, with their sources).
 """
 from __future__ import annotations
 
@@ -57,6 +58,9 @@ class Oracle:
         I = ctypes.c_int
         lib.oracle_score_topk.restype = I
         lib.oracle_score_topk.argtypes = [P, P, P, P, I64, I64, I, I, I, I, I, P, I64, P, P, I]
+        lib.oracle_sparse_attention.restype = I
+        lib.oracle_sparse_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
+                                                ctypes.c_double, I, P, I64, P, I]
         self.lib = lib
 
     def half_to_double(self, bits: int) -> float:
@@ -107,6 +111,50 @@ class Oracle:
         if st != 0:
             raise OracleError(f"oracle_score_topk: {STATUS.get(st, st)}")
         return (out, scores) if want_scores else out
+
+
+    def sparse_attention(self, q_bits, kp_bits, vp_bits, kl_bits, vl_bits, idx, pos, *,
+                         dtype: str, window: int, scale: float, tokens=None, threads: int = 1):
+        """Attention of each token's heads over its local window of raw rows plus
+        the pooled rows its index list names (definition in oracle.c).
+
+        q_bits  uint16 [T, HA, DK]; kp_bits [N, DK], vp_bits [N, DV] (pooled rows);
+        kl_bits [L, DK], vl_bits [L, DV] (raw rows by absolute position);
+        idx     int32 [T, topk] (-1 = padding); pos int32 [T].
+        Returns float64 [n_out, HA, DV].
+        """
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kp_bits = np.ascontiguousarray(kp_bits, dtype=np.uint16)
+        vp_bits = np.ascontiguousarray(vp_bits, dtype=np.uint16)
+        kl_bits = np.ascontiguousarray(kl_bits, dtype=np.uint16)
+        vl_bits = np.ascontiguousarray(vl_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        T, HA, DK = q_bits.shape
+        N, L = kp_bits.shape[0], kl_bits.shape[0]
+        DV = vp_bits.shape[1] if vp_bits.ndim == 2 else vl_bits.shape[1]
+        topk = idx.shape[1] if idx.ndim == 2 else 0
+        if (pos.shape != (T,) or (N and (kp_bits.shape[1] != DK or vp_bits.shape != (N, DV)))
+                or (L and (kl_bits.shape[1] != DK or vl_bits.shape != (L, DV)))
+                or (topk and idx.shape[0] != T)):
+            raise OracleError("oracle: inconsistent shapes")
+        if tokens is None:
+            tok, n_out = None, T
+        else:
+            tok = np.ascontiguousarray(tokens, dtype=np.int64)
+            n_out = int(tok.shape[0])
+        out = np.empty((n_out, HA, DV), dtype=np.float64)
+
+        def ptr(a):
+            return None if a is None or a.size == 0 else a.ctypes.data_as(ctypes.c_void_p)
+
+        st = self.lib.oracle_sparse_attention(ptr(q_bits), ptr(kp_bits), ptr(vp_bits), ptr(kl_bits),
+                                              ptr(vl_bits), ptr(idx), ptr(pos), T, N, L, HA, DK, DV,
+                                              topk, int(window), float(scale), DTYPES[dtype], ptr(tok),
+                                              n_out, ptr(out), int(threads))
+        if st != 0:
+            raise OracleError(f"oracle_sparse_attention: {STATUS.get(st, st)}")
+        return out
 
 
 _default = None

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the lightning indexer.
+"""Seeded synthetic inputs for the lightning indexer and for the sparse
+attention that consumes its selection.
 
 This module only draws random numbers and lays them out; it holds none of the
 method's arithmetic (no scores, no visibility rule, no selection).  Both the
@@ -105,3 +106,90 @@ def make(wl: Workload | str):
         wl = WORKLOADS[wl]
     q, k, w = draw(wl.T, wl.N, wl.H, wl.D, wl.dtype, wl.dist, wl.seed)
     return {"q": q, "k": k, "w": w, "pos": wl.positions, "wl": wl}
+
+
+# --- sparse attention over the selected rows ---------------------------------
+#
+# The attention consumes, per token, a list of pooled rows (in the full path,
+# the indexer's selection).  Its inputs here are drawn independently of any
+# indexer run: the list of token t holds m_t distinct pooled rows drawn
+# uniformly from 0..N-1, ascending, padded with -1, with m_t = topk except
+# for every `short_every`-th token, whose list is cut to a random length (the
+# attention itself does not require the rows to be causally visible; that is
+# the indexer's guarantee).  The query heads, pooled keys and values, and raw
+# (local) keys and values are N(0,1) draws (queries and keys scaled by
+# 1/sqrt(DK)), rounded to the storage type.  Draw order from
+# default_rng(seed): q, kp, vp, kl, vl, then the index lists token by token.
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    T: int          # query tokens
+    p0: int         # position of the first query token
+    N: int          # pooled (compressed) rows
+    L: int          # raw rows kept, indexed by absolute position
+    HA: int         # attention heads
+    DK: int
+    DV: int
+    topk: int
+    window: int     # local rows per token (the causal sliding window)
+    dtype: str
+    short_every: int = 0  # every n-th token gets a shorter index list (0: none)
+    seed: int = 0
+
+    @property
+    def positions(self) -> np.ndarray:
+        return np.arange(self.p0, self.p0 + self.T, dtype=np.int32)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.DK)
+
+
+ATTN_WORKLOADS = {
+    "attn_tiny": AttnWorkload("attn_tiny", T=96, p0=100, N=49, L=196, HA=32, DK=64, DV=64,
+                              topk=16, window=8, dtype="f16", short_every=5),
+    # the consumer of the 32k prefill chunk's indices
+    "attn32k": AttnWorkload("attn32k", T=2048, p0=30720, N=8192, L=32768, HA=64, DK=128, DV=128,
+                            topk=512, window=128, dtype="bf16"),
+}
+
+
+def draw_index_lists(rng, T: int, N: int, topk: int, short_every: int = 0) -> np.ndarray:
+    """Per token: an ascending set of distinct rows of 0..N-1, -1 padded to topk
+    entries -- the rows holding the m smallest of N uniform draws, with
+    m = min(N, topk), or a uniform count in 0..m for every short_every-th token
+    (those counts are drawn after all the uniforms)."""
+    idx = np.full((T, topk), -1, dtype=np.int32)
+    full = min(N, topk)
+    if T == 0 or full == 0:
+        return idx
+    keys = rng.random((T, N), dtype=np.float32)
+    part = np.argpartition(keys, full - 1, axis=1)[:, :full] if full < N else \
+        np.broadcast_to(np.arange(N), (T, N)).copy()
+    order = np.argsort(np.take_along_axis(keys, part, axis=1), axis=1, kind="stable")
+    part = np.take_along_axis(part, order, axis=1)  # by increasing draw
+    m = np.full(T, full, dtype=np.int64)
+    if short_every:
+        sel = np.arange(T) % short_every == short_every - 1
+        m[sel] = rng.integers(0, full + 1, size=int(sel.sum()))
+    for t in range(T):
+        if m[t]:
+            idx[t, :m[t]] = np.sort(part[t, :m[t]])
+    return idx
+
+
+def make_attention(wl: AttnWorkload | str):
+    """Inputs of a named attention workload (raw uint16 bits for the 16-bit tensors)."""
+    if isinstance(wl, str):
+        wl = ATTN_WORKLOADS[wl]
+    rng = np.random.default_rng(wl.seed)
+    sk = 1.0 / math.sqrt(wl.DK)
+    q = to_bits(rng.standard_normal(size=(wl.T, wl.HA, wl.DK)) * sk, wl.dtype)
+    kp = to_bits(rng.standard_normal(size=(wl.N, wl.DK)) * sk, wl.dtype)
+    vp = to_bits(rng.standard_normal(size=(wl.N, wl.DV)), wl.dtype)
+    kl = to_bits(rng.standard_normal(size=(wl.L, wl.DK)) * sk, wl.dtype)
+    vl = to_bits(rng.standard_normal(size=(wl.L, wl.DV)), wl.dtype)
+    pos = wl.positions
+    idx = draw_index_lists(rng, wl.T, wl.N, wl.topk, wl.short_every)
+    return {"q": q, "kp": kp, "vp": vp, "kl": kl, "vl": vl, "idx": idx, "pos": pos, "wl": wl}

@@ -382,6 +382,197 @@ def pin_nonfinite_rejected(orc: Oracle):
         raise AssertionError("non-finite input was accepted")
 
 
+# ----------------------------------------------------------------------------
+# sparse attention over the selected rows
+# ----------------------------------------------------------------------------
+
+def f16_bits(x) -> np.ndarray:
+    """fp16 bits of values that fp16 holds exactly (checked)."""
+    a = np.asarray(x, dtype=np.float64)
+    b = a.astype(np.float16)
+    assert np.array_equal(b.astype(np.float64), a), "value not exact in fp16"
+    return b.view(np.uint16)
+
+
+def rand_attn_case(rng, T, N, L, HA, DK, DV, topk, dtype="f16", pos_lo=-2, pos_hi=None):
+    """Small random attention inputs: Gaussian q/k/v, random positions (some
+    negative, some past L), random index lists with padding anywhere."""
+    pos_hi = L + 3 if pos_hi is None else pos_hi
+    q = synth.to_bits(rng.standard_normal((T, HA, DK)) * 0.5, dtype)
+    kp = synth.to_bits(rng.standard_normal((N, DK)) * 0.5, dtype)
+    vp = synth.to_bits(rng.standard_normal((N, DV)), dtype)
+    kl = synth.to_bits(rng.standard_normal((L, DK)) * 0.5, dtype)
+    vl = synth.to_bits(rng.standard_normal((L, DV)), dtype)
+    pos = rng.integers(pos_lo, pos_hi + 1, size=T).astype(np.int32)
+    idx = np.full((T, topk), -1, dtype=np.int32)
+    for t in range(T):
+        m = int(rng.integers(0, min(N, topk) + 1))
+        idx[t, rng.permutation(topk)[:m]] = rng.choice(N, size=m, replace=False)
+    return q, kp, vp, kl, vl, idx, pos
+
+
+def decoded(bits, dtype):
+    if dtype == "f16":
+        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_attn_library_sdpa(orc: Oracle):
+    """Dense equivalence: attending over the local window plus the listed pooled
+    rows equals torch's scaled_dot_product_attention (float64, CPU) over all
+    raw and pooled rows with a boolean mask that admits exactly those rows; a
+    token with no admitted row gets zeros."""
+    import torch
+    rng = np.random.default_rng(11)
+    for (T, N, L, HA, DK, DV, topk, W, dtype) in [(9, 7, 12, 3, 4, 5, 4, 3, "f16"),
+                                                    (12, 20, 30, 2, 8, 8, 6, 5, "bf16"),
+                                                    (6, 5, 8, 1, 3, 2, 5, 20, "f16")]:
+        q, kp, vp, kl, vl, idx, pos = rand_attn_case(rng, T, N, L, HA, DK, DV, topk, dtype)
+        scale = 0.7
+        got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype=dtype, window=W, scale=scale)
+        keys = torch.from_numpy(np.concatenate([decoded(kl, dtype), decoded(kp, dtype)]))
+        vals = torch.from_numpy(np.concatenate([decoded(vl, dtype), decoded(vp, dtype)]))
+        mask = np.zeros((T, L + N), dtype=bool)
+        raw = np.arange(L)
+        for t in range(T):
+            mask[t, :L] = (raw <= pos[t]) & (raw > pos[t] - W)
+            for j in idx[t]:
+                if j >= 0:
+                    mask[t, L + j] = True
+        qd = torch.from_numpy(decoded(q, dtype))                       # [T, HA, DK]
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qd.permute(1, 0, 2).unsqueeze(2),                            # [HA, T, 1, DK]
+            keys.expand(HA, T, L + N, DK),
+            vals.expand(HA, T, L + N, DV),
+            attn_mask=torch.from_numpy(mask).unsqueeze(1).expand(HA, T, 1, L + N),
+            scale=scale).squeeze(2).permute(1, 0, 2).numpy()             # [T, HA, DV]
+        empty = ~mask.any(axis=1)
+        want[empty] = 0.0
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), \
+            f"oracle attention != library attention (max diff {np.abs(got - want).max()})"
+
+
+def pin_attn_constant_keys_mean(orc: Oracle):
+    """Every key equal: every admitted row weighs the same, so the output is the
+    plain mean of the admitted value rows.  With raw value row p = p and pooled
+    value row j = 1000 + j the mean pins the window edges, the clamp to 0 and
+    to L-1, the padding and the pooled rows exactly."""
+    T, N, L, DK, DV, topk = 7, 6, 10, 2, 1, 4
+    kp = f16_bits(np.ones((N, DK)))
+    kl = f16_bits(np.ones((L, DK)))
+    vl = f16_bits(np.arange(L, dtype=np.float64)[:, None])
+    vp = f16_bits(1000.0 + np.arange(N, dtype=np.float64)[:, None])
+    q = f16_bits(np.full((T, 1, DK), 0.5))
+    pos = np.array([0, 1, 4, 9, 12, -1, 3], dtype=np.int32)
+    idx = np.array([[-1, -1, -1, -1], [2, -1, 5, -1], [-1, -1, -1, -1], [0, 1, 2, 3],
+                    [-1, 4, -1, -1], [-1, -1, -1, -1], [5, -1, -1, -1]], dtype=np.int32)
+    for W in (0, 1, 3, 20):
+        got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype="f16", window=W, scale=1.3)
+        for t in range(T):
+            rows = []
+            if pos[t] >= 0 and W > 0:
+                rows += list(range(max(0, pos[t] - W + 1), min(pos[t], L - 1) + 1))
+            rows_v = [float(r) for r in rows] + [1000.0 + j for j in idx[t] if j >= 0]
+            want = sum(Fraction(v) for v in rows_v) / len(rows_v) if rows_v else Fraction(0)
+            assert abs(got[t, 0, 0] - float(want)) <= 1e-12 * max(1.0, abs(float(want))), \
+                (W, t, got[t, 0, 0], float(want))
+
+
+def pin_attn_single_row(orc: Oracle):
+    """A set of one row returns that row's value exactly, whatever the scores."""
+    rng = np.random.default_rng(5)
+    q, kp, vp, kl, vl, _, _ = rand_attn_case(rng, 4, 6, 9, 2, 4, 3, 3)
+    pos = np.array([0, 5, 8, 3], dtype=np.int32)
+    idx = np.full((4, 3), -1, dtype=np.int32)
+    got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype="f16", window=1, scale=2.0)
+    for t in range(4):
+        for h in range(2):
+            assert np.array_equal(got[t, h], decoded(vl[pos[t]], "f16"))
+    idx = np.array([[4, -1, -1], [-1, 0, -1], [-1, -1, 5], [2, -1, -1]], dtype=np.int32)
+    got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype="f16", window=0, scale=2.0)
+    for t in range(4):
+        j = int(idx[t][idx[t] >= 0][0])
+        for h in range(2):
+            assert np.array_equal(got[t, h], decoded(vp[j], "f16"))
+
+
+def pin_attn_dominant_key(orc: Oracle):
+    """One pooled key far ahead of the others (score gap > 1000): its value comes
+    out, and nothing overflows on the way."""
+    T, N, L, DK, DV = 2, 5, 6, 2, 3
+    q = f16_bits(np.tile(np.array([1.0, 0.0]), (T, 1, 1)))
+    kp = f16_bits(np.array([[1.0, 0], [2048.0, 0], [-3.0, 1], [0.5, 0.5], [4.0, 0]]))
+    kl = f16_bits(np.zeros((L, DK)))
+    rng = np.random.default_rng(9)
+    vp = f16_bits(rng.integers(-8, 9, (N, DV)).astype(np.float64))
+    vl = f16_bits(rng.integers(-8, 9, (L, DV)).astype(np.float64))
+    idx = np.array([[0, 1, 2, 3], [3, 4, 1, -1]], dtype=np.int32)
+    pos = np.array([5, 2], dtype=np.int32)
+    got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype="f16", window=4, scale=1.0)
+    for t in range(T):
+        assert np.all(np.isfinite(got[t])) and np.allclose(got[t, 0], decoded(vp[1], "f16"),
+                                                           rtol=0, atol=1e-12)
+
+
+def pin_attn_invariances(orc: Oracle):
+    """Adding one vector to every key shifts each head's scores by a constant:
+    no change.  Adding one vector to every value adds it to the output.
+    Reordering a token's index entries (padding anywhere) changes nothing."""
+    rng = np.random.default_rng(21)
+    T, N, L, HA, DK, DV, topk, W = 8, 10, 14, 3, 4, 3, 6, 4
+    ki = lambda n: rng.integers(-3, 4, (n, DK)).astype(np.float64)  # noqa: E731
+    kp0, kl0 = ki(N), ki(L)
+    vp0 = rng.integers(-5, 6, (N, DV)).astype(np.float64)
+    vl0 = rng.integers(-5, 6, (L, DV)).astype(np.float64)
+    q = f16_bits(rng.integers(-2, 3, (T, HA, DK)) * 0.25)
+    pos = rng.integers(-1, L + 2, T).astype(np.int32)
+    idx = np.full((T, topk), -1, dtype=np.int32)
+    for t in range(T):
+        m = int(rng.integers(0, topk + 1))
+        idx[t, :m] = np.sort(rng.choice(N, m, replace=False))
+    base = orc.sparse_attention(q, f16_bits(kp0), f16_bits(vp0), f16_bits(kl0), f16_bits(vl0),
+                                idx, pos, dtype="f16", window=W, scale=0.9)
+    u = np.array([1.0, -2.0, 3.0, 0.5])
+    shifted = orc.sparse_attention(q, f16_bits(kp0 + u), f16_bits(vp0), f16_bits(kl0 + u),
+                                   f16_bits(vl0), idx, pos, dtype="f16", window=W, scale=0.9)
+    assert np.allclose(shifted, base, rtol=1e-12, atol=1e-12), "not invariant to a key shift"
+    c = np.array([7.0, -3.0, 0.25])
+    moved = orc.sparse_attention(q, f16_bits(kp0), f16_bits(vp0 + c), f16_bits(kl0),
+                                 f16_bits(vl0 + c), idx, pos, dtype="f16", window=W, scale=0.9)
+    has = np.array([(p >= 0) or (idx[t] >= 0).any() for t, p in enumerate(pos)])
+    assert np.allclose(moved[has], base[has] + c, rtol=1e-12, atol=1e-12), "value translation"
+    perm = np.stack([row[rng.permutation(topk)] for row in idx])
+    again = orc.sparse_attention(q, f16_bits(kp0), f16_bits(vp0), f16_bits(kl0), f16_bits(vl0),
+                                 perm, pos, dtype="f16", window=W, scale=0.9)
+    assert np.allclose(again, base, rtol=1e-12, atol=1e-12), "index order or padding position"
+
+
+def pin_attn_empty_and_errors(orc: Oracle):
+    """No admitted row: zeros.  A listed row >= N, or non-finite data: rejected."""
+    rng = np.random.default_rng(3)
+    q, kp, vp, kl, vl, _, _ = rand_attn_case(rng, 3, 4, 5, 2, 3, 2, 2)
+    idx = np.full((3, 2), -1, dtype=np.int32)
+    pos = np.array([-1, 2, -5], dtype=np.int32)
+    got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype="f16", window=0, scale=1.0)
+    assert not got.any()
+    got = orc.sparse_attention(q, kp, vp, kl, vl, idx, pos, dtype="f16", window=3, scale=1.0)
+    assert not got[0].any() and not got[2].any() and got[1].any()
+    bad = idx.copy()
+    bad[1, 0] = 4
+    try:
+        orc.sparse_attention(q, kp, vp, kl, vl, bad, pos, dtype="f16", window=3, scale=1.0)
+        raise AssertionError("row >= N accepted")
+    except OracleError:
+        pass
+    vp2 = vp.copy()
+    vp2[0, 0] = 0x7C00  # +inf
+    try:
+        orc.sparse_attention(q, kp, vp2, kl, vl, idx, pos, dtype="f16", window=3, scale=1.0)
+        raise AssertionError("non-finite value accepted")
+    except OracleError:
+        pass
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -52,6 +52,18 @@ MUTANTS = [
     ("f16_subnormal", "ldexp((double)frac, -24);", "ldexp((double)frac, -25);"),
     ("bf16_bias", "expo - 134); /*", "expo - 133); /*"),
     ("bf16_frac_bits", "int frac = bits & 0x7F;", "int frac = bits & 0x3F;"),
+    # sparse attention
+    ("attn_scale_dropped", "s[r] = jb->scale * x;", "s[r] = x;"),
+    ("attn_window_one_short", "lo = p - jb->window + 1;", "lo = p - jb->window + 2;"),
+    ("attn_window_excludes_self", "hi = p < jb->L - 1 ? p : jb->L - 1;",
+     "hi = p - 1 < jb->L - 1 ? p - 1 : jb->L - 1;"),
+    ("attn_padding_ends_list", "if (j < 0)\n                continue;", "if (j < 0)\n                break;"),
+    ("attn_no_max_shift", "s[r] = exp(s[r] - m);", "s[r] = exp(s[r]);"),
+    ("attn_unnormalised", "const double a = s[r] / z;", "const double a = s[r];"),
+    ("attn_local_values_reversed", "vrow[nr] = jb->vl + r * DV;", "vrow[nr] = jb->vl + (hi - (r - lo)) * DV;"),
+    ("attn_every_head_is_head0", "jb->q[(t * HA + h) * DK + d]", "jb->q[(t * HA) * DK + d]"),
+    ("attn_pooled_keys_reversed", "krow[nr] = jb->kp + (int64_t)j * DK;",
+     "krow[nr] = jb->kp + (int64_t)(jb->N - 1 - j) * DK;"),
 ]
 
 
