@@ -156,6 +156,56 @@ int ds_indexer_timing_read(ds_indexer *ix, double *ms, int64_t *launches);
 /* Static, human-readable text for a status code (never NULL). */
 const char *ds_indexer_status_str(int status);
 
+/*
+ * Sparse attention over the selected rows: the consumer of the indices.
+ *
+ * The pages describe it as compressed attention over local key/value state
+ * together with pooled (compressed) key/value state, the pooled rows given by
+ * indices ("How I turned one oversized DeepSeek optimization into three merged
+ * oMLX PRs", section "1. Route ratio-128 prefill through native attention"),
+ * and the pooled rows a token attends to are the ones the lightning indexer
+ * selected for it ("How I made DeepSeek 12x faster on a Mac Studio", opening
+ * of section "1: the kernels").  For token t at position pos[t] and head h:
+ *
+ *   R(t)     = local rows  max(0, pos[t] - window + 1) .. min(pos[t], L - 1)
+ *              (none when pos[t] < 0 or window == 0)
+ *            + pooled rows idx[t][e] for every entry with 0 <= idx[t][e] < N
+ *   o[t,h,:] = sum over r in R(t) of softmax_r(scale * q[t,h,:] . key_r) * value_r
+ *            = 0 when R(t) is empty.
+ * Keys and values are shared by all heads.  Entries outside [0, N) are padding
+ * (ds_indexer_score_topk writes -1 there); a row listed twice counts twice.
+ *
+ *   q       [T][n_heads][head_dim]  fp16/bf16 bits (dtype), device
+ *   k_pool  [N][head_dim], v_pool [N][head_dim]   pooled rows, device
+ *   k_local [L][head_dim], v_local [L][head_dim]  raw rows by absolute position, device
+ *   idx     [T][topk] int32, device (e.g. the output of ds_indexer_score_topk)
+ *   pos     [T] int32 absolute positions, device
+ *   out     [T][n_heads][head_dim] float32, device (written in full)
+ *   stream  hipStream_t, NULL = null stream; the call only enqueues work
+ * Supported: n_heads in {32, 64, 128}, head_dim in {64, 128}, dtype DS_F16 or
+ * DS_BF16, 0 <= topk <= 2048, window >= 0, N * head_dim and L * head_dim below
+ * 2^30 elements.  q, k_*, v_* and out 16-byte aligned; idx and pos 4-byte
+ * aligned.  The caller owns every buffer and keeps it alive until the stream
+ * has run the call; the library keeps no state and allocates nothing.
+ *
+ * Arithmetic: scores and softmax in float32 (base-2 exponentials), the weights
+ * rounded to the value type for the value product (relative rounding of each
+ * weight at most 2^-8 for bf16, 2^-11 for fp16), accumulation in float32, so
+ * each output differs from exact attention by at most about that fraction of
+ * the largest |value| in the token's rows.
+ *
+ * Returns DS_OK, DS_ERR_INVALID_ARG (a null pointer where one is needed,
+ * misalignment, negative sizes, non-finite scale), DS_ERR_UNSUPPORTED (head
+ * count, head dim, dtype or topk outside the list above) or DS_ERR_HIP
+ * (launch failure).  Arguments are checked on the host before any launch;
+ * positions and index values are not read on the host.
+ */
+int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
+                        const void *k_local, const void *v_local, const int32_t *idx,
+                        const int32_t *pos, int64_t T, int64_t N, int64_t L, int n_heads,
+                        int head_dim, int dtype, int topk, int window, float scale, float *out,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

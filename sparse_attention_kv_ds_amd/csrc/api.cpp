@@ -323,6 +323,51 @@ void ds_indexer_destroy(ds_indexer *ix)
     delete ix;
 }
 
+int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
+                        const void *k_local, const void *v_local, const int32_t *idx,
+                        const int32_t *pos, int64_t T, int64_t N, int64_t L, int n_heads,
+                        int head_dim, int dtype, int topk, int window, float scale, float *out,
+                        void *stream)
+{
+    if (T < 0 || N < 0 || L < 0 || topk < 0 || window < 0 || !(scale == scale) ||
+        scale > 3.0e38f || scale < -3.0e38f)
+        return DS_ERR_INVALID_ARG;
+    if (!dsi::attention_supported(n_heads, head_dim, dtype) || topk > dsi::kAttnMaxTopk)
+        return DS_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 30;
+    if (T > INT_MAX || N * head_dim >= lim || L * head_dim >= lim ||
+        T * (int64_t)n_heads * head_dim >= ((int64_t)1 << 40))
+        return DS_ERR_UNSUPPORTED;
+    if (T == 0)
+        return DS_OK;
+    if (!q || !pos || !out || (topk > 0 && !idx) || (N > 0 && (!k_pool || !v_pool)) ||
+        (L > 0 && (!k_local || !v_local)))
+        return DS_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+        !aligned(k_local, 16) || !aligned(v_local, 16) || !aligned(out, 16) ||
+        !aligned(idx, 4) || !aligned(pos, 4))
+        return DS_ERR_INVALID_ARG;
+    dsi::AttnProblem a;
+    a.q = q;
+    a.kp = k_pool;
+    a.vp = v_pool;
+    a.kl = k_local;
+    a.vl = v_local;
+    a.idx = idx;
+    a.pos = pos;
+    a.T = (int)T;
+    a.N = (int)N;
+    a.L = (int)L;
+    a.HA = n_heads;
+    a.D = head_dim;
+    a.topk = topk;
+    a.window = window;
+    a.dtype = dtype;
+    a.scale = scale;
+    a.out = out;
+    return dsi::launch_sparse_attention(a, (hipStream_t)stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
 const char *ds_indexer_status_str(int status)
 {
     switch (status) {

@@ -1,0 +1,322 @@
+// attention.hip -- sparse attention over the selected rows, for gfx950.
+//
+// For token t at position p and attention head h, one softmax over the rows
+// R(t) = the local raw rows max(0, p - window + 1) .. min(p, L-1) plus the
+// pooled rows listed in idx[t] (entries outside [0, N) are padding):
+//   o[t,h,:] = sum_r softmax_r(scale * q[t,h,:] . key_r) value_r
+// with keys and values shared by all heads ("How I turned one oversized
+// DeepSeek optimization into three merged oMLX PRs", section "1. Route
+// ratio-128 prefill through native attention": local and pooled key/value
+// state attended together, the pooled rows given by indices; the indices are
+// the lightning indexer's selection, "How I made DeepSeek 12x faster on a Mac
+// Studio", section "1: the kernels").
+//
+// One work-group per token, one wave per 32 heads.  The token's rows are taken
+// in blocks of 32: the local rows first (their last block padded), then the
+// index list in order, so that every block reads one tensor pair.  Each
+// block's K and V rows go straight from memory into LDS (buffer loads with the
+// LDS bit), the next block's while the current one is computed.
+//   * S^T = K_blk . Q^T on the 32x32x16 MFMA: each lane then holds 16 keys of
+//     one head, so the softmax statistics of a head live in one lane pair.
+//   * Online softmax in base 2 with a lazy rescale: the running exponent base
+//     of a head moves only when a block's maximum exceeds it by more than 8,
+//     so p <= 2^8 and the accumulators are rescaled rarely.
+//   * O^T += V_blk^T . P^T on the MFMA: P comes straight from the S^T
+//     accumulators (converted to the value type), V^T fragments from the
+//     row-major V block by LDS transpose reads (ds_read_b64_tr_b16).
+// Output fp32, o = O / (sum of p), 0 for a token with no row.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dsi {
+
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// 4 x 16-bit of the transposed LDS read: within each group of 16 lanes, lane
+// i receives element i % 4 of the 8-byte chunk addressed by lane 4 e + i / 4,
+// for e = 0..3.
+__device__ __forceinline__ uint64_t lds_read_tr16(const void *p)
+{
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)const_cast<void *>(p));
+    return __builtin_bit_cast(uint64_t, r);
+}
+
+// two floats -> two 16-bit values of type DT (round to nearest even)
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    if constexpr (DT == kF16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const b2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+template <int WAVES, int D, int DT>
+__global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kp,
+    const uint16_t *__restrict__ vp, const uint16_t *__restrict__ kl,
+    const uint16_t *__restrict__ vl, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ pos, int N, int L, int topk, int window, float scale_log2,
+    float *__restrict__ out)
+{
+    constexpr int HA = WAVES * 32;
+    constexpr int KS = D / 16;            // MFMA steps along D for S
+    constexpr int DTL = D / 32;           // 32-wide value tiles
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
+    constexpr int RPL = 64 / CPR;         // rows per 1 KiB load
+    constexpr int BLK_B = 32 * D * 2;     // bytes of 32 rows
+    constexpr int LPB = BLK_B / 1024;     // 1 KiB loads per block and tensor
+    constexpr int LPW = 2 * LPB / WAVES;  // loads per wave per block (K and V)
+    static_assert(2 * LPB % WAVES == 0, "block loads split evenly over the waves");
+    static_assert(LPW <= 16, "vmcnt headroom");
+
+    __shared__ int32_t ids[kAttnMaxTopk];
+    // one array per stage and tensor, so that the compiler can tell that the
+    // loads into one stage do not touch the fragment reads of the other
+    __shared__ __attribute__((aligned(1024))) unsigned char ks0[BLK_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char ks1[BLK_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char vs0[BLK_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char vs1[BLK_B];
+
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int col = lane & 31;
+    const int hf = lane >> 5;
+    const int p = pos[t];
+    int lo = 0, n_loc = 0;
+    if (p >= 0 && window > 0) {
+        lo = max(0, p - window + 1);
+        n_loc = max(0, min(p, L - 1) - lo + 1);
+    }
+    const int nb_loc = (n_loc + 31) >> 5;
+    const int nb = nb_loc + ((topk + 31) >> 5);
+
+    // the token's index list (entries outside [0, N) are padding)
+    for (int e = threadIdx.x; e < topk; e += WAVES * 64)
+        ids[e] = idx[(long long)t * topk + e];
+
+    // this wave's 32 heads as MFMA B fragments: head col, elements 16 kk + 8 hf ..
+    const auto rq = make_rsrc(q + ((long long)t * HA + wave * 32) * D, 32u * D * 2);
+    u32x4 qf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+        qf[kk] = buf_load16(rq, ((uint32_t)col * D + kk * 16 + hf * 8) * 2);
+    __syncthreads(); // the index list
+
+    const auto rkp = make_rsrc(kp, (uint32_t)N * D * 2);
+    const auto rvp = make_rsrc(vp, (uint32_t)N * D * 2);
+    const auto rkl = make_rsrc(kl, (uint32_t)L * D * 2);
+    const auto rvl = make_rsrc(vl, (uint32_t)L * D * 2);
+
+    // row of key slot r (0..31) of block b, or -1 when the slot is empty
+    auto block_row = [&](int b, int r) -> int {
+        if (b < nb_loc) {
+            const int k = 32 * b + r;
+            return k < n_loc ? lo + k : -1;
+        }
+        const int e = 32 * (b - nb_loc) + r;
+        const int j = e < topk ? ids[e] : -1;
+        return (j >= 0 && j < N) ? j : -1;
+    };
+    // this wave's share of block b's K and V rows into the given stage: load u
+    // of the block fills 16-byte units [64 i, 64 i + 64) of K (u < LPB, i = u)
+    // or of V (i = u - LPB), lane by lane; K rows are chunk-swizzled, V rows are
+    // plain (the transpose reads want whole 8-byte runs of a row)
+    auto load_block = [&](int b, unsigned char *kst, unsigned char *vst) {
+        const bool local = b < nb_loc;
+#pragma unroll
+        for (int x = 0; x < LPW; ++x) {
+            const int u = wave * LPW + x;
+            const bool isk = u < LPB;
+            const int i = isk ? u : u - LPB;
+            const int r = i * RPL + lane / CPR;
+            const int pc = lane % CPR;
+            const int row = block_row(b, r);
+            const int c = isk ? pc ^ ((r / (16 / CPR)) % CPR) : pc;
+            const uint32_t off = row >= 0 ? ((uint32_t)row * CPR + c) * 16 : kOffNone;
+            unsigned char *dst = (isk ? kst : vst) + i * 1024;
+            if (isk) {
+                if (local)
+                    buf_load16_lds(rkl, dst, off);
+                else
+                    buf_load16_lds(rkp, dst, off);
+            } else {
+                if (local)
+                    buf_load16_lds(rvl, dst, off);
+                else
+                    buf_load16_lds(rvp, dst, off);
+            }
+        }
+    };
+
+    // per lane: head col of this wave's tile; the two half-waves hold
+    // different keys of the same head and keep the same exponent base
+    float m_base = -__builtin_huge_valf(); // exponent base (log2 domain)
+    float l_part = 0.f;                    // this lane's part of the sum of p
+    f32x16 o[DTL];
+#pragma unroll
+    for (int d = 0; d < DTL; ++d)
+        o[d] = f32x16{};
+
+    // K fragment offsets within a stage: key col, elements 16 kk + 8 hf ..
+    uint32_t koff[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+        koff[kk] = (uint32_t)stage_slot<CPR>(col, 2 * kk + hf) * 16;
+    // V^T fragment offsets (transpose reads): group g = lane / 16 covers value
+    // columns 16 (g % 2) .. + 15 of a 32-wide tile and keys 4 (g / 2) + 0..3 of
+    // each 8-key run; lane L of the group addresses key 4 (g / 2) + L / 4,
+    // columns 4 (L % 4) .. + 3
+    const int g = lane >> 4, Lg = lane & 15;
+    const uint32_t voff = ((uint32_t)(4 * (g >> 1) + (Lg >> 2)) * D + 16 * (g & 1) + 4 * (Lg & 3)) * 2;
+
+    auto compute_block = [&](int b, const unsigned char *kst, const unsigned char *vst) {
+        // valid keys of the block (bit r), the same in every lane
+        const uint64_t vm = ballot(lane < 32 && block_row(b, lane) >= 0);
+        // S^T: lane holds head col, keys 8 (i / 4) + 4 hf + i % 4
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kst + koff[kk]);
+            s = mfma32<DT>(kf, qf[kk], s);
+        }
+        float mx = -__builtin_huge_valf();
+        const uint32_t mh = (uint32_t)(vm >> (4 * hf));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = 8 * (i >> 2) + (i & 3);
+            float x = s[i] * scale_log2;
+            if ((vm & 0xFFFFFFFFull) != 0xFFFFFFFFull)
+                x = (mh >> key) & 1u ? x : -__builtin_huge_valf();
+            s[i] = x;
+            mx = fmaxf(mx, x);
+        }
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                             __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        // lazy rescale: move the base only when the block's maximum is more
+        // than 2^8 above it
+        if (ballot(mx > m_base + 8.f)) {
+            const bool move = mx > m_base + 8.f;
+            const float nbase = move ? mx : m_base;
+            // 0 when the old base is -inf; 1 for a head whose base stays
+            const float alpha = move ? exp2f(m_base - nbase) : 1.f;
+            m_base = nbase;
+            l_part *= alpha;
+#pragma unroll
+            for (int d = 0; d < DTL; ++d)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    o[d][i] *= alpha;
+        }
+        const float base = m_base == -__builtin_huge_valf() ? 0.f : m_base;
+        uint32_t pk[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const float p0 = exp2f(s[i] - base);
+            const float p1 = exp2f(s[i + 1] - base);
+            l_part += p0 + p1;
+            pk[i >> 1] = pack2<DT>(p0, p1);
+        }
+        // O^T += V^T . P^T over the block's two 16-key steps
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const u32x4 pf = {pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]};
+#pragma unroll
+            for (int d = 0; d < DTL; ++d) {
+                const unsigned char *vb = vst + voff + (uint32_t)(16 * st * D + 32 * d) * 2;
+                const uint64_t lo4 = lds_read_tr16(vb);
+                const uint64_t hi4 = lds_read_tr16(vb + 8 * D * 2);
+                const u32x4 vf = {(uint32_t)lo4, (uint32_t)(lo4 >> 32), (uint32_t)hi4,
+                                  (uint32_t)(hi4 >> 32)};
+                o[d] = mfma32<DT>(vf, pf, o[d]);
+            }
+        }
+    };
+
+    if (nb > 0) {
+        load_block(0, ks0, vs0);
+        wait_vmcnt<0>(); // block 0 and the query fragments
+        __syncthreads();
+        // two blocks per iteration, so that every stage offset is a constant
+        for (int b = 0;;) {
+            if (b + 1 < nb)
+                load_block(b + 1, ks1, vs1);
+            compute_block(b, ks0, vs0);
+            wait_vmcnt<0>();
+            lds_barrier();
+            if (++b >= nb)
+                break;
+            if (b + 1 < nb)
+                load_block(b + 1, ks0, vs0);
+            compute_block(b, ks1, vs1);
+            wait_vmcnt<0>();
+            lds_barrier();
+            if (++b >= nb)
+                break;
+        }
+    }
+
+    // o = O / l for head col (the two halves' parts of l added)
+    float l = add_other_half(l_part);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float *ot = out + ((long long)t * HA + wave * 32 + col) * D;
+#pragma unroll
+    for (int d = 0; d < DTL; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float4 v;
+            v.x = o[d][4 * r] * inv;
+            v.y = o[d][4 * r + 1] * inv;
+            v.z = o[d][4 * r + 2] * inv;
+            v.w = o[d][4 * r + 3] * inv;
+            *reinterpret_cast<float4 *>(ot + 32 * d + 8 * r + 4 * hf) = v;
+        }
+}
+
+template <int WAVES, int D>
+hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
+{
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+    if (a.dtype == kF16)
+        return launch_kernel(sparse_attention_kernel<WAVES, D, kF16>, dim3(a.T), dim3(WAVES * 64), 0,
+                             st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
+                             a.L, a.topk, a.window, scale_log2, a.out);
+    return launch_kernel(sparse_attention_kernel<WAVES, D, kBF16>, dim3(a.T), dim3(WAVES * 64), 0,
+                         st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N, a.L,
+                         a.topk, a.window, scale_log2, a.out);
+}
+
+} // namespace
+
+bool attention_supported(int HA, int D, int dtype)
+{
+    return (HA == 32 || HA == 64 || HA == 128) && (D == 64 || D == 128) &&
+           (dtype == kF16 || dtype == kBF16);
+}
+
+hipError_t launch_sparse_attention(const AttnProblem &a, hipStream_t st, Timing *tm)
+{
+    if (a.T <= 0)
+        return hipSuccess;
+#define DSI_ATTN(w, d)                                                                    \
+    if (a.HA == 32 * w && a.D == d)                                                       \
+        return attn_one<w, d>(a, st, tm);
+    DSI_ATTN(1, 64) DSI_ATTN(1, 128) DSI_ATTN(2, 64) DSI_ATTN(2, 128) DSI_ATTN(4, 64)
+    DSI_ATTN(4, 128)
+#undef DSI_ATTN
+    return hipErrorInvalidValue;
+}
+
+} // namespace dsi

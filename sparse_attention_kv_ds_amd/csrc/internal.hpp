@@ -27,6 +27,10 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds
 {
     hipEvent_t e0 = tm && first ? tm->start : nullptr;
     hipEvent_t e1 = tm && last ? tm->stop : nullptr;
+    // the runtime's last-error slot may still hold the result of an unrelated
+    // earlier call (a query answered "not ready", say): clear it, so that the
+    // check below reports this launch only
+    (void)hipGetLastError();
     if (e0 || e1)
         hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u,
                               static_cast<P>(args)...);
@@ -85,5 +89,23 @@ hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int r
 
 // p[0..n) = v
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st);
+
+// sparse attention over the selected rows (attention.hip)
+constexpr int kAttnMaxTopk = 2048; // index-list entries per token held in LDS
+
+struct AttnProblem {
+    const void *q;        // [T][HA][D] raw fp16/bf16 bits
+    const void *kp, *vp;  // [N][D] pooled rows
+    const void *kl, *vl;  // [L][D] raw rows by absolute position
+    const int32_t *idx;   // [T][topk]
+    const int32_t *pos;   // [T]
+    int T, N, L, HA, D, topk, window, dtype;
+    float scale;
+    float *out;           // [T][HA][D] fp32
+};
+
+bool attention_supported(int HA, int D, int dtype);
+
+hipError_t launch_sparse_attention(const AttnProblem &a, hipStream_t st, Timing *tm = nullptr);
 
 } // namespace dsi

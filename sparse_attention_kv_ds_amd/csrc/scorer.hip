@@ -501,6 +501,7 @@ hipError_t launch_fill(float *p, long long n, float v, hipStream_t st)
     long long blocks = (n + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;
+    (void)hipGetLastError(); // (see launch_kernel)
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
     return hipGetLastError();
 }

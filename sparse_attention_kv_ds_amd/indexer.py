@@ -33,7 +33,7 @@ KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select")
 
 EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
-           "ds_indexer_timing_read")
+           "ds_indexer_timing_read", "ds_sparse_attention")
 
 
 class IndexerError(RuntimeError):
@@ -44,6 +44,10 @@ class IndexerError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch first: its HIP runtime must be the one the library binds to, so that
+    # torch's device pointers and stream handles are valid in the library's calls
+    # (loaded the other way round, the process can end up with two runtimes)
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
                           "the indexer has no non-HIP implementation")
@@ -63,6 +67,9 @@ def _load() -> ctypes.CDLL:
     lib.ds_indexer_timing.argtypes = [P, I]
     lib.ds_indexer_timing_read.restype = I
     lib.ds_indexer_timing_read.argtypes = [P, P, P]
+    lib.ds_sparse_attention.restype = I
+    lib.ds_sparse_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
+                                        ctypes.c_float, P, P]
     return lib
 
 
@@ -110,6 +117,12 @@ def ds_indexer_timing_read(handle):
     n = (ctypes.c_int64 * DS_KERNEL_CLASSES)()
     st = _lib.ds_indexer_timing_read(handle, ms, n)
     return st, list(ms), list(n)
+
+
+def ds_sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, T, N, L, n_heads,
+                        head_dim, dtype, topk, window, scale, out, stream) -> int:
+    return _lib.ds_sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, T, N, L,
+                                    n_heads, head_dim, dtype, topk, window, scale, out, stream)
 
 
 # --- torch-facing wrapper -------------------------------------------------------------
@@ -214,3 +227,43 @@ class Indexer:
         if st != DS_OK:
             raise IndexerError(st, "ds_indexer_scores")
         return out
+
+
+def sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, *, window: int,
+                     scale: float, dtype=None, out=None):
+    """Attention of each token's heads over its local raw rows plus the pooled
+    rows listed in idx (ds_sparse_attention).  q [T, HA, D], k_pool/v_pool
+    [N, D], k_local/v_local [L, D] (fp16/bf16 or their raw bits), idx [T, topk]
+    int32, pos [T] int32, all contiguous on one device; returns out [T, HA, D]
+    float32.  Work is enqueued on torch's current stream of that device."""
+    import torch
+    dev = q.device
+    T, HA, D = q.shape
+    N, L = k_pool.shape[0], k_local.shape[0]
+    topk = idx.shape[1] if idx.dim() == 2 else 0
+    if dtype is None:
+        dtype = q.dtype
+    code = _dtype_code(dtype)
+    for name, t_ in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("k_local", k_local),
+                     ("v_local", v_local), ("idx", idx), ("pos", pos)):
+        if t_.device != dev or not t_.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    for name, t_ in (("k_pool", k_pool), ("v_pool", v_pool), ("k_local", k_local),
+                     ("v_local", v_local)):
+        if t_.element_size() != 2 or (t_.numel() and tuple(t_.shape[1:]) != (D,)):
+            raise ValueError(f"{name} must be [rows, {D}] with 16-bit elements")
+    if idx.dtype != torch.int32 or pos.dtype != torch.int32 or tuple(pos.shape) != (T,):
+        raise ValueError("idx [T, topk] and pos [T] must be int32")
+    if out is None:
+        out = torch.empty((T, HA, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def ptr(t_):
+        return t_.data_ptr() if t_.numel() else None
+
+    st = ds_sparse_attention(ptr(q), ptr(k_pool), ptr(v_pool), ptr(k_local), ptr(v_local),
+                             ptr(idx), pos.data_ptr(), T, N, L, HA, D, code, topk, window,
+                             float(scale), out.data_ptr(), stream)
+    if st != DS_OK:
+        raise IndexerError(st, "ds_sparse_attention")
+    return out

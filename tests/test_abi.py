@@ -20,14 +20,14 @@ def ix():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ds_indexer_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ds_[a-z_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ds_indexer_create", "ds_indexer_score_topk",
                                            "ds_indexer_destroy", "ds_indexer_scores",
                                            "ds_indexer_status_str", "ds_indexer_timing",
-                                           "ds_indexer_timing_read"])
+                                           "ds_indexer_timing_read", "ds_sparse_attention"])
 
 
 def test_every_declared_symbol_is_exported(ix):
@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(ix):
         assert hasattr(lib, name), name
     dyn = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (ds_indexer_\w+)", dyn))
+    exported = set(re.findall(r"\bT (ds_[a-z_]+)\b", dyn))
     assert exported == set(declared_functions())
 
 
@@ -99,3 +99,26 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b|liboracle|oracle_score",
                                      text, flags=re.M), f"{f} reaches into the oracle"
+
+
+def test_sparse_attention_rejects_bad_arguments_on_the_host(ix):
+    """Every rejection happens before any device call (no GPU is used here)."""
+    fake = 0x1000  # never dereferenced: each call below returns before any launch
+    def call(**kw):
+        a = dict(q=fake, k_pool=fake, v_pool=fake, k_local=fake, v_local=fake, idx=fake,
+                 pos=fake, T=4, N=8, L=8, n_heads=64, head_dim=128, dtype=ix.DS_BF16, topk=4,
+                 window=2, scale=0.1, out=fake, stream=None)
+        a.update(kw)
+        return ix.ds_sparse_attention(*a.values())
+    assert call(T=-1) == ix.DS_ERR_INVALID_ARG
+    assert call(window=-1) == ix.DS_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == ix.DS_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == ix.DS_ERR_INVALID_ARG
+    assert call(n_heads=48) == ix.DS_ERR_UNSUPPORTED
+    assert call(head_dim=96) == ix.DS_ERR_UNSUPPORTED
+    assert call(dtype=7) == ix.DS_ERR_UNSUPPORTED
+    assert call(topk=2049) == ix.DS_ERR_UNSUPPORTED
+    assert call(q=None) == ix.DS_ERR_INVALID_ARG
+    assert call(idx=None) == ix.DS_ERR_INVALID_ARG
+    assert call(out=fake + 4) == ix.DS_ERR_INVALID_ARG  # misaligned
+    assert call(T=0, q=None, out=None) == ix.DS_OK      # nothing to do

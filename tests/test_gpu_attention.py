@@ -1,0 +1,162 @@
+"""GPU parity of the sparse attention (ds_sparse_attention) against the CPU oracle.
+
+Tolerance, from the arithmetic of the kernel: scores and softmax run in
+float32; each weight p is rounded to the value type (unit roundoff u = 2^-8
+for bf16, 2^-11 for fp16) before the value product; sums are float32.  So
+|o_gpu - o_exact| <= u * max |value| over the token's rows, plus float32
+rounding of order 1e-6.  The tests allow twice that.  Inputs are seeded and
+synthetic (sparse_attention_kv_ds_amd.synth); the index lists are drawn
+independently of any indexer run.
+"""
+import numpy as np
+import pytest
+
+from sparse_attention_kv_ds_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+@pytest.fixture(scope="module")
+def ix():
+    from sparse_attention_kv_ds_amd import indexer
+    return indexer
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle
+    return oracle.load()
+
+
+def to_dev(d):
+    import torch
+    dev = torch.device("cuda", 0)
+    t = {k: torch.from_numpy(np.ascontiguousarray(d[k]).view(np.int16)).to(dev)
+         for k in ("q", "kp", "vp", "kl", "vl")}
+    t["idx"] = torch.from_numpy(np.ascontiguousarray(d["idx"])).to(dev)
+    t["pos"] = torch.from_numpy(np.ascontiguousarray(d["pos"])).to(dev)
+    return t
+
+
+def run_gpu(ix, d, dtype, window, scale):
+    import torch
+    t = to_dev(d)
+    out = ix.sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], t["idx"], t["pos"],
+                              window=window, scale=scale, dtype=dtype)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def vmax(d, dtype):
+    def dec(b):
+        b = np.asarray(b, dtype=np.uint16)
+        if dtype == "f16":
+            return b.view(np.float16).astype(np.float64)
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    m = 0.0
+    for k in ("vp", "vl"):
+        if d[k].size:
+            m = max(m, float(np.abs(dec(d[k])).max()))
+    return m
+
+
+def check(got, want, d, dtype, where=""):
+    tol = 2 * U[dtype] * vmax(d, dtype) + 1e-5
+    err = np.abs(got - want)
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, (f"{where}: {len(bad)} outputs beyond {tol:.3g}; worst {err.max():.3g} "
+                           f"at {tuple(bad[0])}: got {got[tuple(bad[0])]}, want {want[tuple(bad[0])]}")
+
+
+def test_tiny_workload(ix, orc):
+    d = synth.make_attention("attn_tiny")
+    wl = d["wl"]
+    got = run_gpu(ix, d, wl.dtype, wl.window, wl.scale)
+    want = orc.sparse_attention(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], d["idx"], d["pos"],
+                                dtype=wl.dtype, window=wl.window, scale=wl.scale)
+    check(got, want, d, wl.dtype, "attn_tiny")
+
+
+def random_case(seed, T, N, L, HA, D, topk, dtype, pos_lo, pos_hi, dup=False):
+    rng = np.random.default_rng(seed)
+    sk = 1.0 / np.sqrt(D)
+    d = {"q": synth.to_bits(rng.standard_normal((T, HA, D)) * sk * 2, dtype),
+         "kp": synth.to_bits(rng.standard_normal((N, D)) * sk, dtype),
+         "vp": synth.to_bits(rng.standard_normal((N, D)), dtype),
+         "kl": synth.to_bits(rng.standard_normal((L, D)) * sk, dtype),
+         "vl": synth.to_bits(rng.standard_normal((L, D)), dtype),
+         "pos": rng.integers(pos_lo, pos_hi + 1, size=T).astype(np.int32)}
+    idx = np.full((T, topk), -1, dtype=np.int32)
+    for t in range(T):
+        if topk == 0 or N == 0:
+            continue
+        m = int(rng.integers(0, min(N, topk) + 1))
+        rows = rng.choice(N, size=m, replace=False)
+        if dup and m >= 2:
+            rows[1] = rows[0]
+        slots = np.sort(rng.choice(topk, size=m, replace=False)) if t % 3 == 0 else np.arange(m)
+        idx[t, slots] = np.sort(rows)
+    d["idx"] = idx
+    return d
+
+
+SHAPES = [
+    # (HA, D, dtype, T, N, L, topk, window, pos range)
+    (32, 64, "f16", 40, 100, 300, 16, 8, (-3, 320)),
+    (32, 128, "bf16", 33, 700, 900, 100, 0, (0, 900)),
+    (64, 64, "bf16", 20, 64, 100, 64, 40, (-1, 120)),
+    (64, 128, "f16", 25, 3000, 5000, 512, 128, (4000, 4999)),
+    (64, 128, "bf16", 17, 2000, 4000, 512, 128, (100, 4100)),
+    (128, 64, "f16", 9, 300, 600, 200, 33, (0, 599)),
+    (128, 128, "bf16", 7, 5000, 9000, 512, 64, (8000, 8999)),
+    (64, 128, "bf16", 12, 40, 60, 0, 50, (-2, 70)),      # local rows only
+    (64, 128, "f16", 12, 800, 10, 33, 1, (-2, 20)),      # one local row, pooled rows
+    (32, 64, "bf16", 30, 5, 5, 7, 5, (-10, 10)),         # tiny pools
+    (64, 128, "bf16", 10, 4096, 4200, 2048, 200, (4000, 4199)),  # largest index list
+]
+
+
+@pytest.mark.parametrize("HA,D,dtype,T,N,L,topk,window,prange", SHAPES)
+def test_shapes(ix, orc, HA, D, dtype, T, N, L, topk, window, prange):
+    d = random_case(HA * 7 + D + T, T, N, L, HA, D, topk, dtype, *prange)
+    scale = 1.0 / np.sqrt(D)
+    got = run_gpu(ix, d, dtype, window, scale)
+    want = orc.sparse_attention(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], d["idx"], d["pos"],
+                                dtype=dtype, window=window, scale=scale, threads=8)
+    check(got, want, d, dtype, f"HA={HA} D={D} {dtype}")
+
+
+def test_duplicate_rows_count_twice(ix, orc):
+    d = random_case(3, 16, 300, 400, 64, 128, 64, "bf16", 100, 399, dup=True)
+    got = run_gpu(ix, d, "bf16", 16, 0.09)
+    want = orc.sparse_attention(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], d["idx"], d["pos"],
+                                dtype="bf16", window=16, scale=0.09)
+    check(got, want, d, "bf16", "duplicates")
+
+
+def test_empty_sets_are_zero(ix):
+    d = random_case(5, 8, 50, 60, 64, 128, 16, "f16", -5, -1)
+    d["idx"][:] = -1
+    got = run_gpu(ix, d, "f16", 4, 0.1)
+    assert not got.any()
+
+
+def test_attn32k_sampled_tokens(ix, orc):
+    """The full 2048-token workload in one launch; 64 evenly spaced tokens checked."""
+    d = synth.make_attention("attn32k")
+    wl = d["wl"]
+    got = run_gpu(ix, d, wl.dtype, wl.window, wl.scale)
+    toks = np.linspace(0, wl.T - 1, 64).astype(np.int64)
+    want = orc.sparse_attention(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], d["idx"], d["pos"],
+                                dtype=wl.dtype, window=wl.window, scale=wl.scale, tokens=toks,
+                                threads=16)
+    check(got[toks], want, d, wl.dtype, "attn32k")
+
+
+def test_deterministic(ix):
+    d = random_case(9, 24, 1000, 1500, 64, 128, 256, "bf16", 1000, 1499)
+    a = run_gpu(ix, d, "bf16", 64, 0.088)
+    b = run_gpu(ix, d, "bf16", 64, 0.088)
+    assert np.array_equal(a, b)
