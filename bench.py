@@ -9,10 +9,12 @@ before the timed region.  The headline value is scored pairs per second
 (sum over tokens of visible rows / step time); query tokens per second is
 reported beside it.
 
-The same run also times the 64k chunk (bf16 Gaussian, 16384 rows) and the
+The same run also times the 64k chunk (bf16 Gaussian, 16384 rows), the
 single-token decode at the 1M window (262144 rows, 64 MiB of K streamed per
 call, 8 distinct K buffers rotated so every call reads HBM rather than the
-256 MB last-level cache), and times the CPU oracle on a bounded token sample of
+256 MB last-level cache) and the sparse attention that consumes the 32k
+chunk's indices (2048 tokens x 64 heads over a 128-row local window plus 512
+listed pooled rows each), and times the CPU oracle on a bounded token sample of
 the headline workload.
 
 The step time is taken over K calls with nothing else on the stream.  The
@@ -142,6 +144,66 @@ def time_workload(name: str, steps: int, warmup: int):
     log(f"[bench] {name}: {ms * 1e3:.1f} us/step ({ms_marked * 1e3:.1f} with kernel markers), "
         + ", ".join(f"{c} {v['avg_ms'] * 1e3:.1f} us" for c, v in kernels.items()))
     return res
+
+
+ATTN_WORKLOAD = "attn32k"
+
+
+def time_attention(name: str, steps: int, warmup: int):
+    """Time `steps` calls of the sparse attention (one kernel per call) on one
+    workload; the duration of a call is events around back-to-back calls on
+    the stream the kernel runs on."""
+    import numpy as np
+    import torch
+    from sparse_attention_kv_ds_amd import synth
+    from sparse_attention_kv_ds_amd.indexer import sparse_attention
+
+    dev = torch.device("cuda", 0)
+    d = synth.make_attention(name)
+    wl = d["wl"]
+    t = {k: torch.from_numpy(np.ascontiguousarray(d[k]).view(np.int16)).to(dev)
+         for k in ("q", "kp", "vp", "kl", "vl")}
+    idx = torch.from_numpy(d["idx"]).to(dev)
+    pos = torch.from_numpy(d["pos"]).to(dev)
+    out = torch.empty((wl.T, wl.HA, wl.DV), dtype=torch.float32, device=dev)
+
+    def call():
+        sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], idx, pos, window=wl.window,
+                         scale=wl.scale, dtype=wl.dtype, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize(dev)
+    ms = a.elapsed_time(b) / steps
+    # rows attended per token: the local window (clamped to positions 0..L-1)
+    # plus the listed pooled rows
+    p = wl.positions.astype(np.int64)
+    lo = np.maximum(0, p - wl.window + 1)
+    hi = np.minimum(p, wl.L - 1)
+    n_loc = np.where((p >= 0) & (wl.window > 0), np.maximum(0, hi - lo + 1), 0)
+    n_pool = ((d["idx"] >= 0) & (d["idx"] < wl.N)).sum(axis=1)
+    rows = int((n_loc + n_pool).sum())
+    flops = 2.0 * wl.HA * (wl.DK + wl.DV) * rows
+    ach = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    byt = (wl.T * wl.HA * wl.DK * 2 + wl.N * (wl.DK + wl.DV) * 2 + wl.L * (wl.DK + wl.DV) * 2
+           + d["idx"].nbytes + wl.T * 4 + wl.T * wl.HA * wl.DV * 4)
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/call, {rows / wl.T:.0f} rows per token, "
+        f"{ach:.0f} TFLOP/s ({ach / peak * 100:.1f} % of {wl.dtype} MFMA peak)")
+    return {"workload": name, "dtype": wl.dtype, "ms_per_step": ms,
+            "value": wl.T / (ms * 1e-3), "unit": "query tokens/s",
+            "rows_attended_per_token": rows / wl.T,
+            "roofline": {"bound": "mfma", "kernel": "sparse_attention", "achieved": ach,
+                         "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                         "algorithmic_flops_per_launch": flops,
+                         "input_output_bytes_per_launch": byt}}
 
 
 def stored_traffic(cls: str, workload: str):
@@ -424,7 +486,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY])
+    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
@@ -464,6 +526,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    if args.only == ATTN_WORKLOAD:
+        res = time_attention(args.only, args.steps, args.warmup)
+        print(json.dumps({k: v for k, v in res.items()}))
+        return 0
     if args.only:
         res = time_workload(args.only, args.steps, args.warmup)
         print(json.dumps({"workload": args.only, "ms_per_step": res["ms_per_step"],
@@ -510,6 +576,8 @@ def main():
             entry.update({"value": r["pairs_per_s"], "unit": "pairs/s",
                           "query_tokens_per_s": r["query_tokens_per_s"]})
         line["secondary"].append(entry)
+    # the consumer of the indices (sparse attention over the selected rows)
+    line["secondary"].append(time_attention(ATTN_WORKLOAD, args.steps, min(args.warmup, 50)))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(HEADLINE)
     print(json.dumps(line))
