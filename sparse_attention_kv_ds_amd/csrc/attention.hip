@@ -44,6 +44,24 @@ __device__ __forceinline__ uint64_t lds_read_tr16(const void *p)
     return __builtin_bit_cast(uint64_t, r);
 }
 
+// c ? a : b between two values.  Inside a lambda that captures by reference,
+// a conditional expression over captured names becomes a choice between
+// their addresses, which keeps the captured variables in scratch memory; as
+// function arguments they are read first and only the values are chosen.
+template <class T>
+__device__ __forceinline__ T pick(bool c, T a, T b)
+{
+    return c ? a : b;
+}
+
+// 2^x by the hardware instruction alone (no rescaling of results below
+// 2^-126: every p here is at most 2^8 and the largest is at least 1, so such
+// terms are far below the rounding of the sum)
+__device__ __forceinline__ float exp2_fast(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
 // two floats -> two 16-bit values of type DT (round to nearest even)
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b)
@@ -78,7 +96,8 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     static_assert(2 * LPB % WAVES == 0, "block loads split evenly over the waves");
     static_assert(LPW <= 16, "vmcnt headroom");
 
-    __shared__ int32_t ids[kAttnMaxTopk];
+    // the token's index list, padded with -1 to whole blocks (sized at launch)
+    extern __shared__ int32_t ids[];
     // one array per stage and tensor, so that the compiler can tell that the
     // loads into one stage do not touch the fragment reads of the other
     __shared__ __attribute__((aligned(1024))) unsigned char ks0[BLK_B];
@@ -98,11 +117,14 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         n_loc = max(0, min(p, L - 1) - lo + 1);
     }
     const int nb_loc = (n_loc + 31) >> 5;
-    const int nb = nb_loc + ((topk + 31) >> 5);
+    const int nb_pool = (topk + 31) >> 5;
+    const int nb = nb_loc + nb_pool;
 
-    // the token's index list (entries outside [0, N) are padding)
-    for (int e = threadIdx.x; e < topk; e += WAVES * 64)
-        ids[e] = idx[(long long)t * topk + e];
+    // entries outside [0, N) and the padding become -1 (empty slots)
+    for (int e = threadIdx.x; e < 32 * nb_pool; e += WAVES * 64) {
+        const int j = e < topk ? idx[(long long)t * topk + e] : -1;
+        ids[e] = (uint32_t)j < (uint32_t)N ? j : -1;
+    }
 
     // this wave's 32 heads as MFMA B fragments: head col, elements 16 kk + 8 hf ..
     const auto rq = make_rsrc(q + ((long long)t * HA + wave * 32) * D, 32u * D * 2);
@@ -112,48 +134,48 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         qf[kk] = buf_load16(rq, ((uint32_t)col * D + kk * 16 + hf * 8) * 2);
     __syncthreads(); // the index list
 
-    const auto rkp = make_rsrc(kp, (uint32_t)N * D * 2);
-    const auto rvp = make_rsrc(vp, (uint32_t)N * D * 2);
-    const auto rkl = make_rsrc(kl, (uint32_t)L * D * 2);
-    const auto rvl = make_rsrc(vl, (uint32_t)L * D * 2);
+    const uint32_t bytes_p = (uint32_t)N * D * 2, bytes_l = (uint32_t)L * D * 2;
 
-    // row of key slot r (0..31) of block b, or -1 when the slot is empty
-    auto block_row = [&](int b, int r) -> int {
-        if (b < nb_loc) {
-            const int k = 32 * b + r;
-            return k < n_loc ? lo + k : -1;
-        }
-        const int e = 32 * (b - nb_loc) + r;
-        const int j = e < topk ? ids[e] : -1;
-        return (j >= 0 && j < N) ? j : -1;
-    };
-    // this wave's share of block b's K and V rows into the given stage: load u
-    // of the block fills 16-byte units [64 i, 64 i + 64) of K (u < LPB, i = u)
-    // or of V (i = u - LPB), lane by lane; K rows are chunk-swizzled, V rows are
-    // plain (the transpose reads want whole 8-byte runs of a row)
+    // Loads of a block: 1 KiB load i (0 <= i < LPB) of a tensor covers rows
+    // RPL i .. RPL i + RPL-1, lane by lane (row RPL i + lane / CPR, 16-byte
+    // chunk lane % CPR; K chunks swizzled, V rows plain, as the transpose reads
+    // want whole 8-byte runs of a row).  With several waves, the first half
+    // loads K and the second half V, each wave NI consecutive loads from i0; a
+    // single wave loads both.
+    constexpr int NI = LPW < LPB ? LPW : LPB;
+    const int i0 = WAVES == 1 ? 0 : (wave % (WAVES / 2 > 0 ? WAVES / 2 : 1)) * NI;
+    const int pc = lane % CPR;
+
     auto load_block = [&](int b, unsigned char *kst, unsigned char *vst) {
+        // this lane's row of each of its loads, -1 for an empty slot (the
+        // pooled rows come from the index list in one round of LDS reads)
+        int row[NI];
         const bool local = b < nb_loc;
+        if (local) {
 #pragma unroll
-        for (int x = 0; x < LPW; ++x) {
-            const int u = wave * LPW + x;
-            const bool isk = u < LPB;
-            const int i = isk ? u : u - LPB;
-            const int r = i * RPL + lane / CPR;
-            const int pc = lane % CPR;
-            const int row = block_row(b, r);
-            const int c = isk ? pc ^ ((r / (16 / CPR)) % CPR) : pc;
-            const uint32_t off = row >= 0 ? ((uint32_t)row * CPR + c) * 16 : kOffNone;
-            unsigned char *dst = (isk ? kst : vst) + i * 1024;
-            if (isk) {
-                if (local)
-                    buf_load16_lds(rkl, dst, off);
-                else
-                    buf_load16_lds(rkp, dst, off);
-            } else {
-                if (local)
-                    buf_load16_lds(rvl, dst, off);
-                else
-                    buf_load16_lds(rvp, dst, off);
+            for (int n = 0; n < NI; ++n) {
+                const int k = 32 * b + (i0 + n) * RPL + lane / CPR;
+                row[n] = k < n_loc ? lo + k : -1;
+            }
+        } else {
+            const int32_t *e = ids + 32 * (b - nb_loc) + i0 * RPL + lane / CPR;
+#pragma unroll
+            for (int n = 0; n < NI; ++n)
+                row[n] = e[n * RPL];
+        }
+        const uint32_t bytes = local ? bytes_l : bytes_p;
+#pragma unroll
+        for (int ten = 0; ten < (WAVES == 1 ? 2 : 1); ++ten) {
+            const bool isk = WAVES == 1 ? ten == 0 : wave < WAVES / 2;
+            const uint16_t *base = pick(isk, pick(local, kl, kp), pick(local, vl, vp));
+            const auto r = make_rsrc(base, bytes);
+            unsigned char *st = isk ? kst : vst;
+#pragma unroll
+            for (int n = 0; n < NI; ++n) {
+                const int rr = (i0 + n) * RPL + lane / CPR; // row slot in the block
+                const int c = isk ? pc ^ ((rr / (16 / CPR)) % CPR) : pc;
+                const uint32_t off = row[n] >= 0 ? ((uint32_t)row[n] * CPR + c) * 16 : kOffNone;
+                buf_load16_lds(r, st + (i0 + n) * 1024, off);
             }
         }
     };
@@ -181,7 +203,12 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
 
     auto compute_block = [&](int b, const unsigned char *kst, const unsigned char *vst) {
         // valid keys of the block (bit r), the same in every lane
-        const uint64_t vm = ballot(lane < 32 && block_row(b, lane) >= 0);
+        bool valid;
+        if (b < nb_loc)
+            valid = 32 * b + col < n_loc;
+        else
+            valid = ids[32 * (b - nb_loc) + col] >= 0;
+        const uint64_t vm = ballot(lane < 32 && valid);
         // S^T: lane holds head col, keys 8 (i / 4) + 4 hf + i % 4
         f32x16 s = f32x16{};
 #pragma unroll
@@ -211,7 +238,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             const bool move = mx > m_base + 8.f;
             const float nbase = move ? mx : m_base;
             // 0 when the old base is -inf; 1 for a head whose base stays
-            const float alpha = move ? exp2f(m_base - nbase) : 1.f;
+            const float alpha = move ? exp2_fast(m_base - nbase) : 1.f;
             m_base = nbase;
             l_part *= alpha;
 #pragma unroll
@@ -224,8 +251,8 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-            const float p0 = exp2f(s[i] - base);
-            const float p1 = exp2f(s[i + 1] - base);
+            const float p0 = exp2_fast(s[i] - base);
+            const float p1 = exp2_fast(s[i + 1] - base);
             l_part += p0 + p1;
             pk[i >> 1] = pack2<DT>(p0, p1);
         }
@@ -289,13 +316,15 @@ template <int WAVES, int D>
 hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
 {
     const float scale_log2 = a.scale * 1.4426950408889634f;
+    // the index list, padded to whole blocks of 32
+    const size_t lds = (size_t)((a.topk + 31) / 32 * 32 + 1) * sizeof(int32_t);
     if (a.dtype == kF16)
-        return launch_kernel(sparse_attention_kernel<WAVES, D, kF16>, dim3(a.T), dim3(WAVES * 64), 0,
-                             st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
-                             a.L, a.topk, a.window, scale_log2, a.out);
-    return launch_kernel(sparse_attention_kernel<WAVES, D, kBF16>, dim3(a.T), dim3(WAVES * 64), 0,
-                         st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N, a.L,
-                         a.topk, a.window, scale_log2, a.out);
+        return launch_kernel(sparse_attention_kernel<WAVES, D, kF16>, dim3(a.T), dim3(WAVES * 64),
+                             lds, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos,
+                             a.N, a.L, a.topk, a.window, scale_log2, a.out);
+    return launch_kernel(sparse_attention_kernel<WAVES, D, kBF16>, dim3(a.T), dim3(WAVES * 64),
+                         lds, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
+                         a.L, a.topk, a.window, scale_log2, a.out);
 }
 
 } // namespace
