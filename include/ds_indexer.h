@@ -195,9 +195,9 @@ const char *ds_indexer_status_str(int status);
  * the largest |value| in the token's rows.
  *
  * Returns DS_OK, DS_ERR_INVALID_ARG (a null pointer where one is needed,
- * misalignment, negative sizes, non-finite scale), DS_ERR_UNSUPPORTED (head
- * count, head dim, dtype or topk outside the list above) or DS_ERR_HIP
- * (launch failure).  Arguments are checked on the host before any launch;
+ * misalignment, negative sizes, a scale that is not positive and finite),
+ * DS_ERR_UNSUPPORTED (head count, head dim, dtype or topk outside the list
+ * above) or DS_ERR_HIP (launch failure).  Arguments are checked on the host before any launch;
  * positions and index values are not read on the host.
  */
 int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,

@@ -23,7 +23,8 @@ SOURCES = ["api.cpp", "scorer.hip", "topk.hip", "attention.hip"]
 # costs an extra canonicalising instruction.
 # MFMA accumulators are kept in ordinary VGPRs (the epilogue reads them with
 # VALU instructions; in AGPRs every read would cost an extra move).
-EXTRA = {"scorer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"scorer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

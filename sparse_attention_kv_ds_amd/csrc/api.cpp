@@ -329,8 +329,9 @@ int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
                         int head_dim, int dtype, int topk, int window, float scale, float *out,
                         void *stream)
 {
-    if (T < 0 || N < 0 || L < 0 || topk < 0 || window < 0 || !(scale == scale) ||
-        scale > 3.0e38f || scale < -3.0e38f)
+    // the softmax temperature is a positive finite number (the kernel takes
+    // each head's maximum on the unscaled scores)
+    if (T < 0 || N < 0 || L < 0 || topk < 0 || window < 0 || !(scale > 0.f) || scale > 3.0e38f)
         return DS_ERR_INVALID_ARG;
     if (!dsi::attention_supported(n_heads, head_dim, dtype) || topk > dsi::kAttnMaxTopk)
         return DS_ERR_UNSUPPORTED;

@@ -209,6 +209,8 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         else
             valid = ids[32 * (b - nb_loc) + col] >= 0;
         const uint64_t vm = ballot(lane < 32 && valid);
+        if (vm == 0)
+            return; // nothing to attend in this block
         // S^T: lane holds head col, keys 8 (i / 4) + 4 hf + i % 4
         f32x16 s = f32x16{};
 #pragma unroll
@@ -216,21 +218,25 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             const u32x4 kf = *reinterpret_cast<const u32x4 *>(kst + koff[kk]);
             s = mfma32<DT>(kf, qf[kk], s);
         }
-        float mx = -__builtin_huge_valf();
-        const uint32_t mh = (uint32_t)(vm >> (4 * hf));
+        // empty key slots (partial blocks only) score -inf
+        if ((uint32_t)vm != 0xFFFFFFFFu) {
+            const uint32_t mh = (uint32_t)(vm >> (4 * hf));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = 8 * (i >> 2) + (i & 3);
-            float x = s[i] * scale_log2;
-            if ((vm & 0xFFFFFFFFull) != 0xFFFFFFFFull)
-                x = (mh >> key) & 1u ? x : -__builtin_huge_valf();
-            s[i] = x;
-            mx = fmaxf(mx, x);
+            for (int i = 0; i < 16; ++i) {
+                const int key = 8 * (i >> 2) + (i & 3);
+                s[i] = (mh >> key) & 1u ? s[i] : -__builtin_huge_valf();
+            }
         }
+        // the block's maximum of the head in the log2 domain (the scale is
+        // positive, so it is the scaled maximum of the raw scores)
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            mx = fmaxf(mx, s[i]);
         {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
                                                              __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
         }
         // lazy rescale: move the base only when the block's maximum is more
         // than 2^8 above it
@@ -247,12 +253,12 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
                 for (int i = 0; i < 16; ++i)
                     o[d][i] *= alpha;
         }
-        const float base = m_base == -__builtin_huge_valf() ? 0.f : m_base;
+        const float nb2 = m_base == -__builtin_huge_valf() ? 0.f : -m_base;
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-            const float p0 = exp2_fast(s[i] - base);
-            const float p1 = exp2_fast(s[i + 1] - base);
+            const float p0 = exp2_fast(fmaf(s[i], scale_log2, nb2));
+            const float p1 = exp2_fast(fmaf(s[i + 1], scale_log2, nb2));
             l_part += p0 + p1;
             pk[i >> 1] = pack2<DT>(p0, p1);
         }

@@ -114,6 +114,8 @@ def test_sparse_attention_rejects_bad_arguments_on_the_host(ix):
     assert call(window=-1) == ix.DS_ERR_INVALID_ARG
     assert call(scale=float("nan")) == ix.DS_ERR_INVALID_ARG
     assert call(scale=float("inf")) == ix.DS_ERR_INVALID_ARG
+    assert call(scale=0.0) == ix.DS_ERR_INVALID_ARG
+    assert call(scale=-0.1) == ix.DS_ERR_INVALID_ARG
     assert call(n_heads=48) == ix.DS_ERR_UNSUPPORTED
     assert call(head_dim=96) == ix.DS_ERR_UNSUPPORTED
     assert call(dtype=7) == ix.DS_ERR_UNSUPPORTED
