@@ -44,6 +44,15 @@ __device__ __forceinline__ uint64_t lds_read_tr16(const void *p)
     return __builtin_bit_cast(uint64_t, r);
 }
 
+// Swizzle of V row r in LDS: its 16-byte chunks are XORed with 4 vswz(r), so
+// that rows r, r+1, r+2, r+3 (D = 128: 256-byte rows) or r .. r+7 (D = 64)
+// put the same 32 columns on four different 64-byte quarters of the banks.
+template <int D>
+__device__ __forceinline__ int vswz(int r)
+{
+    return D == 128 ? (r & 3) : ((r >> 1) & 1);
+}
+
 // c ? a : b between two values.  Inside a lambda that captures by reference,
 // a conditional expression over captured names becomes a choice between
 // their addresses, which keeps the captured variables in scratch memory; as
@@ -92,12 +101,8 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     constexpr int RPL = 64 / CPR;         // rows per 1 KiB load
     constexpr int BLK_B = 32 * D * 2;     // bytes of 32 rows
     constexpr int LPB = BLK_B / 1024;     // 1 KiB loads per block and tensor
-    constexpr int LPW = 2 * LPB / WAVES;  // loads per wave per block (K and V)
-    static_assert(2 * LPB % WAVES == 0, "block loads split evenly over the waves");
-    static_assert(LPW <= 16, "vmcnt headroom");
 
-    // the token's index list, padded with -1 to whole blocks (sized at launch)
-    extern __shared__ int32_t ids[];
+    __shared__ int32_t ids[kAttnMaxTopk];
     // one array per stage and tensor, so that the compiler can tell that the
     // loads into one stage do not touch the fragment reads of the other
     __shared__ __attribute__((aligned(1024))) unsigned char ks0[BLK_B];
@@ -139,19 +144,19 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     // Loads of a block: 1 KiB load i (0 <= i < LPB) of a tensor covers rows
     // RPL i .. RPL i + RPL-1, lane by lane (row RPL i + lane / CPR, 16-byte
     // chunk lane % CPR; K chunks swizzled, V rows plain, as the transpose reads
-    // want whole 8-byte runs of a row).  With several waves, the first half
-    // loads K and the second half V, each wave NI consecutive loads from i0; a
-    // single wave loads both.
-    constexpr int NI = LPW < LPB ? LPW : LPB;
-    const int i0 = WAVES == 1 ? 0 : (wave % (WAVES / 2 > 0 ? WAVES / 2 : 1)) * NI;
+    // want whole 8-byte runs of a row).  Wave w issues loads i0 .. i0 + NI - 1
+    // of both tensors: the rows, not the tensors, are split over the waves
+    // (measured: with one wave per tensor the same gather takes about twice
+    // as long).
+    constexpr int NI = LPB / WAVES;
+    static_assert(NI >= 1 && NI * WAVES == LPB, "block loads split evenly over the waves");
+    const int i0 = wave * NI;
     const int pc = lane % CPR;
 
-    auto load_block = [&](int b, unsigned char *kst, unsigned char *vst) {
-        // this lane's row of each of its loads, -1 for an empty slot (the
-        // pooled rows come from the index list in one round of LDS reads)
-        int row[NI];
-        const bool local = b < nb_loc;
-        if (local) {
+    // this lane's row of each of its loads of block b, -1 for an empty slot
+    // (the pooled rows come from the index list in one round of LDS reads)
+    auto block_rows = [&](int b, int (&row)[NI]) {
+        if (b < nb_loc) {
 #pragma unroll
             for (int n = 0; n < NI; ++n) {
                 const int k = 32 * b + (i0 + n) * RPL + lane / CPR;
@@ -163,21 +168,30 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             for (int n = 0; n < NI; ++n)
                 row[n] = e[n * RPL];
         }
-        const uint32_t bytes = local ? bytes_l : bytes_p;
+    };
+    // this wave's loads of block b of K (isk) or V, rows `row`, into stage st
+    auto issue = [&](int b, const int (&row)[NI], unsigned char *st, bool isk) {
+        const bool local = b < nb_loc;
+        const uint16_t *base = pick(isk, pick(local, kl, kp), pick(local, vl, vp));
+        const auto r = make_rsrc(base, local ? bytes_l : bytes_p);
 #pragma unroll
-        for (int ten = 0; ten < (WAVES == 1 ? 2 : 1); ++ten) {
-            const bool isk = WAVES == 1 ? ten == 0 : wave < WAVES / 2;
-            const uint16_t *base = pick(isk, pick(local, kl, kp), pick(local, vl, vp));
-            const auto r = make_rsrc(base, bytes);
-            unsigned char *st = isk ? kst : vst;
-#pragma unroll
-            for (int n = 0; n < NI; ++n) {
-                const int rr = (i0 + n) * RPL + lane / CPR; // row slot in the block
-                const int c = isk ? pc ^ ((rr / (16 / CPR)) % CPR) : pc;
-                const uint32_t off = row[n] >= 0 ? ((uint32_t)row[n] * CPR + c) * 16 : kOffNone;
-                buf_load16_lds(r, st + (i0 + n) * 1024, off);
-            }
+        for (int n = 0; n < NI; ++n) {
+            const int rr = (i0 + n) * RPL + lane / CPR; // row slot in the block
+            const int c = isk ? pc ^ ((rr / (16 / CPR)) % CPR) : pc ^ (4 * vswz<D>(rr));
+            const uint32_t off = row[n] >= 0 ? ((uint32_t)row[n] * CPR + c) * 16 : kOffNone;
+            buf_load16_lds(r, st + (i0 + n) * 1024, off);
         }
+    };
+    auto load_rows = [&](int b, unsigned char *st, bool isk) {
+        int row[NI];
+        block_rows(b, row);
+        issue(b, row, st, isk);
+    };
+    auto load_block = [&](int b, unsigned char *kst, unsigned char *vst) {
+        int row[NI];
+        block_rows(b, row);
+        issue(b, row, kst, true);
+        issue(b, row, vst, false);
     };
 
     // per lane: head col of this wave's tile; the two half-waves hold
@@ -197,9 +211,17 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     // V^T fragment offsets (transpose reads): group g = lane / 16 covers value
     // columns 16 (g % 2) .. + 15 of a 32-wide tile and keys 4 (g / 2) + 0..3 of
     // each 8-key run; lane L of the group addresses key 4 (g / 2) + L / 4,
-    // columns 4 (L % 4) .. + 3
+    // columns 4 (L % 4) .. + 3.  V rows are swizzled in 64-byte groups (chunk
+    // c of row r sits at c ^ 4 vswz(r)), so that the eight rows one read
+    // touches fall on all the LDS banks rather than on the same quarter; every
+    // row this lane addresses has the same vswz.
     const int g = lane >> 4, Lg = lane & 15;
-    const uint32_t voff = ((uint32_t)(4 * (g >> 1) + (Lg >> 2)) * D + 16 * (g & 1) + 4 * (Lg & 3)) * 2;
+    const int vsw_lane = vswz<D>(4 * (g >> 1) + (Lg >> 2));
+    uint32_t voffd[DTL];
+#pragma unroll
+    for (int d = 0; d < DTL; ++d)
+        voffd[d] = ((uint32_t)(4 * (g >> 1) + (Lg >> 2)) * D + 32 * (d ^ vsw_lane) + 16 * (g & 1) +
+                    4 * (Lg & 3)) * 2;
 
     auto compute_block = [&](int b, const unsigned char *kst, const unsigned char *vst) {
         // valid keys of the block (bit r), the same in every lane
@@ -268,7 +290,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             const u32x4 pf = {pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]};
 #pragma unroll
             for (int d = 0; d < DTL; ++d) {
-                const unsigned char *vb = vst + voff + (uint32_t)(16 * st * D + 32 * d) * 2;
+                const unsigned char *vb = vst + voffd[d] + (uint32_t)(16 * st * D) * 2;
                 const uint64_t lo4 = lds_read_tr16(vb);
                 const uint64_t hi4 = lds_read_tr16(vb + 8 * D * 2);
                 const u32x4 vf = {(uint32_t)lo4, (uint32_t)(lo4 >> 32), (uint32_t)hi4,
@@ -323,13 +345,12 @@ hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
 {
     const float scale_log2 = a.scale * 1.4426950408889634f;
     // the index list, padded to whole blocks of 32
-    const size_t lds = (size_t)((a.topk + 31) / 32 * 32 + 1) * sizeof(int32_t);
     if (a.dtype == kF16)
         return launch_kernel(sparse_attention_kernel<WAVES, D, kF16>, dim3(a.T), dim3(WAVES * 64),
-                             lds, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos,
+                             0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos,
                              a.N, a.L, a.topk, a.window, scale_log2, a.out);
     return launch_kernel(sparse_attention_kernel<WAVES, D, kBF16>, dim3(a.T), dim3(WAVES * 64),
-                         lds, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
+                         0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
                          a.L, a.topk, a.window, scale_log2, a.out);
 }
 
