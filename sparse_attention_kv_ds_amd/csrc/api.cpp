@@ -34,7 +34,7 @@ struct ds_indexer {
 namespace {
 
 constexpr int kMaxTopk = 2048;
-// single-token path: partitions of kDecodePart rows, at least 16 candidates each
+// single-token path: partitions of kDecodePart rows, at least 8 candidates each
 constexpr int64_t kDecodeMaxRows = (int64_t)dsi::kDecodeMaxParts * dsi::kDecodePart;
 
 struct DeviceGuard {
@@ -59,12 +59,12 @@ bool aligned(const void *p, uintptr_t a)
 }
 
 // candidates kept per decode partition (a power of two): at least twice the
-// k best spread evenly over the partitions and at least 16, while the union of
+// k best spread evenly over the partitions and at least 8, while the union of
 // all lists still fits the merge
 int decode_kp(int64_t N, int topk)
 {
     const int64_t P = (N + dsi::kDecodePart - 1) / dsi::kDecodePart;
-    int64_t kp = 16;
+    int64_t kp = 8;
     while (kp * P < 2 * (int64_t)topk && kp < dsi::kDecodePart)
         kp *= 2;
     while (kp > 1 && P * kp > dsi::kDecodeUnion)
@@ -223,14 +223,17 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
     const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
     hipError_t e;
     if (T == 1 && ix->decode_ok) {
-        const int kp = decode_kp(N, topk);
+        dsi::DecodeLists dl;
+        dl.kp = decode_kp(N, topk);
+        dl.cand = ix->cand;
+        dl.pcount = ix->pcount;
+        dl.pmin = ix->pmin;
         e = timed(ix, DS_KERNEL_DECODE_SCORE, [&](dsi::Timing *tm) {
-            return dsi::launch_decode_scorer(p, topk, ix->S, s, tm);
+            return dsi::launch_decode_scorer(p, topk, ix->S, dl, s, tm);
         });
         if (e == hipSuccess)
             e = timed(ix, DS_KERNEL_DECODE_SELECT, [&](dsi::Timing *tm) {
-                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, kp, ix->cand,
-                                                 ix->pcount, ix->pmin, out, s, tm);
+                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, dl, out, s, tm);
             });
     } else {
         e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
@@ -262,7 +265,7 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
     hipError_t e = dsi::launch_fill(scores, T * N, -__builtin_huge_valf(), s);
     if (e == hipSuccess) {
         if (T == 1 && ix->decode_ok)
-            e = dsi::launch_decode_scorer(p, 0, scores, s);
+            e = dsi::launch_decode_scorer(p, 0, scores, dsi::DecodeLists{}, s);
         else
             e = dsi::launch_prefill_scorer(p, 0, scores, (long long)N, s);
     }

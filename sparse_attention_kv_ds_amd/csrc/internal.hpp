@@ -52,12 +52,12 @@ struct Problem {
     int T, N, ratio, H, D, dtype;
 };
 
-// rows per decode-selection partition
-constexpr int kDecodePart = 1024;
+// rows per decode-selection partition (one decode work-group)
+constexpr int kDecodePart = 512;
 // largest candidate union the decode merge holds in registers (64 per thread)
 constexpr int kDecodeUnion = 16384;
-// most decode partitions: each lists at least 16 candidates
-constexpr int kDecodeMaxParts = kDecodeUnion / 16;
+// most decode partitions: each lists at least 8 candidates
+constexpr int kDecodeMaxParts = kDecodeUnion / 8;
 
 bool scorer_supported(int H, int D, int dtype);
 
@@ -66,10 +66,24 @@ bool scorer_supported(int H, int D, int dtype);
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
                                  hipStream_t st, Timing *tm = nullptr);
 
+// Per-partition candidate lists of the single-token selection: partition p
+// (rows p * kDecodePart ..) lists its exact best kp keys in row order in
+// cand[p * kp ..] (all its rows when they are <= kp, key 0 in unused slots),
+// their number in pcount[p] and the smallest listed key in pmin[p] (0 when
+// the list holds every row).  kp is a power of two,
+// ceil(N / kDecodePart) * kp <= kDecodeUnion.  cand == nullptr: no lists.
+struct DecodeLists {
+    int kp = 0;
+    uint64_t *cand = nullptr;
+    int *pcount = nullptr;
+    uint64_t *pmin = nullptr;
+};
+
 // Same for a single token (T == 1): one work-group per kDecodePart-row
-// partition streams K; writes S[j] for j < n.
-hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st,
-                                Timing *tm = nullptr);
+// partition streams K; writes S[j] for j < n and, with dl.cand, the
+// partition's candidate list.
+hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const DecodeLists &dl,
+                                hipStream_t st, Timing *tm = nullptr);
 
 // Per-token streaming top-k over S rows (one wave per token); skip path for
 // tokens whose visible rows all fit.
@@ -77,15 +91,13 @@ hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos,
                               int ratio, int topk, int32_t *out, hipStream_t st,
                               Timing *tm = nullptr);
 
-// Single-token selection over S[0..n): each kDecodePart-row partition lists
-// its exact best kp keys (in row order) in cand[p*kp ..], their number in
-// pcount[p] and the smallest of them in pmin[p] (0 when the partition's rows
-// all fit); one work-group then merges the lists into the exact top-k (with an
-// exact re-stream of S for partitions whose list may be short).  kp is a power
-// of two, ceil(N / kDecodePart) * kp <= kDecodeUnion.
+// Single-token selection over S[0..n) from the partitions' candidate lists
+// (written by launch_decode_scorer): one work-group merges the lists into the
+// exact top-k, with an exact re-stream of S for partitions whose list may be
+// short.
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
-                                int kp, uint64_t *cand, int *pcount, uint64_t *pmin, int32_t *out,
-                                hipStream_t st, Timing *tm = nullptr);
+                                const DecodeLists &dl, int32_t *out, hipStream_t st,
+                                Timing *tm = nullptr);
 
 // p[0..n) = v
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st);

@@ -18,6 +18,7 @@
 // half-waves.
 #include "common.hpp"
 #include "internal.hpp"
+#include "select.hpp"
 
 namespace dsi {
 
@@ -262,7 +263,8 @@ constexpr int kStreamAux = 2;
 template <int H, int D, int DT, int WAVES, int NB>
 __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
-    const int32_t *__restrict__ pos, int N, int ratio, int min_rows, float *__restrict__ S)
+    const int32_t *__restrict__ pos, int N, int ratio, int min_rows, float *__restrict__ S, int kp,
+    uint64_t *__restrict__ cand, int *__restrict__ pcount, uint64_t *__restrict__ pmin)
 {
     constexpr int KS = D / 16;
     constexpr int MT = H > 32 ? 2 : 1;       // 32-head tiles of the query
@@ -374,6 +376,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
                 wait_vmcnt<2>();
         }
     };
+    float scb[NB]; // this lane's score of row col of each block
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         wait_block(b);
@@ -406,8 +409,63 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
                 s1 = fmaf(wr[mt][i + 1], fmaxf(acc[mt][i + 1], 0.f), s1);
             }
         const float sc = add_other_half(s0 + s1);
+        scb[b] = sc;
         // rows >= n dropped
         buf_store_f32(rs, hf == 0 ? (uint32_t)(wrow + b * 32 + col) * 4 : kOffNone, sc);
+    }
+    if (cand == nullptr)
+        return;
+
+    // The work-group's rows are one selection partition: list its kp best keys
+    // in row order (all its rows when they are <= kp, key 0 in unused slots),
+    // their number in pcount and the smallest listed key in pmin (0 when the
+    // list holds every row).  The scores go through LDS (each wave's first
+    // slot: its loads have all landed and been read) to one wave, which
+    // selects without barriers.  (Taking the best keys by rounds of wave
+    // maxima instead of the threshold search measured slower.)
+    constexpr int ROWS = WAVES * NB * 32;
+    constexpr int E = ROWS / 64; // keys per lane
+    static_assert(ROWS == kDecodePart, "a decode work-group covers one selection partition");
+    float *const mine = reinterpret_cast<float *>(kst0 + wave * BLK_B);
+    if (hf == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            mine[b * 32 + col] = scb[b];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    const int rows = min(ROWS, n - r0);
+    uint32_t hi[E], lo[E];
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+        const int i = s * 64 + lane; // row r0 + i, held by wave i / (NB * 32)
+        const float v = reinterpret_cast<const float *>(kst0 + (i / (NB * 32)) * BLK_B)[i % (NB * 32)];
+        const uint64_t key = i < rows ? make_key(v, (uint32_t)(r0 + i)) : 0ull;
+        hi[s] = (uint32_t)(key >> 32);
+        lo[s] = (uint32_t)key;
+    }
+    uint64_t t = 1ull; // every valid key is >= 1
+    if (rows > kp) {
+        WaveReduce red;
+        t = select_bound<E>(hi, lo, E, rows, kp, 0, red); // the kp-th best key
+    }
+    uint64_t *list = cand + (size_t)blockIdx.x * kp;
+    int nc = 0;
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+        const uint64_t key = ((uint64_t)hi[s] << 32) | lo[s];
+        const bool keep = key >= t;
+        const uint64_t m = ballot(keep);
+        if (keep)
+            list[nc + mbcnt(m)] = key;
+        nc += popc(m);
+    }
+    for (int i = nc + lane; i < kp; i += 64)
+        list[i] = 0ull;
+    if (lane == 0) {
+        pcount[blockIdx.x] = nc;
+        pmin[blockIdx.x] = rows > kp ? t : 0ull;
     }
 }
 
@@ -433,12 +491,14 @@ constexpr int kDecWaves = 4;  // waves per decode work-group
 constexpr int kDecBlocks = 4; // 32-row K blocks per decode wave
 
 template <int H, int D, int DT>
-hipError_t decode_one(const Problem &p, int min_rows, float *S, hipStream_t st, Timing *tm)
+hipError_t decode_one(const Problem &p, int min_rows, float *S, const DecodeLists &dl,
+                      hipStream_t st, Timing *tm)
 {
     constexpr int ROWS = kDecWaves * kDecBlocks * 32; // per work-group
     return launch_kernel(decode_scorer_kernel<H, D, DT, kDecWaves, kDecBlocks>,
                          dim3((p.N + ROWS - 1) / ROWS), dim3(kDecWaves * 64), 0, st, tm, true,
-                         true, p.q, p.k, p.w, p.pos, p.N, p.ratio, min_rows, S);
+                         true, p.q, p.k, p.w, p.pos, p.N, p.ratio, min_rows, S, dl.kp, dl.cand,
+                         dl.pcount, dl.pmin);
 }
 
 // (H, D, dtype) -> instantiation
@@ -463,9 +523,10 @@ template <int H, int D, int DT> struct PrefillF {
     }
 };
 template <int H, int D, int DT> struct DecodeF {
-    static hipError_t run(const Problem &p, int m, float *S, hipStream_t st, Timing *tm)
+    static hipError_t run(const Problem &p, int m, float *S, const DecodeLists *dl, hipStream_t st,
+                          Timing *tm)
     {
-        return decode_one<H, D, DT>(p, m, S, st, tm);
+        return decode_one<H, D, DT>(p, m, S, *dl, st, tm);
     }
 };
 
@@ -486,12 +547,12 @@ hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long 
     return dispatch<PrefillF>(p.H, p.D, p.dtype, p, min_rows, S, ldS, st, tm);
 }
 
-hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, hipStream_t st,
-                                Timing *tm)
+hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const DecodeLists &dl,
+                                hipStream_t st, Timing *tm)
 {
     if (p.T <= 0 || p.N <= 0)
         return hipSuccess;
-    return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, st, tm);
+    return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, &dl, st, tm);
 }
 
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st)

@@ -135,69 +135,8 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
 }
 
 // ---------------------------------------------------------------------------
-// decode, stage 1: one wave per partition of kDecodePart rows of S lists the
-// partition's kp best keys in row order (all its rows when they are <= kp,
-// then key 0 in the unused slots), their number in pcount[p] and the smallest
-// listed key in pmin[p] (0 when the list holds every row).  16 keys per lane,
-// selected without barriers (one wave's search steps are the cheapest here).
-// ---------------------------------------------------------------------------
-constexpr int kPartWaves = 4;
-
-__global__ __launch_bounds__(kPartWaves * 64) void decode_partition_kernel(
-    const float *__restrict__ S, const int32_t *__restrict__ pos, int N, int ratio, int topk,
-    int kp, uint64_t *__restrict__ cand, int *__restrict__ pcount, uint64_t *__restrict__ pmin)
-{
-    constexpr int E = kDecodePart / 64; // keys per lane
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int p = blockIdx.x * kPartWaves + wave;
-    const int32_t p0 = pos[0];
-    const int r0 = p * kDecodePart;
-    // the scores are fetched before the visible count is known (rows past N read as 0)
-    const auto rs = make_rsrc(S, (uint32_t)N * 4);
-    float sv[E];
-#pragma unroll
-    for (int s = 0; s < E; ++s)
-        sv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rs, (uint32_t)(r0 + s * 64 + lane) * 4, 0, 0));
-    const int n = visible_rows(p0, ratio, N);
-    if (n <= topk || r0 >= n)
-        return; // same for the whole wave
-    const int rows = min(kDecodePart, n - r0);
-    uint32_t hi[E], lo[E];
-    const int rem = rows - lane; // slot s holds a row iff s * 64 < rem
-#pragma unroll
-    for (int s = 0; s < E; ++s) {
-        const uint64_t key = s * 64 < rem ? make_key(sv[s], (uint32_t)(r0 + s * 64 + lane)) : 0ull;
-        hi[s] = (uint32_t)(key >> 32);
-        lo[s] = (uint32_t)key;
-    }
-    uint64_t t = 1ull; // every valid key is >= 1
-    if (rows > kp) {
-        WaveReduce red;
-        t = select_bound<E>(hi, lo, E, rows, kp, 0, red); // the kp-th best key
-    }
-    uint64_t *list = cand + (size_t)p * kp;
-    int nc = 0;
-#pragma unroll
-    for (int s = 0; s < E; ++s) {
-        const uint64_t key = ((uint64_t)hi[s] << 32) | lo[s];
-        const bool keep = key >= t;
-        const uint64_t m = ballot(keep);
-        if (keep)
-            list[nc + mbcnt(m)] = key;
-        nc += popc(m);
-    }
-    for (int i = nc + lane; i < kp; i += 64)
-        list[i] = 0ull; // unused slots hold "no key"
-    if (lane == 0) {
-        pcount[p] = nc;
-        pmin[p] = rows > kp ? t : 0ull;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// decode, stage 2: one work-group merges the partition lists.  With tU the
+// decode selection: one work-group merges the partition lists (written by
+// the decode scorer, one list per work-group of rows).  With tU the
 // k-th best key of their union, the union's top k is the exact answer unless
 // some partition listed only part of its rows and its smallest listed key is
 // above tU (it may hold unlisted rows above tU).  That case falls back to an
@@ -344,17 +283,18 @@ hipError_t topk_stream_one(const float *S, long long ldS, const int32_t *pos, in
 template <int MAXS>
 hipError_t merge_one(const float *S, const int32_t *pos, int N, int ratio, int topk, int kp,
                      const uint64_t *cand, const int *pcount, const uint64_t *pmin, int32_t *out,
-                     hipStream_t st, Timing *tm, bool first)
+                     hipStream_t st, Timing *tm)
 {
     const size_t lds = (size_t)MAXS * 64 * sizeof(uint64_t);
     const long long U = (long long)((N + kDecodePart - 1) / kDecodePart) * kp;
     // four waves: a search step's count and its barrier cost about the same
+    // (sixteen waves, or three pivots per barrier, measured slower)
     constexpr int NT = 256;
     if (U <= 16 * NT)
         return launch_kernel(decode_merge_kernel<MAXS, 16, NT>, dim3(1), dim3(NT), lds, st, tm,
-                             first, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
+                             true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
     return launch_kernel(decode_merge_kernel<MAXS, kDecodeUnion / NT, NT>, dim3(1), dim3(NT), lds,
-                         st, tm, first, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
+                         st, tm, true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
 }
 
 } // namespace
@@ -374,29 +314,18 @@ hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos,
 }
 
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
-                                int kp, uint64_t *cand, int *pcount, uint64_t *pmin, int32_t *out,
-                                hipStream_t st, Timing *tm)
+                                const DecodeLists &dl, int32_t *out, hipStream_t st, Timing *tm)
 {
-    bool first = true; // the merge opens the timed step when there is no partition stage
-    if (N > 0) {
-        const int parts = (N + kDecodePart - 1) / kDecodePart;
-        const hipError_t e = launch_kernel(decode_partition_kernel,
-                                           dim3((parts + kPartWaves - 1) / kPartWaves),
-                                           dim3(kPartWaves * 64), 0, st, tm, true, false, S, pos,
-                                           N, ratio, topk, kp, cand, pcount, pmin);
-        if (e != hipSuccess)
-            return e;
-        first = false;
-    }
+    const int kp = dl.kp;
     switch (select_slots(topk, 64)) {
-    case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
-    case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+    case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
+    case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
     case 16:
-        return merge_one<16>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+        return merge_one<16>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
     case 32:
-        return merge_one<32>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+        return merge_one<32>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
     default:
-        return merge_one<64>(S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, st, tm, first);
+        return merge_one<64>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
     }
 }
 
