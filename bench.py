@@ -26,7 +26,7 @@ that pass's step time is reported apart.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W = 200: the
                        GPU needs some tens of milliseconds of work to reach its full clock)
-       python bench.py --only prefill32k|prefill64k|decode1m   (one workload, for profilers)
+       python bench.py --only prefill32k|prefill64k|decode1m|attn32k   (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --ceilings                               (vendor GEMM and plain-copy
                        rates with the workloads' value distributions)
@@ -60,7 +60,9 @@ SECONDARY = ("prefill64k", "decode1m")
 DECODE_K_BUFFERS = 8
 KERNEL_SOURCES = {  # kernel class -> sources whose change invalidates stored counters
     "score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
-    "decode_score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
+    "decode_score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp",
+                     "sparse_attention_kv_ds_amd/csrc/select.hpp"],
+    "attention": ["sparse_attention_kv_ds_amd/csrc/attention.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -201,7 +203,8 @@ def time_attention(name: str, steps: int, warmup: int):
             "value": wl.T / (ms * 1e-3), "unit": "query tokens/s",
             "rows_attended_per_token": rows / wl.T,
             "roofline": {"bound": "mfma", "kernel": "sparse_attention", "achieved": ach,
-                         "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                         "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                         "traffic": stored_traffic("attention", name),
                          "algorithmic_flops_per_launch": flops,
                          "input_output_bytes_per_launch": byt}}
 
@@ -417,7 +420,8 @@ def _pmc_table(directory: str):
 
 DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
             "prefill32k": ("score", "prefill_scorer_kernel"),
-            "prefill64k": ("score", "prefill_scorer_kernel")}
+            "prefill64k": ("score", "prefill_scorer_kernel"),
+            "attn32k": ("attention", "sparse_attention_kernel")}
 
 
 def record_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch: str, copy_write: str):
