@@ -128,8 +128,9 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
  * call's stream, per class:
  *   DS_KERNEL_SCORE          prefill scorer           (T > 1)
  *   DS_KERNEL_SELECT         prefill per-token top-k  (T > 1)
- *   DS_KERNEL_DECODE_SCORE   single-token scorer      (T == 1)
- *   DS_KERNEL_DECODE_SELECT  single-token selection   (T == 1; both of its kernels)
+ *   DS_KERNEL_DECODE_SCORE   single-token scorer      (T == 1; it also lists each
+ *                            512-row partition's best keys)
+ *   DS_KERNEL_DECODE_SELECT  single-token selection   (T == 1; the merge of those lists)
  * The pages' own evidence is end-to-end prompt throughput with bracketing
  * controls ("How I turned one oversized DeepSeek optimization into three
  * merged oMLX PRs", section "Turn review feedback into an experiment"); this
