@@ -338,6 +338,7 @@ int oracle_score_topk(const uint16_t *q, const uint16_t *k, const float *w, cons
     return status;
 }
 
+
 /* ======================================================================== *
  * Sparse attention over the selected rows (the consumer of the indices).
  *
@@ -355,7 +356,12 @@ int oracle_score_topk(const uint16_t *q, const uint16_t *k, const float *w, cons
  *   rows R(t) = local rows p = max(0, pos_t - window + 1) .. min(pos_t, L-1)
  *               of the raw cache (none when pos_t < 0 or window == 0),
  *             + pooled rows j = idx[t][i] for every entry i with idx >= 0
- *               (entries < 0 are padding; an entry >= N is an error)
+ *               (entries < 0 are padding; an entry >= N is an error),
+ *               or, in the all-visible form (oracle_sparse_attention_all),
+ *               every pooled row the token can see: j = 0 .. n_t - 1 with
+ *               n_t = oracle_visible_rows(pos_t, ratio, N) -- the
+ *               sequential pooled indices that ratio-128 layers attend to
+ *               without an indexer (same section of the oMLX page)
  *   s_r       = scale * sum_d q[t,h,d] * key_r[d]
  *   o[t,h,:]  = sum_r  exp(s_r - max_r s) / sum_r' exp(s_r' - max s) * value_r
  *             = 0 when R(t) is empty.
@@ -373,6 +379,7 @@ typedef struct {
     const int32_t *idx, *pos; /* [T][topk], [T] */
     int64_t T, N, L;
     int HA, DK, DV, topk, window, dtype;
+    int ratio;                /* > 0: every visible pooled row, idx unused */
     double scale;
     const int64_t *tokens;
     int64_t n_out;
@@ -384,7 +391,7 @@ static void *run_attn_job(void *arg)
 {
     attn_job *jb = (attn_job *)arg;
     const int HA = jb->HA, DK = jb->DK, DV = jb->DV;
-    const int64_t cap = (int64_t)jb->topk + (jb->window > 0 ? jb->window : 0);
+    const int64_t cap = (jb->ratio > 0 ? jb->N : (int64_t)jb->topk) + (jb->window > 0 ? jb->window : 0);
     const double **krow = (const double **)malloc(sizeof(double *) * (size_t)(cap > 0 ? cap : 1));
     const double **vrow = (const double **)malloc(sizeof(double *) * (size_t)(cap > 0 ? cap : 1));
     double *s = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
@@ -409,6 +416,14 @@ static void *run_attn_job(void *arg)
             for (r = lo; r <= hi; ++r) {
                 krow[nr] = jb->kl + r * DK;
                 vrow[nr] = jb->vl + r * DV;
+                ++nr;
+            }
+        }
+        if (jb->ratio > 0) {
+            const int64_t nv = oracle_visible_rows(p, jb->ratio, jb->N);
+            for (r = 0; r < nv; ++r) {
+                krow[nr] = jb->kp + r * DK;
+                vrow[nr] = jb->vp + r * DV;
                 ++nr;
             }
         }
@@ -494,13 +509,14 @@ static double *decode_all(const uint16_t *bits, int64_t n, int dtype, int *statu
  *   idx  [T][topk] int32: pooled rows of each token, -1 = padding
  *   pos  [T] int32 absolute positions
  *   out  [n_out][HA][DV] double
+ *   ratio > 0 selects the all-visible form (idx unused, topk 0)
  *
  * Returns ORACLE_OK, ORACLE_ERR_ARG, ORACLE_ERR_NONFINITE or ORACLE_ERR_NOMEM.
  */
-int oracle_sparse_attention(const uint16_t *q, const uint16_t *kp, const uint16_t *vp,
+static int attention_common(const uint16_t *q, const uint16_t *kp, const uint16_t *vp,
                             const uint16_t *kl, const uint16_t *vl, const int32_t *idx,
                             const int32_t *pos, int64_t T, int64_t N, int64_t L, int HA, int DK,
-                            int DV, int topk, int window, double scale, int dtype,
+                            int DV, int topk, int ratio, int window, double scale, int dtype,
                             const int64_t *tokens, int64_t n_out, double *out, int threads)
 {
     double *kpd = NULL, *vpd = NULL, *kld = NULL, *vld = NULL;
@@ -558,6 +574,7 @@ int oracle_sparse_attention(const uint16_t *q, const uint16_t *kp, const uint16_
         jb->DK = DK;
         jb->DV = DV;
         jb->topk = topk;
+        jb->ratio = ratio;
         jb->window = window;
         jb->dtype = dtype;
         jb->scale = scale;
@@ -588,4 +605,31 @@ out:
     free(tids);
     free(started);
     return status;
+}
+
+int oracle_sparse_attention(const uint16_t *q, const uint16_t *kp, const uint16_t *vp,
+                            const uint16_t *kl, const uint16_t *vl, const int32_t *idx,
+                            const int32_t *pos, int64_t T, int64_t N, int64_t L, int HA, int DK,
+                            int DV, int topk, int window, double scale, int dtype,
+                            const int64_t *tokens, int64_t n_out, double *out, int threads)
+{
+    return attention_common(q, kp, vp, kl, vl, idx, pos, T, N, L, HA, DK, DV, topk, 0, window,
+                            scale, dtype, tokens, n_out, out, threads);
+}
+
+/*
+ * The all-visible form: every token attends to its local rows plus every
+ * pooled row it can see (rows 0 .. n_t - 1, n_t = oracle_visible_rows(pos_t,
+ * ratio, N)); no index list.  ratio >= 1.  Same arguments otherwise.
+ */
+int oracle_sparse_attention_all(const uint16_t *q, const uint16_t *kp, const uint16_t *vp,
+                                const uint16_t *kl, const uint16_t *vl, const int32_t *pos,
+                                int64_t T, int64_t N, int64_t L, int HA, int DK, int DV, int ratio,
+                                int window, double scale, int dtype, const int64_t *tokens,
+                                int64_t n_out, double *out, int threads)
+{
+    if (ratio < 1)
+        return ORACLE_ERR_ARG;
+    return attention_common(q, kp, vp, kl, vl, NULL, pos, T, N, L, HA, DK, DV, 0, ratio, window,
+                            scale, dtype, tokens, n_out, out, threads);
 }

@@ -61,6 +61,9 @@ class Oracle:
         lib.oracle_sparse_attention.restype = I
         lib.oracle_sparse_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                                 ctypes.c_double, I, P, I64, P, I]
+        lib.oracle_sparse_attention_all.restype = I
+        lib.oracle_sparse_attention_all.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
+                                                    ctypes.c_double, I, P, I64, P, I]
         self.lib = lib
 
     def half_to_double(self, bits: int) -> float:
@@ -154,6 +157,43 @@ class Oracle:
                                               n_out, ptr(out), int(threads))
         if st != 0:
             raise OracleError(f"oracle_sparse_attention: {STATUS.get(st, st)}")
+        return out
+
+
+    def sparse_attention_all(self, q_bits, kp_bits, vp_bits, kl_bits, vl_bits, pos, *, dtype: str,
+                             ratio: int, window: int, scale: float, tokens=None, threads: int = 1):
+        """The all-visible form: each token attends to its local window plus
+        every pooled row it can see, rows 0 .. n_t-1 (definition in oracle.c).
+        Arrays as in sparse_attention, without idx.  Returns float64 [n_out, HA, DV]."""
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kp_bits = np.ascontiguousarray(kp_bits, dtype=np.uint16)
+        vp_bits = np.ascontiguousarray(vp_bits, dtype=np.uint16)
+        kl_bits = np.ascontiguousarray(kl_bits, dtype=np.uint16)
+        vl_bits = np.ascontiguousarray(vl_bits, dtype=np.uint16)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        T, HA, DK = q_bits.shape
+        N, L = kp_bits.shape[0], kl_bits.shape[0]
+        DV = vp_bits.shape[1] if vp_bits.ndim == 2 else vl_bits.shape[1]
+        if (pos.shape != (T,) or (N and (kp_bits.shape[1] != DK or vp_bits.shape != (N, DV)))
+                or (L and (kl_bits.shape[1] != DK or vl_bits.shape != (L, DV)))):
+            raise OracleError("oracle: inconsistent shapes")
+        if tokens is None:
+            tok, n_out = None, T
+        else:
+            tok = np.ascontiguousarray(tokens, dtype=np.int64)
+            n_out = int(tok.shape[0])
+        out = np.empty((n_out, HA, DV), dtype=np.float64)
+
+        def ptr(a):
+            return None if a is None or a.size == 0 else a.ctypes.data_as(ctypes.c_void_p)
+
+        st = self.lib.oracle_sparse_attention_all(ptr(q_bits), ptr(kp_bits), ptr(vp_bits),
+                                                  ptr(kl_bits), ptr(vl_bits), ptr(pos), T, N, L,
+                                                  HA, DK, DV, int(ratio), int(window), float(scale),
+                                                  DTYPES[dtype], ptr(tok), n_out, ptr(out),
+                                                  int(threads))
+        if st != 0:
+            raise OracleError(f"oracle_sparse_attention_all: {STATUS.get(st, st)}")
         return out
 
 

@@ -573,6 +573,65 @@ def pin_attn_empty_and_errors(orc: Oracle):
         pass
 
 
+def pin_attn_all_library_sdpa(orc: Oracle):
+    """The all-visible form (every pooled row the token can see, no index list)
+    equals torch's scaled_dot_product_attention (float64, CPU) with a mask that
+    admits the local window and the pooled rows j whose r raw tokens
+    r*j .. r*j+r-1 all lie at or before the token's position."""
+    import torch
+    rng = np.random.default_rng(17)
+    for (T, N, L, HA, DK, DV, ratio, W, dtype) in [(10, 9, 40, 2, 4, 3, 4, 5, "f16"),
+                                                     (8, 3, 400, 1, 5, 4, 128, 2, "bf16"),
+                                                     (7, 6, 9, 3, 2, 2, 1, 0, "f16")]:
+        q, kp, vp, kl, vl, _, pos = rand_attn_case(rng, T, N, L, HA, DK, DV, 1, dtype,
+                                                   pos_lo=-2, pos_hi=ratio * N + 5)
+        scale = 0.45
+        got = orc.sparse_attention_all(q, kp, vp, kl, vl, pos, dtype=dtype, ratio=ratio, window=W,
+                                       scale=scale)
+        keys = torch.from_numpy(np.concatenate([decoded(kl, dtype), decoded(kp, dtype)]))
+        vals = torch.from_numpy(np.concatenate([decoded(vl, dtype), decoded(vp, dtype)]))
+        mask = np.zeros((T, L + N), dtype=bool)
+        raw, pooled = np.arange(L), np.arange(N)
+        for t in range(T):
+            mask[t, :L] = (raw <= pos[t]) & (raw > pos[t] - W)
+            mask[t, L:] = ratio * pooled + ratio - 1 <= pos[t]
+        qd = torch.from_numpy(decoded(q, dtype))
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qd.permute(1, 0, 2).unsqueeze(2), keys.expand(HA, T, L + N, DK),
+            vals.expand(HA, T, L + N, DV),
+            attn_mask=torch.from_numpy(mask).unsqueeze(1).expand(HA, T, 1, L + N),
+            scale=scale).squeeze(2).permute(1, 0, 2).numpy()
+        want[~mask.any(axis=1)] = 0.0
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), \
+            f"all-visible attention != library attention (max diff {np.abs(got - want).max()})"
+
+
+def pin_attn_all_constant_keys_mean(orc: Oracle):
+    """All-visible form with every key equal: the plain mean of the admitted
+    values.  Pooled value row j = 1000 + j, so the mean fixes exactly which
+    pooled rows are visible at positions around each multiple of the ratio."""
+    N, L, DK, ratio = 5, 20, 2, 4
+    kp = f16_bits(np.ones((N, DK)))
+    kl = f16_bits(np.ones((L, DK)))
+    vl = f16_bits(np.arange(L, dtype=np.float64)[:, None])
+    vp = f16_bits(1000.0 + np.arange(N, dtype=np.float64)[:, None])
+    pos = np.array([-1, 0, 2, 3, 4, 7, 8, 18, 19, 23, 40], dtype=np.int32)
+    T = len(pos)
+    q = f16_bits(np.full((T, 1, DK), 0.25))
+    for W in (0, 2):
+        got = orc.sparse_attention_all(q, kp, vp, kl, vl, pos, dtype="f16", ratio=ratio, window=W,
+                                       scale=0.9)
+        for t in range(T):
+            p = int(pos[t])
+            rows_v = []
+            if p >= 0 and W > 0:
+                rows_v += [float(r) for r in range(max(0, p - W + 1), min(p, L - 1) + 1)]
+            rows_v += [1000.0 + j for j in range(N) if ratio * j + ratio - 1 <= p]
+            want = sum(Fraction(v) for v in rows_v) / len(rows_v) if rows_v else Fraction(0)
+            assert abs(got[t, 0, 0] - float(want)) <= 1e-12 * max(1.0, abs(float(want))), \
+                (W, p, got[t, 0, 0], float(want))
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -62,6 +62,9 @@ MUTANTS = [
     ("attn_unnormalised", "const double a = s[r] / z;", "const double a = s[r];"),
     ("attn_local_values_reversed", "vrow[nr] = jb->vl + r * DV;", "vrow[nr] = jb->vl + (hi - (r - lo)) * DV;"),
     ("attn_every_head_is_head0", "jb->q[(t * HA + h) * DK + d]", "jb->q[(t * HA) * DK + d]"),
+    ("attn_all_one_row_more", "for (r = 0; r < nv; ++r) {", "for (r = 0; r <= nv && r < jb->N; ++r) {"),
+    ("attn_all_visible_off_by_one", "oracle_visible_rows(p, jb->ratio, jb->N)",
+     "oracle_visible_rows(p - 1, jb->ratio, jb->N)"),
     ("attn_pooled_keys_reversed", "krow[nr] = jb->kp + (int64_t)j * DK;",
      "krow[nr] = jb->kp + (int64_t)(jb->N - 1 - j) * DK;"),
 ]
