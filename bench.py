@@ -26,7 +26,7 @@ that pass's step time is reported apart.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W = 200: the
                        GPU needs some tens of milliseconds of work to reach its full clock)
-       python bench.py --only prefill32k|prefill64k|decode1m|attn32k   (one workload, for profilers)
+       python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|attn32k   (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --ceilings                               (vendor GEMM and plain-copy
                        rates with the workloads' value distributions)
@@ -56,7 +56,7 @@ METRIC = "indexer scored pairs/sec + query tokens/sec at 32k/64k context; decode
 PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0                               # MI355X HBM3E
 HEADLINE = "prefill32k"
-SECONDARY = ("prefill64k", "decode1m")
+SECONDARY = ("prefill64k", "decode1m", "prefill2k")
 DECODE_K_BUFFERS = 8
 KERNEL_SOURCES = {  # kernel class -> sources whose change invalidates stored counters
     "score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
@@ -149,6 +149,7 @@ def time_workload(name: str, steps: int, warmup: int):
 
 
 ATTN_WORKLOAD = "attn32k"
+ATTN_SECONDARY = ("attn32k_r128",)
 
 
 def time_attention(name: str, steps: int, warmup: int):
@@ -158,7 +159,7 @@ def time_attention(name: str, steps: int, warmup: int):
     import numpy as np
     import torch
     from sparse_attention_kv_ds_amd import synth
-    from sparse_attention_kv_ds_amd.indexer import sparse_attention
+    from sparse_attention_kv_ds_amd.indexer import sparse_attention, sparse_attention_all
 
     dev = torch.device("cuda", 0)
     d = synth.make_attention(name)
@@ -170,8 +171,12 @@ def time_attention(name: str, steps: int, warmup: int):
     out = torch.empty((wl.T, wl.HA, wl.DV), dtype=torch.float32, device=dev)
 
     def call():
-        sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], idx, pos, window=wl.window,
-                         scale=wl.scale, dtype=wl.dtype, out=out)
+        if wl.ratio > 0:  # every visible pooled row, no index list
+            sparse_attention_all(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], pos, ratio=wl.ratio,
+                                 window=wl.window, scale=wl.scale, dtype=wl.dtype, out=out)
+        else:
+            sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], idx, pos,
+                             window=wl.window, scale=wl.scale, dtype=wl.dtype, out=out)
 
     for _ in range(warmup):
         call()
@@ -190,7 +195,10 @@ def time_attention(name: str, steps: int, warmup: int):
     lo = np.maximum(0, p - wl.window + 1)
     hi = np.minimum(p, wl.L - 1)
     n_loc = np.where((p >= 0) & (wl.window > 0), np.maximum(0, hi - lo + 1), 0)
-    n_pool = ((d["idx"] >= 0) & (d["idx"] < wl.N)).sum(axis=1)
+    if wl.ratio > 0:
+        n_pool = np.clip((p + 1) // wl.ratio, 0, wl.N)
+    else:
+        n_pool = ((d["idx"] >= 0) & (d["idx"] < wl.N)).sum(axis=1)
     rows = int((n_loc + n_pool).sum())
     flops = 2.0 * wl.HA * (wl.DK + wl.DV) * rows
     ach = flops / (ms * 1e-3) / 1e12
@@ -204,7 +212,7 @@ def time_attention(name: str, steps: int, warmup: int):
             "rows_attended_per_token": rows / wl.T,
             "roofline": {"bound": "mfma", "kernel": "sparse_attention", "achieved": ach,
                          "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
-                         "traffic": stored_traffic("attention", name),
+                         "traffic": stored_traffic("attention", name) if name in DOMINANT else None,
                          "algorithmic_flops_per_launch": flops,
                          "input_output_bytes_per_launch": byt}}
 
@@ -222,6 +230,15 @@ def stored_traffic(cls: str, workload: str):
 
 def roofline(res):
     wl = res["wl"]
+    if "score" not in res["kernels"] and "decode_score" not in res["kernels"]:
+        # every row fits (N <= topk): only the sequential-rows kernel runs
+        cls = "select" if wl.T > 1 else "decode_select"
+        t = res["kernels"][cls]["avg_ms"] * 1e-3
+        algo = wl.T * wl.topk * 4 + wl.T * 4  # out written, pos read
+        ach = algo / t / 1e9
+        return {"bound": "hbm", "kernel": "sequential_rows", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": algo}
     if wl.T == 1:
         cls = "decode_score"
         t = res["kernels"][cls]["avg_ms"] * 1e-3
@@ -490,7 +507,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD])
+    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD, *ATTN_SECONDARY])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
@@ -530,7 +547,7 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
-    if args.only == ATTN_WORKLOAD:
+    if args.only in (ATTN_WORKLOAD, *ATTN_SECONDARY):
         res = time_attention(args.only, args.steps, args.warmup)
         print(json.dumps({k: v for k, v in res.items()}))
         return 0
@@ -581,7 +598,8 @@ def main():
                           "query_tokens_per_s": r["query_tokens_per_s"]})
         line["secondary"].append(entry)
     # the consumer of the indices (sparse attention over the selected rows)
-    line["secondary"].append(time_attention(ATTN_WORKLOAD, args.steps, min(args.warmup, 50)))
+    for name in (ATTN_WORKLOAD, *ATTN_SECONDARY):
+        line["secondary"].append(time_attention(name, args.steps, min(args.warmup, 50)))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(HEADLINE)
     print(json.dumps(line))

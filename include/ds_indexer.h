@@ -97,6 +97,11 @@ int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, i
  *
  * T == 1 uses the single-token decode kernels (K streamed once across the
  * whole GPU, multi-work-group selection); T > 1 uses the prefill kernels.
+ * When N <= topk every visible row of every token is selected: the call then
+ * writes each token's rows 0 .. n_t-1 (then -1) and launches no scorer ("How
+ * I turned one oversized DeepSeek optimization into three merged oMLX PRs",
+ * section "3. Do not rank candidates when every candidate wins", decided here
+ * from N alone, on the host, with no synchronisation).
  * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY or DS_ERR_HIP.
  */
 int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const float *w,
@@ -206,6 +211,26 @@ int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
                         const int32_t *pos, int64_t T, int64_t N, int64_t L, int n_heads,
                         int head_dim, int dtype, int topk, int window, float scale, float *out,
                         void *stream);
+
+/*
+ * Sparse attention in its all-visible form: every token attends to its local
+ * rows (as above) plus every pooled row it can see -- rows 0 .. n_t - 1 with
+ * n_t = clamp(floor((pos[t] + 1) / ratio), 0, N), the same causal rule as the
+ * indexer -- with no index list.  These are the sequential pooled indices that
+ * layers with a large compression ratio (128) attend to without an indexer
+ * ("How I turned one oversized DeepSeek optimization into three merged oMLX
+ * PRs", section "1. Route ratio-128 prefill through native attention"), and
+ * what the indexer's selection reduces to when every row fits (section "3. Do
+ * not rank candidates when every candidate wins").
+ *
+ * Arguments, layout, ownership, arithmetic and errors as ds_sparse_attention,
+ * without idx and topk; ratio >= 1 (else DS_ERR_INVALID_ARG) and N <= 2048
+ * (else DS_ERR_UNSUPPORTED).
+ */
+int ds_sparse_attention_all(const void *q, const void *k_pool, const void *v_pool,
+                            const void *k_local, const void *v_local, const int32_t *pos,
+                            int64_t T, int64_t N, int64_t L, int n_heads, int head_dim, int dtype,
+                            int ratio, int window, float scale, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -222,7 +222,13 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
     hipStream_t s = (hipStream_t)stream;
     const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
     hipError_t e;
-    if (T == 1 && ix->decode_ok) {
+    if (N <= topk) {
+        // every row of K fits in topk, so every token's visible rows do: the
+        // sequential rows, with no scorer and no selection launched
+        e = timed(ix, T == 1 ? DS_KERNEL_DECODE_SELECT : DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
+            return dsi::launch_sequential_rows(pos, (int)T, (int)N, ratio, topk, out, s, tm);
+        });
+    } else if (T == 1 && ix->decode_ok) {
         dsi::DecodeLists dl;
         dl.kp = decode_kp(N, topk);
         dl.cand = ix->cand;
@@ -326,11 +332,14 @@ void ds_indexer_destroy(ds_indexer *ix)
     delete ix;
 }
 
-int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
-                        const void *k_local, const void *v_local, const int32_t *idx,
-                        const int32_t *pos, int64_t T, int64_t N, int64_t L, int n_heads,
-                        int head_dim, int dtype, int topk, int window, float scale, float *out,
-                        void *stream)
+namespace {
+
+// shared by both attention entry points: ratio == 0 takes the index list
+// idx[T][topk]; ratio > 0 attends to every visible pooled row (topk == N)
+int attention_call(const void *q, const void *k_pool, const void *v_pool, const void *k_local,
+                   const void *v_local, const int32_t *idx, const int32_t *pos, int64_t T,
+                   int64_t N, int64_t L, int n_heads, int head_dim, int dtype, int64_t topk,
+                   int ratio, int window, float scale, float *out, void *stream)
 {
     // the softmax temperature is a positive finite number (the kernel takes
     // each head's maximum on the unscaled scores)
@@ -344,8 +353,8 @@ int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
         return DS_ERR_UNSUPPORTED;
     if (T == 0)
         return DS_OK;
-    if (!q || !pos || !out || (topk > 0 && !idx) || (N > 0 && (!k_pool || !v_pool)) ||
-        (L > 0 && (!k_local || !v_local)))
+    if (!q || !pos || !out || (ratio == 0 && topk > 0 && !idx) ||
+        (N > 0 && (!k_pool || !v_pool)) || (L > 0 && (!k_local || !v_local)))
         return DS_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
         !aligned(k_local, 16) || !aligned(v_local, 16) || !aligned(out, 16) ||
@@ -357,19 +366,43 @@ int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
     a.vp = v_pool;
     a.kl = k_local;
     a.vl = v_local;
-    a.idx = idx;
+    a.idx = ratio > 0 ? nullptr : idx;
     a.pos = pos;
     a.T = (int)T;
     a.N = (int)N;
     a.L = (int)L;
     a.HA = n_heads;
     a.D = head_dim;
-    a.topk = topk;
+    a.topk = (int)topk;
+    a.ratio = ratio;
     a.window = window;
     a.dtype = dtype;
     a.scale = scale;
     a.out = out;
     return dsi::launch_sparse_attention(a, (hipStream_t)stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+} // namespace
+
+int ds_sparse_attention(const void *q, const void *k_pool, const void *v_pool,
+                        const void *k_local, const void *v_local, const int32_t *idx,
+                        const int32_t *pos, int64_t T, int64_t N, int64_t L, int n_heads,
+                        int head_dim, int dtype, int topk, int window, float scale, float *out,
+                        void *stream)
+{
+    return attention_call(q, k_pool, v_pool, k_local, v_local, idx, pos, T, N, L, n_heads,
+                          head_dim, dtype, topk, 0, window, scale, out, stream);
+}
+
+int ds_sparse_attention_all(const void *q, const void *k_pool, const void *v_pool,
+                            const void *k_local, const void *v_local, const int32_t *pos,
+                            int64_t T, int64_t N, int64_t L, int n_heads, int head_dim, int dtype,
+                            int ratio, int window, float scale, float *out, void *stream)
+{
+    if (ratio < 1)
+        return DS_ERR_INVALID_ARG;
+    return attention_call(q, k_pool, v_pool, k_local, v_local, nullptr, pos, T, N, L, n_heads,
+                          head_dim, dtype, N, ratio, window, scale, out, stream);
 }
 
 const char *ds_indexer_status_str(int status)

@@ -11,6 +11,11 @@
 // the lightning indexer's selection, "How I made DeepSeek 12x faster on a Mac
 // Studio", section "1: the kernels").
 //
+// The all-visible form (ratio > 0, no index list) attends to every pooled row
+// the token can see, rows 0 .. n-1 with n = floor((p + 1) / ratio) clamped
+// to [0, N]: the sequential pooled indices of ratio-128 layers (same section
+// of the oMLX page).
+//
 // One work-group per token, one wave per 32 heads.  The token's rows are taken
 // in blocks of 32: the local rows first (their last block padded), then the
 // index list in order, so that every block reads one tensor pair.  Each
@@ -91,8 +96,8 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kp,
     const uint16_t *__restrict__ vp, const uint16_t *__restrict__ kl,
     const uint16_t *__restrict__ vl, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ pos, int N, int L, int topk, int window, float scale_log2,
-    float *__restrict__ out)
+    const int32_t *__restrict__ pos, int N, int L, int topk, int ratio, int window,
+    float scale_log2, float *__restrict__ out)
 {
     constexpr int HA = WAVES * 32;
     constexpr int KS = D / 16;            // MFMA steps along D for S
@@ -125,9 +130,15 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     const int nb_pool = (topk + 31) >> 5;
     const int nb = nb_loc + nb_pool;
 
-    // entries outside [0, N) and the padding become -1 (empty slots)
+    // entries outside [0, N) and the padding become -1 (empty slots); with
+    // ratio > 0 the list is every pooled row the token can see, 0 .. n-1
+    const int n_all = ratio > 0 ? visible_rows(p, ratio, N) : 0;
     for (int e = threadIdx.x; e < 32 * nb_pool; e += WAVES * 64) {
-        const int j = e < topk ? idx[(long long)t * topk + e] : -1;
+        int j;
+        if (ratio > 0)
+            j = e < n_all ? e : -1;
+        else
+            j = e < topk ? idx[(long long)t * topk + e] : -1;
         ids[e] = (uint32_t)j < (uint32_t)N ? j : -1;
     }
 
@@ -348,10 +359,10 @@ hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
     if (a.dtype == kF16)
         return launch_kernel(sparse_attention_kernel<WAVES, D, kF16>, dim3(a.T), dim3(WAVES * 64),
                              0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos,
-                             a.N, a.L, a.topk, a.window, scale_log2, a.out);
+                             a.N, a.L, a.topk, a.ratio, a.window, scale_log2, a.out);
     return launch_kernel(sparse_attention_kernel<WAVES, D, kBF16>, dim3(a.T), dim3(WAVES * 64),
                          0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
-                         a.L, a.topk, a.window, scale_log2, a.out);
+                         a.L, a.topk, a.ratio, a.window, scale_log2, a.out);
 }
 
 } // namespace

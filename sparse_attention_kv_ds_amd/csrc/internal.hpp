@@ -99,6 +99,11 @@ hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int r
                                 const DecodeLists &dl, int32_t *out, hipStream_t st,
                                 Timing *tm = nullptr);
 
+// Every token's rows 0 .. n_t-1, then -1, in out[T][topk] (for N <= topk,
+// where every visible row is selected and nothing needs scoring).
+hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, int topk,
+                                  int32_t *out, hipStream_t st, Timing *tm = nullptr);
+
 // p[0..n) = v
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st);
 
@@ -109,9 +114,10 @@ struct AttnProblem {
     const void *q;        // [T][HA][D] raw fp16/bf16 bits
     const void *kp, *vp;  // [N][D] pooled rows
     const void *kl, *vl;  // [L][D] raw rows by absolute position
-    const int32_t *idx;   // [T][topk]
+    const int32_t *idx;   // [T][topk]; unused when ratio > 0
     const int32_t *pos;   // [T]
     int T, N, L, HA, D, topk, window, dtype;
+    int ratio;            // > 0: every visible pooled row (list of N entries), idx unused
     float scale;
     float *out;           // [T][HA][D] fp32
 };

@@ -297,7 +297,39 @@ hipError_t merge_one(const float *S, const int32_t *pos, int N, int ratio, int t
                          st, tm, true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
 }
 
+// ---------------------------------------------------------------------------
+// Whole-call skip: when every row of K fits in topk, every token's visible rows
+// fit, and the answer is each token's rows 0 .. n_t-1, then -1, with nothing
+// scored ("How I turned one oversized DeepSeek optimization into three merged
+// oMLX PRs", section "3. Do not rank candidates when every candidate wins").
+// One thread per output entry.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sequential_rows_kernel(const int32_t *__restrict__ pos, int T,
+                                                              int N, int ratio, int topk,
+                                                              int32_t *__restrict__ out)
+{
+    const long long total = (long long)T * topk;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256) {
+        const int t = (int)(i / topk), e = (int)(i % topk);
+        const int n = visible_rows(pos[t], ratio, N);
+        out[i] = e < n ? e : -1;
+    }
+}
+
 } // namespace
+
+hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, int topk,
+                                  int32_t *out, hipStream_t st, Timing *tm)
+{
+    if (T <= 0 || topk <= 0)
+        return hipSuccess;
+    long long blocks = ((long long)T * topk + 255) / 256;
+    if (blocks > 8192)
+        blocks = 8192;
+    return launch_kernel(sequential_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, tm, true,
+                         true, pos, T, N, ratio, topk, out);
+}
 
 hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos, int T, int N,
                               int ratio, int topk, int32_t *out, hipStream_t st, Timing *tm)

@@ -33,7 +33,7 @@ KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select")
 
 EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
-           "ds_indexer_timing_read", "ds_sparse_attention")
+           "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all")
 
 
 class IndexerError(RuntimeError):
@@ -70,6 +70,9 @@ def _load() -> ctypes.CDLL:
     lib.ds_sparse_attention.restype = I
     lib.ds_sparse_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                         ctypes.c_float, P, P]
+    lib.ds_sparse_attention_all.restype = I
+    lib.ds_sparse_attention_all.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
+                                            ctypes.c_float, P, P]
     return lib
 
 
@@ -227,6 +230,57 @@ class Indexer:
         if st != DS_OK:
             raise IndexerError(st, "ds_indexer_scores")
         return out
+
+
+def ds_sparse_attention_all(q, k_pool, v_pool, k_local, v_local, pos, T, N, L, n_heads, head_dim,
+                            dtype, ratio, window, scale, out, stream) -> int:
+    return _lib.ds_sparse_attention_all(q, k_pool, v_pool, k_local, v_local, pos, T, N, L, n_heads,
+                                        head_dim, dtype, ratio, window, scale, out, stream)
+
+
+def _attention_args(q, k_pool, v_pool, k_local, v_local, idx, pos, dtype, out):
+    import torch
+    dev = q.device
+    T, HA, D = q.shape
+    if dtype is None:
+        dtype = q.dtype
+    code = _dtype_code(dtype)
+    tensors = [("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("k_local", k_local),
+               ("v_local", v_local), ("pos", pos)] + ([("idx", idx)] if idx is not None else [])
+    for name, t_ in tensors:
+        if t_.device != dev or not t_.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    for name, t_ in (("k_pool", k_pool), ("v_pool", v_pool), ("k_local", k_local),
+                     ("v_local", v_local)):
+        if t_.element_size() != 2 or (t_.numel() and tuple(t_.shape[1:]) != (D,)):
+            raise ValueError(f"{name} must be [rows, {D}] with 16-bit elements")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (T,) or (
+            idx is not None and idx.dtype != torch.int32):
+        raise ValueError("idx [T, topk] and pos [T] must be int32")
+    if out is None:
+        out = torch.empty((T, HA, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    return T, HA, D, code, out, stream
+
+
+def _ptr(t_):
+    return t_.data_ptr() if t_.numel() else None
+
+
+def sparse_attention_all(q, k_pool, v_pool, k_local, v_local, pos, *, ratio: int, window: int,
+                         scale: float, dtype=None, out=None):
+    """Attention of each token's heads over its local raw rows plus every pooled
+    row it can see (ds_sparse_attention_all); arguments as sparse_attention,
+    with the compression ratio instead of an index list."""
+    T, HA, D, code, out, stream = _attention_args(q, k_pool, v_pool, k_local, v_local, None, pos,
+                                                  dtype, out)
+    st = ds_sparse_attention_all(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_local),
+                                 _ptr(v_local), pos.data_ptr(), T, k_pool.shape[0],
+                                 k_local.shape[0], HA, D, code, int(ratio), window, float(scale),
+                                 out.data_ptr(), stream)
+    if st != DS_OK:
+        raise IndexerError(st, "ds_sparse_attention_all")
+    return out
 
 
 def sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, *, window: int,

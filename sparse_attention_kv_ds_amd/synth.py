@@ -11,7 +11,8 @@ chunk of a cold 8k / 32k / 64k-context prefill at compression ratio 4 with
 Mac Studio", section "1: the kernels", cold-prefill table; the 2048-token
 prefill step of "How I turned one oversized DeepSeek optimization into three
 merged oMLX PRs", section "Independent upstream reproduction"), a single
-decode token at the 1M-token window, and a tiny case for exhaustive checks.
+decode token at the 1M-token window, a tiny case for exhaustive checks, and
+the first 2048-token chunk of a prompt (every row fits in the top-512).
 
 Draw order for one workload, from numpy.random.default_rng(seed): q, then k,
 then w (for power-of-two weights: the signs, then the exponents).
@@ -52,6 +53,9 @@ class Workload:
 WORKLOADS = {
     "tiny": Workload("tiny", T=256, p0=0, N=64, H=4, D=32, topk=48, ratio=4,
                      dtype="f16", dist="int"),
+    # the first 2048-token chunk of any prompt: 512 rows, all of them fit in top-512
+    "prefill2k": Workload("prefill2k", T=2048, p0=0, N=512, H=64, D=128, topk=512, ratio=4,
+                          dtype="f16", dist="int"),
     "prefill8k": Workload("prefill8k", T=2048, p0=6144, N=2048, H=64, D=128, topk=512,
                           ratio=4, dtype="f16", dist="int"),
     "prefill32k": Workload("prefill32k", T=2048, p0=30720, N=8192, H=64, D=128, topk=512,
@@ -136,6 +140,7 @@ class AttnWorkload:
     dtype: str
     short_every: int = 0  # every n-th token gets a shorter index list (0: none)
     seed: int = 0
+    ratio: int = 0  # > 0: no index list; every pooled row a token can see (all-visible form)
 
     @property
     def positions(self) -> np.ndarray:
@@ -152,6 +157,10 @@ ATTN_WORKLOADS = {
     # the consumer of the 32k prefill chunk's indices
     "attn32k": AttnWorkload("attn32k", T=2048, p0=30720, N=8192, L=32768, HA=64, DK=128, DV=128,
                             topk=512, window=128, dtype="bf16"),
+    # the same chunk in a ratio-128 layer: every visible pooled row (240..256 of
+    # 256), no indexer
+    "attn32k_r128": AttnWorkload("attn32k_r128", T=2048, p0=30720, N=256, L=32768, HA=64, DK=128,
+                                 DV=128, topk=0, window=128, dtype="bf16", ratio=128),
 }
 
 
@@ -191,5 +200,6 @@ def make_attention(wl: AttnWorkload | str):
     kl = to_bits(rng.standard_normal(size=(wl.L, wl.DK)) * sk, wl.dtype)
     vl = to_bits(rng.standard_normal(size=(wl.L, wl.DV)), wl.dtype)
     pos = wl.positions
-    idx = draw_index_lists(rng, wl.T, wl.N, wl.topk, wl.short_every)
+    idx = draw_index_lists(rng, wl.T, wl.N, wl.topk, wl.short_every) if wl.ratio == 0 else \
+        np.full((wl.T, 0), -1, dtype=np.int32)
     return {"q": q, "kp": kp, "vp": vp, "kl": kl, "vl": vl, "idx": idx, "pos": pos, "wl": wl}

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ds_indexer_create", "ds_indexer_score_topk",
                                            "ds_indexer_destroy", "ds_indexer_scores",
                                            "ds_indexer_status_str", "ds_indexer_timing",
-                                           "ds_indexer_timing_read", "ds_sparse_attention"])
+                                           "ds_indexer_timing_read", "ds_sparse_attention",
+                                           "ds_sparse_attention_all"])
 
 
 def test_every_declared_symbol_is_exported(ix):
@@ -124,3 +125,25 @@ def test_sparse_attention_rejects_bad_arguments_on_the_host(ix):
     assert call(idx=None) == ix.DS_ERR_INVALID_ARG
     assert call(out=fake + 4) == ix.DS_ERR_INVALID_ARG  # misaligned
     assert call(T=0, q=None, out=None) == ix.DS_OK      # nothing to do
+
+
+def test_sparse_attention_all_rejects_bad_arguments_on_the_host(ix):
+    """The all-visible form: same checks, plus ratio >= 1 and at most 2048 pooled
+    rows (the length of its implicit list); no index list is needed."""
+    fake = 0x1000  # never dereferenced: each call below returns before any launch
+    def call(**kw):
+        a = dict(q=fake, k_pool=fake, v_pool=fake, k_local=fake, v_local=fake, pos=fake, T=4,
+                 N=8, L=8, n_heads=64, head_dim=128, dtype=ix.DS_BF16, ratio=128, window=2,
+                 scale=0.1, out=fake, stream=None)
+        a.update(kw)
+        return ix.ds_sparse_attention_all(*a.values())
+    assert call(ratio=0) == ix.DS_ERR_INVALID_ARG
+    assert call(ratio=-4) == ix.DS_ERR_INVALID_ARG
+    assert call(N=2049) == ix.DS_ERR_UNSUPPORTED
+    assert call(T=-1) == ix.DS_ERR_INVALID_ARG
+    assert call(scale=0.0) == ix.DS_ERR_INVALID_ARG
+    assert call(n_heads=16) == ix.DS_ERR_UNSUPPORTED
+    assert call(pos=None) == ix.DS_ERR_INVALID_ARG
+    assert call(k_pool=None) == ix.DS_ERR_INVALID_ARG
+    assert call(v_local=fake + 8) == ix.DS_ERR_INVALID_ARG  # misaligned
+    assert call(T=0, q=None, out=None) == ix.DS_OK

@@ -155,6 +155,61 @@ def test_attn32k_sampled_tokens(ix, orc):
     check(got[toks], want, d, wl.dtype, "attn32k")
 
 
+def run_gpu_all(ix, d, dtype, ratio, window, scale):
+    import torch
+    t = to_dev(d)
+    out = ix.sparse_attention_all(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], t["pos"],
+                                  ratio=ratio, window=window, scale=scale, dtype=dtype)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+ALL_SHAPES = [
+    # (HA, D, dtype, T, N, L, ratio, window, pos range): the all-visible form
+    (64, 128, "bf16", 30, 256, 32768, 128, 128, (30700, 32767)),
+    (32, 64, "f16", 40, 70, 300, 4, 8, (-3, 290)),
+    (128, 128, "f16", 9, 2048, 2100, 1, 16, (1000, 2099)),   # every raw row pooled, 2048 rows
+    (64, 64, "bf16", 21, 33, 4300, 128, 0, (0, 4299)),       # pooled rows only
+    (64, 128, "bf16", 12, 0, 60, 128, 20, (-2, 70)),         # empty pool
+    (32, 128, "bf16", 17, 100, 5000, 16, 64, (1500, 1700)),  # positions past the pool's end
+]
+
+
+@pytest.mark.parametrize("HA,D,dtype,T,N,L,ratio,window,prange", ALL_SHAPES)
+def test_all_visible_shapes(ix, orc, HA, D, dtype, T, N, L, ratio, window, prange):
+    d = random_case(HA * 5 + D + T + ratio, T, N, L, HA, D, 0, dtype, *prange)
+    scale = 1.0 / np.sqrt(D)
+    got = run_gpu_all(ix, d, dtype, ratio, window, scale)
+    want = orc.sparse_attention_all(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], d["pos"],
+                                    dtype=dtype, ratio=ratio, window=window, scale=scale,
+                                    threads=8)
+    check(got, want, d, dtype, f"all-visible HA={HA} D={D} {dtype} ratio={ratio}")
+
+
+def test_all_visible_equals_the_sequential_lists(ix):
+    """The all-visible form and the list form with each token's lists 0 .. n_t-1
+    process the same rows in the same order: bit-identical outputs."""
+    T, N, L, ratio = 24, 256, 33000, 128
+    d = random_case(77, T, N, L, 64, 128, 0, "bf16", 30000, 32999)
+    n = np.clip((d["pos"].astype(np.int64) + 1) // ratio, 0, N)
+    d["idx"] = np.where(np.arange(N)[None, :] < n[:, None], np.arange(N)[None, :], -1).astype(np.int32)
+    a = run_gpu_all(ix, d, "bf16", ratio, 128, 0.088)
+    b = run_gpu(ix, d, "bf16", 128, 0.088)
+    assert np.array_equal(a, b)
+
+
+def test_attn32k_r128_sampled_tokens(ix, orc):
+    """The ratio-128 form of the 32k chunk in one launch; 48 evenly spaced tokens checked."""
+    d = synth.make_attention("attn32k_r128")
+    wl = d["wl"]
+    got = run_gpu_all(ix, d, wl.dtype, wl.ratio, wl.window, wl.scale)
+    toks = np.linspace(0, wl.T - 1, 48).astype(np.int64)
+    want = orc.sparse_attention_all(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], d["pos"],
+                                    dtype=wl.dtype, ratio=wl.ratio, window=wl.window,
+                                    scale=wl.scale, tokens=toks, threads=16)
+    check(got[toks], want, d, wl.dtype, "attn32k_r128")
+
+
 def test_deterministic(ix):
     d = random_case(9, 24, 1000, 1500, 64, 128, 256, "bf16", 1000, 1499)
     a = run_gpu(ix, d, "bf16", 64, 0.088)

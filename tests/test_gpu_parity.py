@@ -284,7 +284,7 @@ def sample_tokens(T, rng, n=40):
     return np.array(sorted(idx), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["prefill8k", "prefill32k"])
+@pytest.mark.parametrize("name", ["prefill2k", "prefill8k", "prefill32k"])
 def test_integer_workloads_full_size(lib, orc, name):
     say(f"full-size {name}")
     d = synth.make(name)
