@@ -26,7 +26,8 @@ that pass's step time is reported apart.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W = 200: the
                        GPU needs some tens of milliseconds of work to reach its full clock)
-       python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|attn32k   (one workload, for profilers)
+       python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|decode1m_b8|attn32k|attn32k_r128
+                                                                 (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --ceilings                               (vendor GEMM and plain-copy
                        rates with the workloads' value distributions)
@@ -150,6 +151,65 @@ def time_workload(name: str, steps: int, warmup: int):
 
 ATTN_WORKLOAD = "attn32k"
 ATTN_SECONDARY = ("attn32k_r128",)
+
+
+DECODE_BATCH = "decode1m_b8"
+
+
+def time_decode_batch(name: str, steps: int, warmup: int):
+    """Time `steps` batched decode calls (B sequences of 262144 rows: 512 MiB of K,
+    above the last-level cache, so every call streams K from HBM)."""
+    import numpy as np
+    import torch
+    from sparse_attention_kv_ds_amd import synth
+    from sparse_attention_kv_ds_amd.indexer import Indexer
+
+    dev = torch.device("cuda", 0)
+    d = synth.make_decode_batch(name)
+    wl, B = d["wl"], d["B"]
+    q = torch.from_numpy(np.ascontiguousarray(d["q"]).view(np.int16)).to(dev)
+    k = torch.from_numpy(np.ascontiguousarray(d["k"]).view(np.int16)).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    pos = torch.from_numpy(d["pos"]).to(dev)
+    out = torch.empty((B, wl.topk), dtype=torch.int32, device=dev)
+    ix = Indexer(wl.H, wl.D, wl.dtype, wl.topk, B, wl.N, device=0)
+
+    def timed_steps():
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        t0.record()
+        for _ in range(steps):
+            ix.score_topk_batch(q, k, w, pos, wl.ratio, wl.topk, out=out)
+        t1.record()
+        torch.cuda.synchronize(dev)
+        return t0.elapsed_time(t1) / steps
+
+    try:
+        for _ in range(warmup):
+            ix.score_topk_batch(q, k, w, pos, wl.ratio, wl.topk, out=out)
+        ms = timed_steps()
+        ix.timing(True)
+        ix.timing_read()
+        ms_marked = timed_steps()
+        per = ix.timing_read()
+        ix.timing(False)
+    finally:
+        ix.close()
+    kernels = {c: v[0] / v[1] for c, v in per.items() if v[1]}
+    algo = B * (wl.N * wl.D * 2 + wl.H * wl.D * 2 + wl.H * 4 + wl.topk * 4)
+    t = kernels["decode_score"] * 1e-3
+    ach = algo / t / 1e9
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/call for {B} sequences ({ms_marked * 1e3:.1f} with "
+        f"kernel markers), " + ", ".join(f"{c} {v * 1e3:.1f} us" for c, v in kernels.items())
+        + f"; scorer {ach:.0f} GB/s ({ach / PEAK_HBM_GBS * 100:.1f} % of HBM)")
+    return {"workload": name, "dtype": wl.dtype, "sequences": B, "ms_per_step": ms,
+            "ms_per_step_with_markers": ms_marked, "kernels_ms": kernels,
+            "value": algo / (ms * 1e-3) / 1e9, "unit": "GB/s (whole batched decode call, K from HBM)",
+            "sequences_per_s": B / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": "decode_scorer (batched)", "achieved": ach,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                         "traffic": None, "algorithmic_bytes_per_launch": algo}}
 
 
 def time_attention(name: str, steps: int, warmup: int):
@@ -507,7 +567,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD, *ATTN_SECONDARY])
+    ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD, *ATTN_SECONDARY,
+                                       DECODE_BATCH])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
@@ -547,6 +608,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    if args.only == DECODE_BATCH:
+        res = time_decode_batch(args.only, args.steps, args.warmup)
+        print(json.dumps(res))
+        return 0
     if args.only in (ATTN_WORKLOAD, *ATTN_SECONDARY):
         res = time_attention(args.only, args.steps, args.warmup)
         print(json.dumps({k: v for k, v in res.items()}))
@@ -598,6 +663,8 @@ def main():
                           "query_tokens_per_s": r["query_tokens_per_s"]})
         line["secondary"].append(entry)
     # the consumer of the indices (sparse attention over the selected rows)
+    # several sequences of one query token each in one call (batched decode)
+    line["secondary"].append(time_decode_batch(DECODE_BATCH, args.steps, min(args.warmup, 50)))
     for name in (ATTN_WORKLOAD, *ATTN_SECONDARY):
         line["secondary"].append(time_attention(name, args.steps, min(args.warmup, 50)))
     if not args.no_cpu_baseline:

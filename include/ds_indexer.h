@@ -109,6 +109,30 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
                           int32_t *out, void *stream);
 
 /*
+ * Batched decode: B independent sequences of one query token each, in one
+ * call -- the single-token path (T == 1) for every sequence at once, so that
+ * several sequences share one K stream across the GPU.  Each sequence's result
+ * is exactly what ds_indexer_score_topk gives it alone (same rule as "How I
+ * made DeepSeek 12x faster on a Mac Studio", section "1: the kernels").
+ *
+ *   q      [B][H][D]  dtype     one query token per sequence
+ *   k      [B][N][D]  dtype     sequence b's compressed rows at k + b*N*D
+ *   w      [B][H]     float32
+ *   pos    [B]        int32     each sequence's token position
+ *   out    [B][topk]  int32     result per sequence (ascending rows, then -1)
+ *   B      0 <= B <= min(max_tokens, 64); N <= max_rows; other arguments,
+ *          alignment, ownership and asynchrony as ds_indexer_score_topk
+ * The handle must allow the single-token path (max_rows <= 1048576), else
+ * DS_ERR_UNSUPPORTED.  Uses the handle's workspace, so calls on one handle
+ * must not overlap (as for every call).  Returns DS_OK, DS_ERR_INVALID_ARG,
+ * DS_ERR_CAPACITY (B, N or topk above the handle's limits),
+ * DS_ERR_UNSUPPORTED or DS_ERR_HIP.
+ */
+int ds_indexer_score_topk_batch(ds_indexer *ix, const void *q, const void *k, const float *w,
+                                const int32_t *pos, int64_t B, int64_t N, int ratio, int topk,
+                                int32_t *out, void *stream);
+
+/*
  * Release the handle and its device scratch.  NULL is accepted and ignored.
  * Waits for the handle's device to finish outstanding work first.
  */

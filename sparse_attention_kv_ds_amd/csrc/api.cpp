@@ -17,10 +17,11 @@ struct ds_indexer {
     int64_t max_tokens, max_rows;
     long long ldS;     // row stride of the score scratch (floats)
     float *S;          // [max_tokens][ldS] scores
-    uint64_t *cand;    // [kDecodeUnion] decode partition candidates
-    int *pcount;       // [decode partitions]
-    uint64_t *pmin;    // [decode partitions]
+    uint64_t *cand;    // [decode_batch][kDecodeUnion] decode partition candidates
+    int *pcount;       // [decode_batch][kDecodeMaxParts]
+    uint64_t *pmin;    // [decode_batch][kDecodeMaxParts]
     bool decode_ok;    // single-token path available (max_rows small enough)
+    int decode_batch;  // sequences per batched decode call: min(max_tokens, kDecodeMaxBatch)
     // per-kernel timing (ds_indexer_timing)
     struct Mark {
         int cls;
@@ -183,12 +184,13 @@ int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, i
     ix->decode_ok = max_rows <= kDecodeMaxRows;
 
     const size_t s_bytes = (size_t)max_tokens * (size_t)ix->ldS * sizeof(float);
-    const int64_t parts = (max_rows + dsi::kDecodePart - 1) / dsi::kDecodePart;
+    ix->decode_batch = (int)(max_tokens < dsi::kDecodeMaxBatch ? max_tokens : dsi::kDecodeMaxBatch);
+    const size_t nb = (size_t)ix->decode_batch;
     bool ok = hipMalloc((void **)&ix->S, s_bytes) == hipSuccess;
     if (ok && ix->decode_ok) {
-        ok = hipMalloc((void **)&ix->cand, sizeof(uint64_t) * dsi::kDecodeUnion) == hipSuccess &&
-             hipMalloc((void **)&ix->pcount, sizeof(int) * (size_t)parts) == hipSuccess &&
-             hipMalloc((void **)&ix->pmin, sizeof(uint64_t) * (size_t)parts) == hipSuccess;
+        ok = hipMalloc((void **)&ix->cand, sizeof(uint64_t) * dsi::kDecodeUnion * nb) == hipSuccess &&
+             hipMalloc((void **)&ix->pcount, sizeof(int) * dsi::kDecodeMaxParts * nb) == hipSuccess &&
+             hipMalloc((void **)&ix->pmin, sizeof(uint64_t) * dsi::kDecodeMaxParts * nb) == hipSuccess;
     }
     if (!ok) {
         (void)hipGetLastError();
@@ -249,6 +251,50 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
             e = timed(ix, DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
                 return dsi::launch_topk_stream(ix->S, ix->ldS, pos, (int)T, (int)N, ratio, topk,
                                                out, s, tm);
+            });
+    }
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_indexer_score_topk_batch(ds_indexer *ix, const void *q, const void *k, const float *w,
+                                const int32_t *pos, int64_t B, int64_t N, int ratio, int topk,
+                                int32_t *out, void *stream)
+{
+    // B sequences of one query token each: the checks of a call with T = B
+    int st = check_call(ix, q, k, w, pos, B, N, ratio, out);
+    if (st != DS_OK)
+        return st;
+    if (topk < 1)
+        return DS_ERR_INVALID_ARG;
+    if (topk > ix->max_topk || B > ix->decode_batch)
+        return DS_ERR_CAPACITY;
+    if (!ix->decode_ok)
+        return DS_ERR_UNSUPPORTED;
+    if (B == 0)
+        return DS_OK;
+    DeviceGuard g(ix->device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    const dsi::Problem p = problem(ix, q, k, w, pos, 1, N, ratio);
+    hipError_t e;
+    if (N <= topk) {
+        e = timed(ix, DS_KERNEL_DECODE_SELECT, [&](dsi::Timing *tm) {
+            return dsi::launch_sequential_rows(pos, (int)B, (int)N, ratio, topk, out, s, tm);
+        });
+    } else {
+        dsi::DecodeLists dl;
+        dl.kp = decode_kp(N, topk);
+        dl.cand = ix->cand;
+        dl.pcount = ix->pcount;
+        dl.pmin = ix->pmin;
+        e = timed(ix, DS_KERNEL_DECODE_SCORE, [&](dsi::Timing *tm) {
+            return dsi::launch_decode_scorer(p, topk, ix->S, dl, s, tm, (int)B, ix->ldS);
+        });
+        if (e == hipSuccess)
+            e = timed(ix, DS_KERNEL_DECODE_SELECT, [&](dsi::Timing *tm) {
+                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, dl, out, s, tm,
+                                                 (int)B, ix->ldS);
             });
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;

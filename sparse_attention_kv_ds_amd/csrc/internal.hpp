@@ -58,6 +58,9 @@ constexpr int kDecodePart = 512;
 constexpr int kDecodeUnion = 16384;
 // most decode partitions: each lists at least 8 candidates
 constexpr int kDecodeMaxParts = kDecodeUnion / 8;
+// most sequences of one batched decode call (each owns kDecodeUnion candidate
+// slots and kDecodeMaxParts partition entries of the workspace)
+constexpr int kDecodeMaxBatch = 64;
 
 bool scorer_supported(int H, int D, int dtype);
 
@@ -79,11 +82,18 @@ struct DecodeLists {
     uint64_t *pmin = nullptr;
 };
 
+// Batched decode: B sequences of one query token each, sequence b with its
+// own q[b] (H x D), K rows k + b * N * D, weights w[b], position pos[b], score
+// row S + b * ldS, candidate slots cand + b * kDecodeUnion, partition entries
+// pcount/pmin + b * kDecodeMaxParts and output out + b * topk.  B = 1 is the
+// single-token call.
+
 // Same for a single token (T == 1): one work-group per kDecodePart-row
 // partition streams K; writes S[j] for j < n and, with dl.cand, the
 // partition's candidate list.
 hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const DecodeLists &dl,
-                                hipStream_t st, Timing *tm = nullptr);
+                                hipStream_t st, Timing *tm = nullptr, int B = 1,
+                                long long ldS = 0);
 
 // Per-token streaming top-k over S rows (one wave per token); skip path for
 // tokens whose visible rows all fit.
@@ -97,7 +107,7 @@ hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos,
 // short.
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
                                 const DecodeLists &dl, int32_t *out, hipStream_t st,
-                                Timing *tm = nullptr);
+                                Timing *tm = nullptr, int B = 1, long long ldS = 0);
 
 // Every token's rows 0 .. n_t-1, then -1, in out[T][topk] (for N <= topk,
 // where every visible row is selected and nothing needs scoring).

@@ -264,8 +264,23 @@ template <int H, int D, int DT, int WAVES, int NB>
 __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int N, int ratio, int min_rows, float *__restrict__ S, int kp,
-    uint64_t *__restrict__ cand, int *__restrict__ pcount, uint64_t *__restrict__ pmin)
+    uint64_t *__restrict__ cand, int *__restrict__ pcount, uint64_t *__restrict__ pmin,
+    long long ldS)
 {
+    // sequence blockIdx.y of a batched call (0 for a single token)
+    {
+        const int sb = blockIdx.y;
+        q += (size_t)sb * H * D;
+        k += (size_t)sb * N * D;
+        w += sb * H;
+        pos += sb;
+        S += sb * ldS;
+        if (cand) {
+            cand += (size_t)sb * kDecodeUnion;
+            pcount += sb * kDecodeMaxParts;
+            pmin += sb * kDecodeMaxParts;
+        }
+    }
     constexpr int KS = D / 16;
     constexpr int MT = H > 32 ? 2 : 1;       // 32-head tiles of the query
     constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -492,13 +507,13 @@ constexpr int kDecBlocks = 4; // 32-row K blocks per decode wave
 
 template <int H, int D, int DT>
 hipError_t decode_one(const Problem &p, int min_rows, float *S, const DecodeLists &dl,
-                      hipStream_t st, Timing *tm)
+                      hipStream_t st, Timing *tm, int B, long long ldS)
 {
     constexpr int ROWS = kDecWaves * kDecBlocks * 32; // per work-group
     return launch_kernel(decode_scorer_kernel<H, D, DT, kDecWaves, kDecBlocks>,
-                         dim3((p.N + ROWS - 1) / ROWS), dim3(kDecWaves * 64), 0, st, tm, true,
+                         dim3((p.N + ROWS - 1) / ROWS, B), dim3(kDecWaves * 64), 0, st, tm, true,
                          true, p.q, p.k, p.w, p.pos, p.N, p.ratio, min_rows, S, dl.kp, dl.cand,
-                         dl.pcount, dl.pmin);
+                         dl.pcount, dl.pmin, ldS);
 }
 
 // (H, D, dtype) -> instantiation
@@ -524,9 +539,9 @@ template <int H, int D, int DT> struct PrefillF {
 };
 template <int H, int D, int DT> struct DecodeF {
     static hipError_t run(const Problem &p, int m, float *S, const DecodeLists *dl, hipStream_t st,
-                          Timing *tm)
+                          Timing *tm, int B, long long ldS)
     {
-        return decode_one<H, D, DT>(p, m, S, *dl, st, tm);
+        return decode_one<H, D, DT>(p, m, S, *dl, st, tm, B, ldS);
     }
 };
 
@@ -548,11 +563,11 @@ hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long 
 }
 
 hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const DecodeLists &dl,
-                                hipStream_t st, Timing *tm)
+                                hipStream_t st, Timing *tm, int B, long long ldS)
 {
-    if (p.T <= 0 || p.N <= 0)
+    if (p.T <= 0 || p.N <= 0 || B <= 0)
         return hipSuccess;
-    return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, &dl, st, tm);
+    return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, &dl, st, tm, B, ldS);
 }
 
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st)

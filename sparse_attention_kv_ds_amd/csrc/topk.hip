@@ -148,8 +148,18 @@ template <int MAXS, int MS, int NT>
 __global__ __launch_bounds__(NT) void decode_merge_kernel(
     const float *__restrict__ S, const int32_t *__restrict__ pos, int N, int ratio, int topk,
     int kp, const uint64_t *__restrict__ cand, const int *__restrict__ pcount,
-    const uint64_t *__restrict__ pmin, int32_t *__restrict__ out)
+    const uint64_t *__restrict__ pmin, int32_t *__restrict__ out, long long ldS)
 {
+    // sequence blockIdx.x of a batched call (0 for a single token)
+    {
+        const int sb = blockIdx.x;
+        S += sb * ldS;
+        pos += sb;
+        cand += (size_t)sb * kDecodeUnion;
+        pcount += sb * kDecodeMaxParts;
+        pmin += sb * kDecodeMaxParts;
+        out += (size_t)sb * topk;
+    }
     constexpr int NW = NT / 64;
     constexpr int PPT = (kDecodeMaxParts + NT - 1) / NT;
     extern __shared__ uint64_t fb_buf[];
@@ -283,7 +293,7 @@ hipError_t topk_stream_one(const float *S, long long ldS, const int32_t *pos, in
 template <int MAXS>
 hipError_t merge_one(const float *S, const int32_t *pos, int N, int ratio, int topk, int kp,
                      const uint64_t *cand, const int *pcount, const uint64_t *pmin, int32_t *out,
-                     hipStream_t st, Timing *tm)
+                     hipStream_t st, Timing *tm, int B, long long ldS)
 {
     const size_t lds = (size_t)MAXS * 64 * sizeof(uint64_t);
     const long long U = (long long)((N + kDecodePart - 1) / kDecodePart) * kp;
@@ -291,10 +301,11 @@ hipError_t merge_one(const float *S, const int32_t *pos, int N, int ratio, int t
     // (sixteen waves, or three pivots per barrier, measured slower)
     constexpr int NT = 256;
     if (U <= 16 * NT)
-        return launch_kernel(decode_merge_kernel<MAXS, 16, NT>, dim3(1), dim3(NT), lds, st, tm,
-                             true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
-    return launch_kernel(decode_merge_kernel<MAXS, kDecodeUnion / NT, NT>, dim3(1), dim3(NT), lds,
-                         st, tm, true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out);
+        return launch_kernel(decode_merge_kernel<MAXS, 16, NT>, dim3(B), dim3(NT), lds, st, tm,
+                             true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out, ldS);
+    return launch_kernel(decode_merge_kernel<MAXS, kDecodeUnion / NT, NT>, dim3(B), dim3(NT), lds,
+                         st, tm, true, true, S, pos, N, ratio, topk, kp, cand, pcount, pmin, out,
+                         ldS);
 }
 
 // ---------------------------------------------------------------------------
@@ -346,18 +357,21 @@ hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos,
 }
 
 hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int ratio, int topk,
-                                const DecodeLists &dl, int32_t *out, hipStream_t st, Timing *tm)
+                                const DecodeLists &dl, int32_t *out, hipStream_t st, Timing *tm,
+                                int B, long long ldS)
 {
+    if (B <= 0)
+        return hipSuccess;
     const int kp = dl.kp;
+    auto *c = dl.cand;
+    auto *pc = dl.pcount;
+    auto *pm = dl.pmin;
     switch (select_slots(topk, 64)) {
-    case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
-    case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
-    case 16:
-        return merge_one<16>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
-    case 32:
-        return merge_one<32>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
-    default:
-        return merge_one<64>(S, pos, N, ratio, topk, kp, dl.cand, dl.pcount, dl.pmin, out, st, tm);
+    case 4: return merge_one<4>(S, pos, N, ratio, topk, kp, c, pc, pm, out, st, tm, B, ldS);
+    case 8: return merge_one<8>(S, pos, N, ratio, topk, kp, c, pc, pm, out, st, tm, B, ldS);
+    case 16: return merge_one<16>(S, pos, N, ratio, topk, kp, c, pc, pm, out, st, tm, B, ldS);
+    case 32: return merge_one<32>(S, pos, N, ratio, topk, kp, c, pc, pm, out, st, tm, B, ldS);
+    default: return merge_one<64>(S, pos, N, ratio, topk, kp, c, pc, pm, out, st, tm, B, ldS);
     }
 }
 

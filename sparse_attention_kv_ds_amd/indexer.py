@@ -33,7 +33,8 @@ KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select")
 
 EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
-           "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all")
+           "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all",
+           "ds_indexer_score_topk_batch")
 
 
 class IndexerError(RuntimeError):
@@ -57,6 +58,8 @@ def _load() -> ctypes.CDLL:
     lib.ds_indexer_create.argtypes = [ctypes.POINTER(P), I, I, I, I, I, I64, I64]
     lib.ds_indexer_score_topk.restype = I
     lib.ds_indexer_score_topk.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P]
+    lib.ds_indexer_score_topk_batch.restype = I
+    lib.ds_indexer_score_topk_batch.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P]
     lib.ds_indexer_destroy.restype = None
     lib.ds_indexer_destroy.argtypes = [P]
     lib.ds_indexer_scores.restype = I
@@ -96,6 +99,10 @@ def ds_indexer_create(device: int, n_heads: int, head_dim: int, dtype: int, max_
 
 def ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream) -> int:
     return _lib.ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream)
+
+
+def ds_indexer_score_topk_batch(handle, q, k, w, pos, B, N, ratio, topk, out, stream) -> int:
+    return _lib.ds_indexer_score_topk_batch(handle, q, k, w, pos, B, N, ratio, topk, out, stream)
 
 
 def ds_indexer_destroy(handle) -> None:
@@ -206,6 +213,29 @@ class Indexer:
                                    pos.data_ptr(), T, N, ratio, topk, out.data_ptr(), stream)
         if st != DS_OK:
             raise IndexerError(st, "ds_indexer_score_topk")
+        return out
+
+    def score_topk_batch(self, q, k, w, pos, ratio: int, topk: int, out=None):
+        """Batched decode (ds_indexer_score_topk_batch): q [B, H, D], k [B, N, D],
+        w [B, H], pos [B]; returns out [B, topk]."""
+        import torch
+        dev = torch.device("cuda", self.device)
+        B = pos.shape[0]
+        if k.dim() != 3 or k.shape[0] != B:
+            raise ValueError(f"k must be [B, N, D]; got {tuple(k.shape)}")
+        N = k.shape[1]
+        _, _, stream = self._check(q, k[0] if B else k.reshape(0, self.D), w, pos)
+        if not k.is_contiguous() or k.device != dev:
+            raise ValueError(f"k must be a contiguous tensor on {dev}")
+        if out is None:
+            out = torch.empty((B, topk), dtype=torch.int32, device=dev)
+        elif (out.dtype != torch.int32 or tuple(out.shape) != (B, topk) or not out.is_contiguous()
+              or out.device != dev):
+            raise ValueError("out must be a contiguous int32 [B, topk] tensor on the device")
+        st = ds_indexer_score_topk_batch(self.handle, q.data_ptr(), k.data_ptr(), w.data_ptr(),
+                                         pos.data_ptr(), B, N, ratio, topk, out.data_ptr(), stream)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_score_topk_batch")
         return out
 
     def timing(self, enable: bool) -> None:

@@ -67,6 +67,24 @@ WORKLOADS = {
 }
 
 
+# batched decode: B sequences, each drawn like the single-token workload with
+# seed + b (sequence b's q, k, w in that order), all at the same position
+DECODE_BATCHES = {"decode1m_b8": ("decode1m", 8)}
+
+
+def make_decode_batch(name: str):
+    """Inputs of a batched decode workload: q [B,H,D], k [B,N,D] (uint16 bits),
+    w [B,H], pos [B] and the per-sequence workload."""
+    base, B = DECODE_BATCHES[name]
+    wl = WORKLOADS[base]
+    qs, ks, ws = [], [], []
+    for b in range(B):
+        q, k, w = draw(wl.T, wl.N, wl.H, wl.D, wl.dtype, wl.dist, wl.seed + b)
+        qs.append(q[0]); ks.append(k); ws.append(w[0])
+    pos = np.full(B, wl.p0, dtype=np.int32)
+    return {"q": np.stack(qs), "k": np.stack(ks), "w": np.stack(ws), "pos": pos, "wl": wl, "B": B}
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to nearest-even bfloat16; return the raw uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                                            "ds_indexer_destroy", "ds_indexer_scores",
                                            "ds_indexer_status_str", "ds_indexer_timing",
                                            "ds_indexer_timing_read", "ds_sparse_attention",
-                                           "ds_sparse_attention_all"])
+                                           "ds_sparse_attention_all",
+                                           "ds_indexer_score_topk_batch"])
 
 
 def test_every_declared_symbol_is_exported(ix):
@@ -86,6 +87,7 @@ def test_create_null_out_pointer(ix):
 
 def test_calls_on_null_handle(ix):
     assert ix.ds_indexer_score_topk(None, 16, 16, 16, 16, 1, 1, 4, 1, 16, None) == -1
+    assert ix.ds_indexer_score_topk_batch(None, 16, 16, 16, 16, 2, 1, 4, 1, 16, None) == -1
     assert ix.ds_indexer_scores(None, 16, 16, 16, 16, 1, 1, 4, 16, None) == -1
     ix.ds_indexer_destroy(None)  # accepted and ignored
     assert ix.ds_indexer_timing(None, 1) == -1

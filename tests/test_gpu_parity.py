@@ -252,6 +252,80 @@ def test_decode_integer_bit_exact(lib, orc, N, topk, dtype):
                    topk=topk, where=f"decode N={N} pos={p}")
 
 
+def batch_run(lib, q, k, w, pos, *, H, D, dtype, ratio, topk):
+    """ds_indexer_score_topk_batch on host arrays: q [B,H,D], k [B,N,D], w [B,H], pos [B]."""
+    B, N = len(pos), k.shape[1]
+    ix = lib.Indexer(H, D, dtype, max(topk, 1), max(B, 1), max(N, 1), device=0)
+    try:
+        tq, tk, tw, tp = dev_inputs(q, k, w, pos)
+        out = ix.score_topk_batch(tq, tk, tw, tp, ratio, topk)
+        torch.cuda.synchronize(DEV)
+        return out.cpu().numpy()
+    finally:
+        ix.close()
+
+
+@pytest.mark.parametrize("B,N,topk,dtype", [(5, 5000, 512, "f16"), (3, 700, 512, "bf16"),
+                                            (9, 1100, 48, "f16"), (2, 300, 512, "f16")])
+def test_decode_batch_integer_bit_exact(lib, orc, B, N, topk, dtype):
+    """Each sequence of a batched decode call equals the oracle on that sequence
+    alone; positions differ per sequence (all rows, half the rows, all-fit, none)."""
+    say(f"batched decode int B={B} N={N} k={topk} {dtype}")
+    rng = np.random.default_rng(B * 1000 + N)
+    H, D = 64, 128
+    qs, ks, ws = [], [], []
+    for b in range(B):
+        q, k, w, _ = rand_int_case(rng, 1, N, H, D, -4, 4, 4, 1, dtype)
+        qs.append(q[0]); ks.append(k); ws.append(w[0])
+    choices = [4 * N - 1, 4 * N + 77, 2 * N + 1, 4 * min(topk, N) - 1, -3, 4 * (N // 3)]
+    pos = np.array([choices[b % len(choices)] for b in range(B)], np.int32)
+    q, k, w = np.stack(qs), np.stack(ks), np.stack(ws)
+    out = batch_run(lib, q, k, w, pos, H=H, D=D, dtype=dtype, ratio=4, topk=topk)
+    for b in range(B):
+        want = orc.score_topk(q[b:b + 1], k[b], w[b:b + 1], pos[b:b + 1], H=H, D=D, dtype=dtype,
+                              ratio=4, topk=topk, threads=8)
+        assert np.array_equal(out[b], want[0]), f"sequence {b} (pos {pos[b]}) differs"
+
+
+def test_decode_batch_equals_single_calls(lib):
+    """Gaussian sequences: the batched call gives every sequence bit for bit what a
+    single-token call gives it, including a sequence whose rows all fit."""
+    say("batched decode vs single calls (gaussian)")
+    rng = np.random.default_rng(8)
+    B, N, H, D, topk = 6, 70000, 64, 128, 512
+    q = synth.to_bits(rng.standard_normal((B, H, D)) / np.sqrt(128.0), "bf16")
+    k = synth.to_bits(rng.standard_normal((B, N, D)) / np.sqrt(128.0), "bf16")
+    w = rng.random((B, H), dtype=np.float32)
+    pos = np.array([4 * N - 1, 4 * N - 1, 3 * N, 1000, 4 * N - 1, 4 * N + 5], np.int32)
+    out = batch_run(lib, q, k, w, pos, H=H, D=D, dtype="bf16", ratio=4, topk=topk)
+    for b in range(B):
+        one = gpu_run(lib, q[b:b + 1], k[b], w[b:b + 1], pos[b:b + 1], H=H, D=D, dtype="bf16",
+                      ratio=4, topk=topk)
+        assert np.array_equal(out[b], one[0]), f"sequence {b} differs from its single call"
+    check_all_tokens(out, None, pos, 4, N, topk, "batched decode")
+
+
+def test_decode1m_batch_full_size(lib, orc):
+    """Eight 1M-token sequences (fp16 Gaussian, 262144 rows each) in one call: two of
+    them against the oracle (tolerance and tie margin), all eight against single calls."""
+    say("full-size batched decode, 8 x 262144 rows")
+    d = synth.make_decode_batch("decode1m_b8")
+    wl, B = d["wl"], d["B"]
+    out = batch_run(lib, d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
+                    ratio=wl.ratio, topk=wl.topk)
+    for b in range(B):
+        one, sc = gpu_run(lib, d["q"][b:b + 1], d["k"][b], d["w"][b:b + 1], d["pos"][b:b + 1],
+                          H=wl.H, D=wl.D, dtype=wl.dtype, ratio=wl.ratio, topk=wl.topk,
+                          scores=True)
+        assert np.array_equal(out[b], one[0]), f"sequence {b} differs from its single call"
+        if b in (0, B - 1):
+            _, osc = orc.score_topk(d["q"][b:b + 1], d["k"][b], d["w"][b:b + 1],
+                                    d["pos"][b:b + 1], H=wl.H, D=wl.D, dtype=wl.dtype,
+                                    ratio=wl.ratio, topk=wl.topk, want_scores=True, threads=16)
+            n = int(visible(d["pos"][b:b + 1], wl.ratio, wl.N)[0])
+            check_tolerant(out[b], sc[0], osc[0], n, wl.topk, f"decode1m_b8 sequence {b}")
+
+
 def test_decode_fallback_paths_exact(lib, orc):
     """Scores rising with the row concentrate the best rows in the last partitions
     (their short candidate lists cannot be trusted), and all-equal scores make
