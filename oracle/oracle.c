@@ -99,6 +99,64 @@ static double decode(uint16_t bits, int dtype)
     return dtype == ORACLE_F16 ? oracle_half_to_double(bits) : oracle_bf16_to_double(bits);
 }
 
+/* Round a double to the nearest value with `sig` significant bits (ties to
+ * even), for a format whose smallest normal exponent is emin and whose
+ * subnormals share the quantum 2^(emin - sig + 1); returns the integer
+ * significand n and the exponent E of the result n * 2^(E - sig + 1) (n <
+ * 2^(sig-1) only for subnormals).  a > 0. */
+static void round_sig(double a, int sig, int emin, double *n, int *E)
+{
+    int ex;
+    frexp(a, &ex);        /* a = m * 2^ex, 0.5 <= m < 1: leading bit 2^(ex-1) */
+    int e = ex - 1;
+    if (e < emin)
+        e = emin;         /* subnormal range: fixed quantum */
+    double q = ldexp(1.0, e - sig + 1);
+    double r = nearbyint(a / q); /* a / q is exact (power-of-two divisor); ties to even */
+    if (r >= ldexp(1.0, sig)) { /* carried into the next binade */
+        r = ldexp(1.0, sig - 1);
+        ++e;
+    }
+    *n = r;
+    *E = e;
+}
+
+/* double -> IEEE binary16 bits, round to nearest even; overflow -> infinity. */
+uint16_t oracle_double_to_half(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v), n;
+    int E;
+    if (isnan(v))
+        return 0x7E00;
+    if (a == 0.0)
+        return sign;
+    round_sig(a, 11, -14, &n, &E);
+    if (n < 1024.0) /* subnormal (or zero) */
+        return (uint16_t)(sign | (uint16_t)n);
+    if (E + 15 >= 31)
+        return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | ((E + 15) << 10) | ((int)n - 1024));
+}
+
+/* double -> bfloat16 bits, round to nearest even; overflow -> infinity. */
+uint16_t oracle_double_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v), n;
+    int E;
+    if (isnan(v))
+        return 0x7FC0;
+    if (a == 0.0)
+        return sign;
+    round_sig(a, 8, -126, &n, &E);
+    if (n < 128.0)
+        return (uint16_t)(sign | (uint16_t)n);
+    if (E + 127 >= 255)
+        return (uint16_t)(sign | 0x7F80);
+    return (uint16_t)(sign | ((E + 127) << 7) | ((int)n - 128));
+}
+
 /* Number of compressed rows visible to a token at absolute position pos:
  * row j is visible iff ratio*j + ratio - 1 <= pos and j < N. */
 int64_t oracle_visible_rows(int64_t pos, int64_t ratio, int64_t n_rows)
@@ -632,4 +690,106 @@ int oracle_sparse_attention_all(const uint16_t *q, const uint16_t *kp, const uin
         return ORACLE_ERR_ARG;
     return attention_common(q, kp, vp, kl, vl, NULL, pos, T, N, L, HA, DK, DV, 0, ratio, window,
                             scale, dtype, tokens, n_out, out, threads);
+}
+
+/* ======================================================================== *
+ * The indexer's query projection, the step just before the scorer: the
+ * query rows of the index heads are a linear map of each token's query
+ * input ("How I made DeepSeek 12x faster on a Mac Studio" names the big Q
+ * projection ahead of the indexer; its weights are model parameters, here
+ * synthetic).  For token t and output feature o = h * D + d:
+ *
+ *   q[t][o] = round_dtype( sum_i x[t][i] * wq[o][i] )
+ *
+ * x [T][d_in] and wq [O][d_in] are raw fp16/bf16 bits; the sum is taken in
+ * double over exactly decoded operands and rounded once, to nearest even,
+ * into the storage type (the scorer reads q in that type).  Non-finite
+ * inputs or results are rejected.
+ * ======================================================================== */
+
+typedef struct {
+    const uint16_t *x, *wq;
+    int64_t T, din, O;
+    int dtype;
+    uint16_t *q;
+    int nthreads, tid, status;
+} proj_job;
+
+static void *run_proj_job(void *arg)
+{
+    proj_job *jb = (proj_job *)arg;
+    int64_t t, o, i;
+    jb->status = ORACLE_OK;
+    for (t = jb->tid; t < jb->T; t += jb->nthreads) {
+        for (o = 0; o < jb->O; ++o) {
+            double acc = 0.0;
+            for (i = 0; i < jb->din; ++i) {
+                const double a = decode(jb->x[t * jb->din + i], jb->dtype);
+                const double b = decode(jb->wq[o * jb->din + i], jb->dtype);
+                if (!isfinite(a) || !isfinite(b)) {
+                    jb->status = ORACLE_ERR_NONFINITE;
+                    return NULL;
+                }
+                acc += a * b;
+            }
+            jb->q[t * jb->O + o] = jb->dtype == ORACLE_F16 ? oracle_double_to_half(acc)
+                                                          : oracle_double_to_bf16(acc);
+            if (!isfinite(decode(jb->q[t * jb->O + o], jb->dtype))) {
+                jb->status = ORACLE_ERR_NONFINITE;
+                return NULL;
+            }
+        }
+    }
+    return NULL;
+}
+
+int oracle_project_q(const uint16_t *x, const uint16_t *wq, int64_t T, int64_t din, int64_t O,
+                     int dtype, uint16_t *q, int threads)
+{
+    proj_job *jobs;
+    pthread_t *tids;
+    int *started;
+    int th, status = ORACLE_OK;
+    if (T < 0 || din < 1 || O < 1 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return ORACLE_ERR_ARG;
+    if (T > 0 && (!x || !wq || !q))
+        return ORACLE_ERR_ARG;
+    if (threads < 1)
+        threads = 1;
+    jobs = (proj_job *)calloc((size_t)threads, sizeof(proj_job));
+    tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    started = (int *)calloc((size_t)threads, sizeof(int));
+    if (!jobs || !tids || !started) {
+        free(jobs);
+        free(tids);
+        free(started);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (th = 0; th < threads; ++th) {
+        jobs[th].x = x;
+        jobs[th].wq = wq;
+        jobs[th].T = T;
+        jobs[th].din = din;
+        jobs[th].O = O;
+        jobs[th].dtype = dtype;
+        jobs[th].q = q;
+        jobs[th].nthreads = threads;
+        jobs[th].tid = th;
+    }
+    for (th = 1; th < threads; ++th)
+        started[th] = pthread_create(&tids[th], NULL, run_proj_job, &jobs[th]) == 0;
+    run_proj_job(&jobs[0]);
+    for (th = 1; th < threads; ++th) {
+        if (started[th])
+            pthread_join(tids[th], NULL);
+        else
+            run_proj_job(&jobs[th]);
+    }
+    for (th = 0; th < threads; ++th)
+        if (jobs[th].status != ORACLE_OK)
+            status = jobs[th].status;
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
 }

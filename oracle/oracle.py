@@ -7,9 +7,10 @@ imports this module.
 The oracle computes, for each query token, the lightning-indexer score of
 every causally visible compressed row in double precision, sorts all of them
 by (score descending, row ascending), keeps the first min(n_t, topk), and
-returns those rows in ascending order padded with -1; and the sparse
-attention of each token over its local raw rows plus its selected pooled
-rows (both definitions are written out in oracle.c, with their sources).
+returns those rows in ascending order padded with -1; the sparse attention of
+each token over its local raw rows plus its selected pooled rows; and the
+query projection ahead of the indexer (the definitions are written out in
+oracle.c, with their sources).
 """
 from __future__ import annotations
 
@@ -61,6 +62,12 @@ class Oracle:
         lib.oracle_sparse_attention.restype = I
         lib.oracle_sparse_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                                 ctypes.c_double, I, P, I64, P, I]
+        lib.oracle_double_to_half.restype = ctypes.c_uint16
+        lib.oracle_double_to_half.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_project_q.restype = I
+        lib.oracle_project_q.argtypes = [P, P, I64, I64, I64, I, P, I]
         lib.oracle_sparse_attention_all.restype = I
         lib.oracle_sparse_attention_all.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                                     ctypes.c_double, I, P, I64, P, I]
@@ -159,6 +166,45 @@ class Oracle:
             raise OracleError(f"oracle_sparse_attention: {STATUS.get(st, st)}")
         return out
 
+
+    def double_to_half(self, v: float) -> int:
+        return self.lib.oracle_double_to_half(float(v))
+
+    def double_to_bf16(self, v: float) -> int:
+        return self.lib.oracle_double_to_bf16(float(v))
+
+    def project_q(self, x_bits, wq_bits, *, dtype: str, threads: int = 1):
+        """The query projection: q = round_dtype(x . wq^T) (definition in oracle.c).
+        x_bits uint16 [T, d_in], wq_bits uint16 [O, d_in]; returns uint16 [T, O]."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        wq_bits = np.ascontiguousarray(wq_bits, dtype=np.uint16)
+        T, din = x_bits.shape
+        O = wq_bits.shape[0]
+        if wq_bits.shape[1] != din:
+            raise OracleError("oracle: inconsistent shapes")
+        q = np.empty((T, O), dtype=np.uint16)
+        st = self.lib.oracle_project_q(x_bits.ctypes.data_as(ctypes.c_void_p),
+                                       wq_bits.ctypes.data_as(ctypes.c_void_p), T, din, O,
+                                       DTYPES[dtype], q.ctypes.data_as(ctypes.c_void_p),
+                                       int(threads))
+        if st != 0:
+            raise OracleError(f"oracle_project_q: {STATUS.get(st, st)}")
+        return q
+
+    def project_score_topk(self, x_bits, wq_bits, k_bits, w, pos, *, H: int, D: int, dtype: str,
+                           ratio: int, topk: int, tokens=None, want_scores: bool = False,
+                           threads: int = 1):
+        """The projection followed by the indexer: q = project_q(x, wq) reshaped to
+        [T, H, D], then score_topk on it (tokens: the rows of x projected and scored)."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        if tokens is not None:
+            tok = np.ascontiguousarray(tokens, dtype=np.int64)
+            x_bits, pos, w = x_bits[tok], pos[tok], w[tok]
+        q = self.project_q(x_bits, wq_bits, dtype=dtype, threads=threads)
+        return self.score_topk(q.reshape(len(pos), H, D), k_bits, w, pos, H=H, D=D, dtype=dtype,
+                               ratio=ratio, topk=topk, want_scores=want_scores, threads=threads)
 
     def sparse_attention_all(self, q_bits, kp_bits, vp_bits, kl_bits, vl_bits, pos, *, dtype: str,
                              ratio: int, window: int, scale: float, tokens=None, threads: int = 1):

@@ -632,6 +632,82 @@ def pin_attn_all_constant_keys_mean(orc: Oracle):
                 (W, p, got[t, 0, 0], float(want))
 
 
+def pin_round_to_storage_types(orc: Oracle):
+    """Rounding a double into fp16 / bf16 (the step after the query projection):
+    every finite pattern round-trips; every midpoint between neighbours rounds
+    to the even pattern and a nudge either way picks the nearer one -- checked
+    against numpy's float16 conversion, and for bf16 against rounding the exact
+    float32 value of the midpoint (synth's bit-level converter)."""
+    f16 = np.arange(0x7C00, dtype=np.uint16)            # +0 .. largest finite
+    vals = f16.view(np.float16).astype(np.float64)
+    for b, v in zip(f16[::37], vals[::37]):
+        assert orc.double_to_half(v) == b and orc.double_to_half(-v) == (b | 0x8000)
+    mids = (vals[:-1] + vals[1:]) / 2
+    for i in range(0, len(mids), 13):
+        m = mids[i]
+        for x in (m, np.nextafter(m, 0.0), np.nextafter(m, np.inf)):
+            want = int(np.float16(x).view(np.uint16))
+            assert orc.double_to_half(x) == want, (x, hex(orc.double_to_half(x)), hex(want))
+    assert orc.double_to_half(65520.0) == 0x7C00 and orc.double_to_half(65519.99) == 0x7BFF
+    bf = np.arange(0x7F80, dtype=np.uint32)             # +0 .. largest finite bf16
+    bvals = (bf << 16).view(np.float32).astype(np.float64)
+    for b, v in zip(bf[::41], bvals[::41]):
+        assert orc.double_to_bf16(v) == b
+    bmids = (bvals[:-1] + bvals[1:]) / 2
+    for i in range(0, len(bmids), 17):
+        m = bmids[i]
+        for x in (m, np.nextafter(m, 0.0), np.nextafter(m, np.inf)):
+            want = int(synth.f32_to_bf16_bits(np.array([x], dtype=np.float32))[0]) \
+                if float(np.float32(x)) == x else None
+            if want is not None:
+                assert orc.double_to_bf16(x) == want, (x, hex(orc.double_to_bf16(x)), hex(want))
+            else:  # a nudge below float32 resolution: compare with the neighbours
+                lo_b, hi_b = int(bf[i]), int(bf[i + 1])
+                assert orc.double_to_bf16(x) == (lo_b if x < m else hi_b)
+
+
+def pin_project_q_exact(orc: Oracle):
+    """Integer-valued x and wq: every sum is exact, so q is the exact product
+    rounded once -- numpy's int64 matmul then float16 (fp16), or the exact
+    float32 value rounded to bf16; Gaussian fp16 operands against numpy's float64
+    matmul rounded to float16."""
+    rng = np.random.default_rng(31)
+    T, din, O = 5, 40, 9
+    xi = rng.integers(-8, 9, size=(T, din))
+    wi = rng.integers(-8, 9, size=(O, din))
+    exact = (xi @ wi.T).astype(np.float64)
+    got = orc.project_q(f16_bits(xi.astype(np.float64)), f16_bits(wi.astype(np.float64)),
+                        dtype="f16")
+    assert np.array_equal(got, exact.astype(np.float16).view(np.uint16))
+    got = orc.project_q(synth.to_bits(xi, "bf16"), synth.to_bits(wi, "bf16"), dtype="bf16")
+    assert np.array_equal(got, synth.f32_to_bf16_bits(exact.astype(np.float32)))
+    xg = synth.to_bits(rng.standard_normal((T, 64)), "f16")
+    wg = synth.to_bits(rng.standard_normal((O, 64)) * 0.1, "f16")
+    ref = (xg.view(np.float16).astype(np.float64) @ wg.view(np.float16).astype(np.float64).T)
+    assert np.array_equal(orc.project_q(xg, wg, dtype="f16"), ref.astype(np.float16).view(np.uint16))
+
+
+def pin_project_then_score(orc: Oracle):
+    """The projection feeds the indexer unchanged: projecting and scoring equals
+    scoring the q that numpy's exact projection gives (integer inputs)."""
+    rng = np.random.default_rng(41)
+    T, din, H, D, N, topk = 12, 24, 4, 8, 30, 6
+    xi = rng.integers(-3, 4, size=(T, din)).astype(np.float64)
+    wi = rng.integers(-2, 3, size=(H * D, din)).astype(np.float64)
+    k = f16_bits(rng.integers(-4, 5, size=(N, D)).astype(np.float64))
+    w = (rng.integers(0, 2, size=(T, H)) * 2 - 1).astype(np.float32)
+    pos = rng.integers(-1, 4 * N + 3, size=T).astype(np.int32)
+    q_ref = (xi @ wi.T).astype(np.float16).view(np.uint16).reshape(T, H, D)
+    want = orc.score_topk(q_ref, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk)
+    got = orc.project_score_topk(f16_bits(xi), f16_bits(wi), k, w, pos, H=H, D=D, dtype="f16",
+                                 ratio=4, topk=topk)
+    assert np.array_equal(got, want)
+    toks = np.array([3, 0, 7])
+    got_t = orc.project_score_topk(f16_bits(xi), f16_bits(wi), k, w, pos, H=H, D=D, dtype="f16",
+                                   ratio=4, topk=topk, tokens=toks)
+    assert np.array_equal(got_t, want[toks])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

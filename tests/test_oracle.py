@@ -52,6 +52,12 @@ MUTANTS = [
     ("f16_subnormal", "ldexp((double)frac, -24);", "ldexp((double)frac, -25);"),
     ("bf16_bias", "expo - 134); /*", "expo - 133); /*"),
     ("bf16_frac_bits", "int frac = bits & 0x7F;", "int frac = bits & 0x3F;"),
+    # query projection and rounding into the storage type
+    ("round_truncates", "double r = nearbyint(a / q);", "double r = floor(a / q);"),
+    ("round_half_away", "double r = nearbyint(a / q);", "double r = floor(a / q + 0.5);"),
+    ("proj_w_transposed", "jb->wq[o * jb->din + i]", "jb->wq[i * jb->O + o]"),
+    ("proj_skips_last_input", "for (i = 0; i < jb->din; ++i) {\n                const double a",
+     "for (i = 0; i + 1 < jb->din; ++i) {\n                const double a"),
     # sparse attention
     ("attn_scale_dropped", "s[r] = jb->scale * x;", "s[r] = x;"),
     ("attn_window_one_short", "lo = p - jb->window + 1;", "lo = p - jb->window + 2;"),
