@@ -26,7 +26,7 @@ that pass's step time is reported apart.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W = 200: the
                        GPU needs some tens of milliseconds of work to reach its full clock)
-       python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|decode1m_b8|attn32k|attn32k_r128
+       python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|decode1m_b8|qproj32k|attn32k|attn32k_r128
                                                                  (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --ceilings                               (vendor GEMM and plain-copy
@@ -154,6 +154,65 @@ ATTN_SECONDARY = ("attn32k_r128",)
 
 
 DECODE_BATCH = "decode1m_b8"
+PROJECTION = "qproj32k"
+
+
+def time_projection(name: str, steps: int, warmup: int):
+    """Time `steps` calls of the query projection fused ahead of the indexer on
+    the 32k chunk (projection, then score + top-k, in one call)."""
+    import numpy as np
+    import torch
+    from sparse_attention_kv_ds_amd import synth
+    from sparse_attention_kv_ds_amd.indexer import Indexer
+
+    dev = torch.device("cuda", 0)
+    d = synth.make_projection(name)
+    wl = d["wl"]
+    up = {kk: torch.from_numpy(np.ascontiguousarray(d[kk]).view(np.int16)).to(dev)
+          for kk in ("x", "wq", "k")}
+    w = torch.from_numpy(d["w"]).to(dev)
+    pos = torch.from_numpy(d["pos"]).to(dev)
+    out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
+    ix = Indexer(wl.H, wl.D, d["dtype"], wl.topk, wl.T, wl.N, device=0)
+
+    def call():
+        ix.project_score_topk(up["x"], up["wq"], up["k"], w, pos, wl.ratio, wl.topk, out=out)
+
+    def timed_steps():
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        t0.record()
+        for _ in range(steps):
+            call()
+        t1.record()
+        torch.cuda.synchronize(dev)
+        return t0.elapsed_time(t1) / steps
+
+    try:
+        for _ in range(warmup):
+            call()
+        ms = timed_steps()
+        ix.timing(True)
+        ix.timing_read()
+        ms_marked = timed_steps()
+        per = ix.timing_read()
+        ix.timing(False)
+    finally:
+        ix.close()
+    kernels = {c: v[0] / v[1] for c, v in per.items() if v[1]}
+    flops = 2.0 * wl.T * d["din"] * wl.H * wl.D
+    ach = flops / (kernels["project"] * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[d["dtype"]]
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/call ({ms_marked * 1e3:.1f} with kernel markers), "
+        + ", ".join(f"{c} {v * 1e3:.1f} us" for c, v in kernels.items())
+        + f"; projection {ach:.0f} TFLOP/s ({ach / peak * 100:.1f} % of {d['dtype']} MFMA peak)")
+    return {"workload": name, "dtype": d["dtype"], "ms_per_step": ms,
+            "ms_per_step_with_markers": ms_marked, "kernels_ms": kernels,
+            "value": wl.T / (ms * 1e-3), "unit": "query tokens/s (projection + score + top-k)",
+            "roofline": {"bound": "mfma", "kernel": "qproj", "achieved": ach, "peak": peak,
+                         "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                         "algorithmic_flops_per_launch": flops}}
 
 
 def time_decode_batch(name: str, steps: int, warmup: int):
@@ -568,7 +627,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD, *ATTN_SECONDARY,
-                                       DECODE_BATCH])
+                                       DECODE_BATCH, PROJECTION])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
@@ -608,6 +667,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    if args.only == PROJECTION:
+        print(json.dumps(time_projection(args.only, args.steps, args.warmup)))
+        return 0
     if args.only == DECODE_BATCH:
         res = time_decode_batch(args.only, args.steps, args.warmup)
         print(json.dumps(res))
@@ -665,6 +727,8 @@ def main():
     # the consumer of the indices (sparse attention over the selected rows)
     # several sequences of one query token each in one call (batched decode)
     line["secondary"].append(time_decode_batch(DECODE_BATCH, args.steps, min(args.warmup, 50)))
+    # the query projection fused ahead of the indexer
+    line["secondary"].append(time_projection(PROJECTION, args.steps, min(args.warmup, 50)))
     for name in (ATTN_WORKLOAD, *ATTN_SECONDARY):
         line["secondary"].append(time_attention(name, args.steps, min(args.warmup, 50)))
     if not args.no_cpu_baseline:

@@ -133,6 +133,38 @@ int ds_indexer_score_topk_batch(ds_indexer *ix, const void *q, const void *k, co
                                 int32_t *out, void *stream);
 
 /*
+ * The indexer's query projection, the step just before the scorer ("How I
+ * made DeepSeek 12x faster on a Mac Studio" names the big Q projection ahead
+ * of the indexer; its weights are a model parameter):
+ *   q[t][h*D + d] = round( sum_i x[t][i] * wq[h*D + d][i] )
+ * fp32 sums on the matrix cores, rounded once to nearest even into the
+ * handle's dtype, i.e. q in the [T][H][D] layout ds_indexer_score_topk reads.
+ *
+ *   x   [T][d_in]       dtype   each token's query input, device
+ *   wq  [H*D][d_in]     dtype   weights, the usual [out][in] layout, device
+ *   q   [T][H][D]       dtype   result (ds_indexer_project_q), device
+ *   d_in a positive multiple of 8; H*D a multiple of 128; T*d_in*2 and
+ *   H*D*d_in*2 below 2^31 bytes; x, wq, q 16-byte aligned.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY (T above max_tokens),
+ * DS_ERR_UNSUPPORTED (d_in or H*D outside the list) or DS_ERR_HIP.
+ */
+int ds_indexer_project_q(ds_indexer *ix, const void *x, const void *wq, int64_t T, int64_t d_in,
+                         void *q, void *stream);
+
+/*
+ * The projection fused ahead of the indexer: ds_indexer_project_q into the
+ * handle's own q buffer, then ds_indexer_score_topk on it, in one call (k, w,
+ * pos, N, ratio, topk, out as there).  When N <= topk nothing is projected or
+ * scored: every visible row is selected ("How I turned one oversized DeepSeek
+ * optimization into three merged oMLX PRs", section "3. Do not rank
+ * candidates when every candidate wins": the query projection is skipped
+ * too).  Errors as the two calls.
+ */
+int ds_indexer_project_score_topk(ds_indexer *ix, const void *x, const void *wq, const void *k,
+                                  const float *w, const int32_t *pos, int64_t T, int64_t N,
+                                  int64_t d_in, int ratio, int topk, int32_t *out, void *stream);
+
+/*
  * Release the handle and its device scratch.  NULL is accepted and ignored.
  * Waits for the handle's device to finish outstanding work first.
  */
@@ -160,6 +192,7 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
  *   DS_KERNEL_DECODE_SCORE   single-token scorer      (T == 1; it also lists each
  *                            512-row partition's best keys)
  *   DS_KERNEL_DECODE_SELECT  single-token selection   (T == 1; the merge of those lists)
+ *   DS_KERNEL_PROJECT        query projection         (ds_indexer_project_*)
  * The pages' own evidence is end-to-end prompt throughput with bracketing
  * controls ("How I turned one oversized DeepSeek optimization into three
  * merged oMLX PRs", section "Turn review feedback into an experiment"); this
@@ -177,7 +210,8 @@ enum {
     DS_KERNEL_SELECT = 1,
     DS_KERNEL_DECODE_SCORE = 2,
     DS_KERNEL_DECODE_SELECT = 3,
-    DS_KERNEL_CLASSES = 4
+    DS_KERNEL_PROJECT = 4,
+    DS_KERNEL_CLASSES = 5
 };
 
 int ds_indexer_timing(ds_indexer *ix, int enable);

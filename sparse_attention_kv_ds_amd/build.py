@@ -17,14 +17,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libds_indexer.so")
-SOURCES = ["api.cpp", "scorer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.cpp", "scorer.hip", "topk.hip", "attention.hip", "qproj.hip"]
 # Extra flags per source.  The scorer is built without NaN semantics: its
 # inputs are finite by contract, and with NaNs honoured every ReLU (fmaxf)
 # costs an extra canonicalising instruction.
 # MFMA accumulators are kept in ordinary VGPRs (the epilogue reads them with
 # VALU instructions; in AGPRs every read would cost an extra move).
 EXTRA = {"scorer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "qproj.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -17,6 +17,7 @@ struct ds_indexer {
     int64_t max_tokens, max_rows;
     long long ldS;     // row stride of the score scratch (floats)
     float *S;          // [max_tokens][ldS] scores
+    void *qbuf;        // [max_tokens][H][D] projected queries (ds_indexer_project_score_topk)
     uint64_t *cand;    // [decode_batch][kDecodeUnion] decode partition candidates
     int *pcount;       // [decode_batch][kDecodeMaxParts]
     uint64_t *pmin;    // [decode_batch][kDecodeMaxParts]
@@ -186,7 +187,8 @@ int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, i
     const size_t s_bytes = (size_t)max_tokens * (size_t)ix->ldS * sizeof(float);
     ix->decode_batch = (int)(max_tokens < dsi::kDecodeMaxBatch ? max_tokens : dsi::kDecodeMaxBatch);
     const size_t nb = (size_t)ix->decode_batch;
-    bool ok = hipMalloc((void **)&ix->S, s_bytes) == hipSuccess;
+    bool ok = hipMalloc((void **)&ix->S, s_bytes) == hipSuccess &&
+              hipMalloc(&ix->qbuf, (size_t)max_tokens * ix->H * ix->D * 2) == hipSuccess;
     if (ok && ix->decode_ok) {
         ok = hipMalloc((void **)&ix->cand, sizeof(uint64_t) * dsi::kDecodeUnion * nb) == hipSuccess &&
              hipMalloc((void **)&ix->pcount, sizeof(int) * dsi::kDecodeMaxParts * nb) == hipSuccess &&
@@ -195,6 +197,7 @@ int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, i
     if (!ok) {
         (void)hipGetLastError();
         hipFree(ix->S);
+        hipFree(ix->qbuf);
         hipFree(ix->cand);
         hipFree(ix->pcount);
         hipFree(ix->pmin);
@@ -254,6 +257,74 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
             });
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+namespace {
+
+// argument checks of the query projection (host only)
+int check_project(const ds_indexer *ix, const void *x, const void *wq, int64_t T, int64_t d_in,
+                  const void *q)
+{
+    if (!ix || T < 0 || d_in < 1)
+        return DS_ERR_INVALID_ARG;
+    if (T > 0 && (!x || !wq || !q))
+        return DS_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(q, 16))
+        return DS_ERR_INVALID_ARG;
+    const int64_t O = (int64_t)ix->H * ix->D;
+    if (d_in >= INT_MAX || !dsi::qproj_supported((int)d_in, (int)O, ix->dtype) ||
+        T * d_in * 2 >= ((int64_t)1 << 31) || O * d_in * 2 >= ((int64_t)1 << 31) ||
+        T * O * 2 >= ((int64_t)1 << 31))
+        return DS_ERR_UNSUPPORTED;
+    if (T > ix->max_tokens)
+        return DS_ERR_CAPACITY;
+    return DS_OK;
+}
+
+} // namespace
+
+int ds_indexer_project_q(ds_indexer *ix, const void *x, const void *wq, int64_t T, int64_t d_in,
+                         void *q, void *stream)
+{
+    const int st = check_project(ix, x, wq, T, d_in, q);
+    if (st != DS_OK)
+        return st;
+    if (T == 0)
+        return DS_OK;
+    const int64_t O = (int64_t)ix->H * ix->D;
+    DeviceGuard g(ix->device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    const hipError_t e = timed(ix, DS_KERNEL_PROJECT, [&](dsi::Timing *tm) {
+        return dsi::launch_qproj(x, wq, (int)T, (int)d_in, (int)O, ix->dtype, q,
+                                 (hipStream_t)stream, tm);
+    });
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_indexer_project_score_topk(ds_indexer *ix, const void *x, const void *wq, const void *k,
+                                  const float *w, const int32_t *pos, int64_t T, int64_t N,
+                                  int64_t d_in, int ratio, int topk, int32_t *out, void *stream)
+{
+    if (!ix)
+        return DS_ERR_INVALID_ARG;
+    // the checks of the scoring call, with the handle's q buffer standing in
+    int st = check_call(ix, T > 0 ? ix->qbuf : nullptr, k, w, pos, T, N, ratio, out);
+    if (st != DS_OK)
+        return st;
+    if (topk < 1)
+        return DS_ERR_INVALID_ARG;
+    if (topk > ix->max_topk)
+        return DS_ERR_CAPACITY;
+    st = check_project(ix, x, wq, T, d_in, ix->qbuf);
+    if (st != DS_OK)
+        return st;
+    if (N > topk) { // otherwise every visible row is selected: no projection
+        st = ds_indexer_project_q(ix, x, wq, T, d_in, ix->qbuf, stream);
+        if (st != DS_OK)
+            return st;
+    }
+    return ds_indexer_score_topk(ix, ix->qbuf, k, w, pos, T, N, ratio, topk, out, stream);
 }
 
 int ds_indexer_score_topk_batch(ds_indexer *ix, const void *q, const void *k, const float *w,
@@ -371,6 +442,7 @@ void ds_indexer_destroy(ds_indexer *ix)
         for (hipEvent_t e : ix->spare)
             (void)hipEventDestroy(e);
         hipFree(ix->S);
+        hipFree(ix->qbuf);
         hipFree(ix->cand);
         hipFree(ix->pcount);
         hipFree(ix->pmin);

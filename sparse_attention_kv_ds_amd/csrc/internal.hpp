@@ -114,6 +114,11 @@ hipError_t launch_decode_select(const float *S, const int32_t *pos, int N, int r
 hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, int topk,
                                   int32_t *out, hipStream_t st, Timing *tm = nullptr);
 
+// q[T][O] = round(x[T][K] . wq[O][K]^T) in dtype (qproj.hip)
+bool qproj_supported(int K, int O, int dtype);
+hipError_t launch_qproj(const void *x, const void *wq, int T, int K, int O, int dtype, void *q,
+                        hipStream_t st, Timing *tm = nullptr);
+
 // p[0..n) = v
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st);
 

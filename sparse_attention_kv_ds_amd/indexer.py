@@ -28,13 +28,14 @@ DS_KERNEL_SCORE = 0
 DS_KERNEL_SELECT = 1
 DS_KERNEL_DECODE_SCORE = 2
 DS_KERNEL_DECODE_SELECT = 3
-DS_KERNEL_CLASSES = 4
-KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select")
+DS_KERNEL_PROJECT = 4
+DS_KERNEL_CLASSES = 5
+KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select", "project")
 
 EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
            "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all",
-           "ds_indexer_score_topk_batch")
+           "ds_indexer_score_topk_batch", "ds_indexer_project_q", "ds_indexer_project_score_topk")
 
 
 class IndexerError(RuntimeError):
@@ -58,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.ds_indexer_create.argtypes = [ctypes.POINTER(P), I, I, I, I, I, I64, I64]
     lib.ds_indexer_score_topk.restype = I
     lib.ds_indexer_score_topk.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P]
+    lib.ds_indexer_project_q.restype = I
+    lib.ds_indexer_project_q.argtypes = [P, P, P, I64, I64, P, P]
+    lib.ds_indexer_project_score_topk.restype = I
+    lib.ds_indexer_project_score_topk.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, P, P]
     lib.ds_indexer_score_topk_batch.restype = I
     lib.ds_indexer_score_topk_batch.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P]
     lib.ds_indexer_destroy.restype = None
@@ -99,6 +104,16 @@ def ds_indexer_create(device: int, n_heads: int, head_dim: int, dtype: int, max_
 
 def ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream) -> int:
     return _lib.ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream)
+
+
+def ds_indexer_project_q(handle, x, wq, T, d_in, q, stream) -> int:
+    return _lib.ds_indexer_project_q(handle, x, wq, T, d_in, q, stream)
+
+
+def ds_indexer_project_score_topk(handle, x, wq, k, w, pos, T, N, d_in, ratio, topk, out,
+                                  stream) -> int:
+    return _lib.ds_indexer_project_score_topk(handle, x, wq, k, w, pos, T, N, d_in, ratio, topk,
+                                              out, stream)
 
 
 def ds_indexer_score_topk_batch(handle, q, k, w, pos, B, N, ratio, topk, out, stream) -> int:
@@ -213,6 +228,42 @@ class Indexer:
                                    pos.data_ptr(), T, N, ratio, topk, out.data_ptr(), stream)
         if st != DS_OK:
             raise IndexerError(st, "ds_indexer_score_topk")
+        return out
+
+    def _check_proj(self, x, wq):
+        import torch
+        dev = torch.device("cuda", self.device)
+        for name, t in (("x", x), ("wq", wq)):
+            if t.device != dev or not t.is_contiguous() or t.element_size() != 2 or t.dim() != 2:
+                raise ValueError(f"{name} must be a contiguous 2-D 16-bit tensor on {dev}")
+        if wq.shape[0] != self.H * self.D or wq.shape[1] != x.shape[1]:
+            raise ValueError(f"wq must be [H*D, d_in]; got {tuple(wq.shape)}, x {tuple(x.shape)}")
+        return x.shape[0], x.shape[1], torch.cuda.current_stream(dev).cuda_stream
+
+    def project_q(self, x, wq, out=None):
+        """The query projection (ds_indexer_project_q): x [T, d_in], wq [H*D, d_in]
+        (16-bit, the handle's dtype); returns q [T, H, D] as int16 bits."""
+        import torch
+        T, din, stream = self._check_proj(x, wq)
+        if out is None:
+            out = torch.empty((T, self.H, self.D), dtype=torch.int16, device=x.device)
+        st = ds_indexer_project_q(self.handle, x.data_ptr(), wq.data_ptr(), T, din,
+                                  out.data_ptr(), stream)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_project_q")
+        return out
+
+    def project_score_topk(self, x, wq, k, w, pos, ratio: int, topk: int, out=None):
+        """Projection then score + top-k in one call (ds_indexer_project_score_topk)."""
+        import torch
+        T, din, stream = self._check_proj(x, wq)
+        if out is None:
+            out = torch.empty((T, topk), dtype=torch.int32, device=x.device)
+        st = ds_indexer_project_score_topk(self.handle, x.data_ptr(), wq.data_ptr(), k.data_ptr(),
+                                           w.data_ptr(), pos.data_ptr(), T, k.shape[0], din,
+                                           ratio, topk, out.data_ptr(), stream)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexer_project_score_topk")
         return out
 
     def score_topk_batch(self, q, k, w, pos, ratio: int, topk: int, out=None):

@@ -67,6 +67,27 @@ WORKLOADS = {
 }
 
 
+# query projection ahead of the indexer: the 32k chunk's shape (2048 tokens at
+# 30720..32767, 8192 rows, 64 x 128 heads, top-512) with a query input of
+# d_in features per token and projection weights [H*D][d_in], all Gaussian in
+# bf16: x = N(0,1), wq = N(0,1) / sqrt(128 d_in) (so q ~ N(0,1)/sqrt(128) as in
+# the Gaussian workloads), k = N(0,1)/sqrt(128), w uniform [0,1).  Draw order
+# from default_rng(seed): x, wq, k, w.
+PROJ_WORKLOADS = {"qproj32k": ("prefill32k", 1536, "bf16", 7)}
+
+
+def make_projection(name: str):
+    base, din, dtype, seed = PROJ_WORKLOADS[name]
+    wl = WORKLOADS[base]
+    rng = np.random.default_rng(seed)
+    x = to_bits(rng.standard_normal((wl.T, din)), dtype)
+    wq = to_bits(rng.standard_normal((wl.H * wl.D, din)) / math.sqrt(128.0 * din), dtype)
+    k = to_bits(rng.standard_normal((wl.N, wl.D)) / math.sqrt(128.0), dtype)
+    w = rng.random((wl.T, wl.H), dtype=np.float32)
+    return {"x": x, "wq": wq, "k": k, "w": w, "pos": wl.positions, "wl": wl, "din": din,
+            "dtype": dtype}
+
+
 # batched decode: B sequences, each drawn like the single-token workload with
 # seed + b (sequence b's q, k, w in that order), all at the same position
 DECODE_BATCHES = {"decode1m_b8": ("decode1m", 8)}

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
                                            "ds_indexer_status_str", "ds_indexer_timing",
                                            "ds_indexer_timing_read", "ds_sparse_attention",
                                            "ds_sparse_attention_all",
-                                           "ds_indexer_score_topk_batch"])
+                                           "ds_indexer_score_topk_batch", "ds_indexer_project_q",
+                                           "ds_indexer_project_score_topk"])
 
 
 def test_every_declared_symbol_is_exported(ix):
@@ -60,7 +61,7 @@ def test_header_constants_match_binding(ix):
     for name in ("DS_F16", "DS_BF16", "DS_OK", "DS_ERR_INVALID_ARG", "DS_ERR_UNSUPPORTED",
                  "DS_ERR_CAPACITY", "DS_ERR_HIP", "DS_ERR_OOM", "DS_KERNEL_SCORE",
                  "DS_KERNEL_SELECT", "DS_KERNEL_DECODE_SCORE", "DS_KERNEL_DECODE_SELECT",
-                 "DS_KERNEL_CLASSES"):
+                 "DS_KERNEL_PROJECT", "DS_KERNEL_CLASSES"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert m and int(m.group(1)) == getattr(ix, name), name
 
@@ -88,6 +89,9 @@ def test_create_null_out_pointer(ix):
 def test_calls_on_null_handle(ix):
     assert ix.ds_indexer_score_topk(None, 16, 16, 16, 16, 1, 1, 4, 1, 16, None) == -1
     assert ix.ds_indexer_score_topk_batch(None, 16, 16, 16, 16, 2, 1, 4, 1, 16, None) == -1
+    assert ix.ds_indexer_project_q(None, 16, 16, 1, 64, 16, None) == -1
+    assert ix.ds_indexer_project_score_topk(None, 16, 16, 16, 16, 16, 1, 1, 64, 4, 1, 16,
+                                            None) == -1
     assert ix.ds_indexer_scores(None, 16, 16, 16, 16, 1, 1, 4, 16, None) == -1
     ix.ds_indexer_destroy(None)  # accepted and ignored
     assert ix.ds_indexer_timing(None, 1) == -1

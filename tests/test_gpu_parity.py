@@ -326,6 +326,119 @@ def test_decode1m_batch_full_size(lib, orc):
             check_tolerant(out[b], sc[0], osc[0], n, wl.topk, f"decode1m_b8 sequence {b}")
 
 
+def proj_run(lib, x, wq, H, D, dtype, topk=None, k=None, w=None, pos=None, ratio=4):
+    """ds_indexer_project_q (topk None) or ds_indexer_project_score_topk on host arrays."""
+    T, din = x.shape
+    N = k.shape[0] if k is not None else 1
+    ix = lib.Indexer(H, D, dtype, max(topk or 1, 1), max(T, 1), max(N, 1), device=0)
+    try:
+        tx = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV)
+        tw = torch.from_numpy(np.ascontiguousarray(wq).view(np.int16)).to(DEV)
+        if topk is None:
+            q = ix.project_q(tx, tw)
+            torch.cuda.synchronize(DEV)
+            return q.cpu().numpy().view(np.uint16).reshape(T, H * D)
+        _, tk, tww, tp = dev_inputs(np.zeros((1, H, D), np.uint16), k, w, pos)
+        out = ix.project_score_topk(tx, tw, tk, tww, tp, ratio, topk)
+        torch.cuda.synchronize(DEV)
+        return out.cpu().numpy()
+    finally:
+        ix.close()
+
+
+def ulp_distance(a_bits, b_bits):
+    """Distance in representable steps between two arrays of 16-bit float bits."""
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+@pytest.mark.parametrize("T,din,H,D,dtype", [(37, 64, 4, 32, "f16"), (300, 200, 64, 128, "bf16"),
+                                             (129, 1536, 64, 128, "f16"), (8, 24, 8, 64, "bf16"),
+                                             (256, 1536, 32, 128, "bf16")])
+def test_project_q_against_oracle(lib, orc, T, din, H, D, dtype):
+    """Gaussian operands: the GPU sums in fp32 and rounds once, the oracle sums
+    in double and rounds once.  So each GPU value lies within one step of the
+    storage type plus the fp32 summation bound d_in * 2^-24 * sum_i |x_i w_i| of
+    the exact sum (that bound matters only where the terms cancel), and all but
+    a small fraction of the values are identical to the oracle's.  Integer operands (exact sums):
+    bit-exact."""
+    say(f"projection T={T} d_in={din} O={H * D} {dtype}")
+    rng = np.random.default_rng(T + din)
+    x = synth.to_bits(rng.standard_normal((T, din)), dtype)
+    wq = synth.to_bits(rng.standard_normal((H * D, din)) / np.sqrt(din), dtype)
+    got = proj_run(lib, x, wq, H, D, dtype)
+    want = orc.project_q(x, wq, dtype=dtype, threads=16)
+    d = ulp_distance(got, want)
+    # a rounding decision differs only where the exact sum lies within the fp32
+    # error of a midpoint: rare (about sqrt(d_in) 2^-24 / 2^-11 at most, fp16)
+    assert (d > 0).mean() < 1e-2, f"{(d > 0).mean():.2e} of q not identical"
+
+    def dec(b):
+        b = np.asarray(b, dtype=np.uint16)
+        if dtype == "f16":
+            return b.view(np.float16).astype(np.float64)
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xd, wd = dec(x), dec(wq)
+    exact = xd @ wd.T
+    bound = din * 2.0 ** -24 * (np.abs(xd) @ np.abs(wd).T)
+    step = np.abs(dec(want) - dec(want ^ np.uint16(1)))  # one step of the type at the oracle's value
+    err = np.abs(dec(got) - exact)
+    bad = np.argwhere(err > step + bound)
+    assert bad.size == 0, f"{len(bad)} values beyond one step plus the fp32 bound, e.g. {tuple(bad[0])}"
+    xi = synth.to_bits(rng.integers(-3, 4, size=(T, din)), dtype)
+    wi = synth.to_bits(rng.integers(-2, 3, size=(H * D, din)), dtype)
+    assert np.array_equal(proj_run(lib, xi, wi, H, D, dtype), orc.project_q(xi, wi, dtype=dtype,
+                                                                            threads=16))
+
+
+def test_project_score_topk_integer_exact(lib, orc):
+    """Projection then score + top-k in one call, integer inputs kept small enough
+    that every fp32 sum is exact (|q| <= 128, |q . k| <= 2^16, 64 heads): bit-exact
+    against the oracle's projection then score + top-k.  A pool that fits in top-k
+    skips the projection and the scoring."""
+    say("projection + indexer, integer, bit-exact")
+    rng = np.random.default_rng(12)
+    T, din, H, D, N, topk = 70, 64, 64, 128, 900, 100
+    x = synth.to_bits(rng.integers(-2, 3, size=(T, din)), "f16")
+    wq = synth.to_bits(rng.integers(-1, 2, size=(H * D, din)), "f16")
+    k = synth.to_bits(rng.integers(-4, 5, size=(N, D)), "f16")
+    w = ((rng.integers(0, 2, size=(T, H)) * 2 - 1) * np.ldexp(1.0, -rng.integers(0, 4, size=(T, H)))
+         ).astype(np.float32)
+    pos = rng.integers(-2, 4 * N + 3, size=T).astype(np.int32)
+    got = proj_run(lib, x, wq, H, D, "f16", topk=topk, k=k, w=w, pos=pos)
+    want = orc.project_score_topk(x, wq, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk,
+                                  threads=16)
+    assert np.array_equal(got, want)
+    got = proj_run(lib, x, wq, H, D, "f16", topk=N, k=k, w=w, pos=pos)
+    want = orc.project_score_topk(x, wq, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=N,
+                                  threads=16)
+    assert np.array_equal(got, want)
+
+
+def test_qproj32k_full_size(lib, orc):
+    """The full 32k-chunk projection (2048 x 1536 -> 64 x 128, bf16 Gaussian) fused
+    ahead of the indexer: sampled tokens within score tolerance and tie margin of
+    the oracle's projection then scores; every token's output valid."""
+    say("full-size qproj32k")
+    d = synth.make_projection("qproj32k")
+    wl = d["wl"]
+    out = proj_run(lib, d["x"], d["wq"], wl.H, wl.D, d["dtype"], topk=wl.topk, k=d["k"],
+                   w=d["w"], pos=d["pos"], ratio=wl.ratio)
+    q_gpu = proj_run(lib, d["x"], d["wq"], wl.H, wl.D, d["dtype"]).reshape(wl.T, wl.H, wl.D)
+    _, sc = gpu_run(lib, q_gpu, d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=d["dtype"],
+                    ratio=wl.ratio, topk=wl.topk, scores=True)
+    toks = sample_tokens(wl.T, np.random.default_rng(9), n=24)
+    _, osc = orc.project_score_topk(d["x"], d["wq"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D,
+                                    dtype=d["dtype"], ratio=wl.ratio, topk=wl.topk, tokens=toks,
+                                    want_scores=True, threads=16)
+    n = visible(d["pos"], wl.ratio, wl.N)
+    for i, t in enumerate(toks):
+        check_tolerant(out[t], sc[t], osc[i], int(n[t]), wl.topk, f"qproj32k token {t}")
+    check_all_tokens(out, sc, d["pos"], wl.ratio, wl.N, wl.topk, "qproj32k")
+
+
 def test_decode_fallback_paths_exact(lib, orc):
     """Scores rising with the row concentrate the best rows in the last partitions
     (their short candidate lists cannot be trusted), and all-equal scores make
