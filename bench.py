@@ -720,6 +720,9 @@ def main():
             rf = entry["roofline"]
             entry.update({"value": rf["achieved"], "unit": "GB/s (decode scorer, K from HBM)",
                           "end_to_end_GBps": rf["algorithmic_bytes_per_launch"] / (r["ms_per_step"] * 1e-3) / 1e9})
+        elif "score" not in r["kernels"]:  # whole-call skip: nothing is scored
+            entry.update({"value": r["query_tokens_per_s"],
+                          "unit": "query tokens/s (every row fits: sequential rows, no scoring)"})
         else:
             entry.update({"value": r["pairs_per_s"], "unit": "pairs/s",
                           "query_tokens_per_s": r["query_tokens_per_s"]})
