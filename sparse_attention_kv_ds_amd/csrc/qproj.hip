@@ -6,12 +6,17 @@
 // K-contiguous, wq in the usual [out][in] layout); q [T][O] is written in the
 // same type, which is the [T][H][D] layout the scorer reads.
 //
-// A plain GEMM on the matrix cores: work-group tiles of 128 tokens x 128
-// features, four waves of 64 x 64 (2 x 2 tiles of v_mfma_f32_32x32x16), K in
-// stages of 64 that go straight from memory into LDS (buffer loads with the
-// LDS bit, two stages, 16-byte chunks XOR-swizzled so that the fragment reads
-// are free of bank conflicts), fp32 accumulation, one rounding (to nearest
-// even) at the end, and the tile written through LDS as 16-byte stores.
+// A plain GEMM on the matrix cores.  A work-group of eight waves computes a
+// tile of 256 tokens x 256 features (256 x 128 when O is not a multiple of
+// 256); each wave holds 128 x 64 (or 64 x 64) of it as 32 x 32 accumulator
+// tiles of v_mfma_f32_32x32x16.  Large tiles keep the operand bytes per flop
+// low at both ends: what the work-group pulls from L2 per stage and what each
+// wave reads from LDS per MFMA.  K goes in stages of 64 straight from memory
+// into LDS (buffer loads with the LDS bit, two stages, 16-byte chunks
+// XOR-swizzled so that the fragment reads are free of bank conflicts); within
+// a stage the fragments of the next 16-wide step are read while the MFMAs of
+// the current one run.  fp32 accumulation, one rounding (to nearest even) at
+// the end, and the tile written through LDS as 16-byte row pieces.
 // Work-groups are ordered so that the tiles of one XCD share an eighth of the
 // weight rows, which then stay in that XCD's L2.
 #include "common.hpp"
@@ -21,9 +26,9 @@ namespace dsi {
 
 namespace {
 
-constexpr int kQpTile = 128;   // tokens and features per work-group
-constexpr int kQpStage = 64;   // K elements per stage
-constexpr int kQpWaves = 4;
+constexpr int kQpWaves = 8;
+constexpr int kQpStage = 64; // K elements per stage
+constexpr int kQpTileM = 256; // tokens per work-group (both configurations)
 
 template <int DT>
 __device__ __forceinline__ uint16_t to_storage(float v)
@@ -34,22 +39,32 @@ __device__ __forceinline__ uint16_t to_storage(float v)
         return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-template <int DT>
+// WM x WN waves, each TM x TN accumulator tiles of 32 x 32
+template <int DT, int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(kQpWaves * 64) void qproj_kernel(const uint16_t *__restrict__ x,
                                                              const uint16_t *__restrict__ wq,
                                                              int T, int K, int O,
                                                              uint16_t *__restrict__ q)
 {
-    constexpr int CPR = kQpStage / 8;                 // 16-byte chunks per staged row
-    constexpr int TILE_B = kQpTile * kQpStage * 2;    // bytes of one operand's stage
-    constexpr int LPW = TILE_B / 1024 / kQpWaves;     // 1 KiB loads per wave and operand
-    constexpr int KS = kQpStage / 16;                 // MFMA steps per stage
-    // separate arrays per stage and operand, so that the compiler can tell that
-    // the loads into one do not touch the fragment reads of another
-    __shared__ __attribute__((aligned(1024))) unsigned char sa0[TILE_B];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb0[TILE_B];
-    __shared__ __attribute__((aligned(1024))) unsigned char sa1[TILE_B];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb1[TILE_B];
+    constexpr int TILEM = WM * TM * 32, TILEN = WN * TN * 32;
+    static_assert(WM * WN == kQpWaves && TILEM == kQpTileM, "tile shape");
+    constexpr int CPR = kQpStage / 8;            // 16-byte chunks per staged row
+    constexpr int A_B = TILEM * kQpStage * 2;    // bytes of one stage of x rows
+    constexpr int B_B = TILEN * kQpStage * 2;    // ... of wq rows
+    constexpr int LA = A_B / 1024 / kQpWaves;    // 1 KiB loads per wave and stage
+    constexpr int LB = B_B / 1024 / kQpWaves;
+    constexpr int KS = kQpStage / 16;            // MFMA steps per stage
+    constexpr int ROW_B = 32 * CPR * 16;         // bytes of 32 staged rows
+    constexpr int SW = TN * 32;                  // width of a wave's output strip
+    constexpr int EPW = A_B / (16 * SW * 2);     // output strips per x stage
+    static_assert(LA >= 1 && LB >= 1 && LA + LB < 64, "stage loads split over the waves");
+    static_assert(kQpWaves <= 2 * EPW, "output strips fit the two x stages");
+    // one array per stage and operand, so that the compiler can tell that the
+    // loads into one do not touch the fragment reads of another
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char sa1[A_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb1[B_B];
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -58,7 +73,7 @@ __global__ __launch_bounds__(kQpWaves * 64) void qproj_kernel(const uint16_t *__
 
     // tile of this work-group: consecutive work-groups go to different XCDs,
     // so XCD x = id % 8 takes the feature blocks of its eighth of the weights
-    const int nbm = (T + kQpTile - 1) / kQpTile, nbn = O / kQpTile;
+    const int nbm = (T + TILEM - 1) / TILEM, nbn = O / TILEN;
     const int id = blockIdx.x;
     int bm, bn;
     if (nbn % 8 == 0) {
@@ -71,121 +86,162 @@ __global__ __launch_bounds__(kQpWaves * 64) void qproj_kernel(const uint16_t *__
     }
     if (bm >= nbm)
         return; // (never: the grid is nbm * nbn work-groups)
-    const int m0 = bm * kQpTile, n0 = bn * kQpTile;
+    const int m0 = bm * TILEM, n0 = bn * TILEN;
 
-    // stage loads: load i of this wave fills 16-byte slots [64 (wave*LPW+i), +64)
-    // of each operand's stage, lane by lane; the lane fetches the chunk that
+    // stage loads: load i of this wave fills 16-byte slots [64 (wave*L+i), +64)
+    // of an operand's stage, lane by lane; the lane fetches the chunk that
     // belongs in its slot; chunks past K and rows past T read as 0
     const auto rx = make_rsrc(x, (uint32_t)T * K * 2);
     const auto rw = make_rsrc(wq, (uint32_t)O * K * 2);
-    uint32_t xoff[LPW], woff[LPW];
-    int kch[LPW]; // first element of the lane's chunk within the stage
+    uint32_t xoff[LA], woff[LB];
+    int xch[LA], wch[LB]; // first element of the lane's chunk within the stage
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int s = (wave * LPW + i) * 64 + lane;
-        const int r = s / CPR;
-        const int c = (s % CPR) ^ ((r / (16 / CPR)) % CPR);
-        kch[i] = c * 8;
+    for (int i = 0; i < LA; ++i) {
+        const int sl = (wave * LA + i) * 64 + lane;
+        const int r = sl / CPR;
+        const int c = (sl % CPR) ^ ((r / (16 / CPR)) % CPR);
+        xch[i] = c * 8;
         xoff[i] = ((uint32_t)(m0 + r) * K + c * 8) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int sl = (wave * LB + i) * 64 + lane;
+        const int r = sl / CPR;
+        const int c = (sl % CPR) ^ ((r / (16 / CPR)) % CPR);
+        wch[i] = c * 8;
         woff[i] = ((uint32_t)(n0 + r) * K + c * 8) * 2;
     }
     auto load_stage = [&](int k0, unsigned char *sa, unsigned char *sb) {
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const bool in = k0 + kch[i] < K;
-            buf_load16_lds(rx, sa + (wave * LPW + i) * 1024, in ? xoff[i] + k0 * 2 : kOffNone);
-            buf_load16_lds(rw, sb + (wave * LPW + i) * 1024, in ? woff[i] + k0 * 2 : kOffNone);
-        }
+        for (int i = 0; i < LA; ++i)
+            buf_load16_lds(rx, sa + (wave * LA + i) * 1024,
+                           k0 + xch[i] < K ? xoff[i] + k0 * 2 : kOffNone);
+#pragma unroll
+        for (int i = 0; i < LB; ++i)
+            buf_load16_lds(rw, sb + (wave * LB + i) * 1024,
+                           k0 + wch[i] < K ? woff[i] + k0 * 2 : kOffNone);
     };
 
-    // fragment offsets: this wave's 64 x 64 sub-tile is rows wm*64.. of x,
-    // rows wn*64.. of wq; fragment (t, kk) is row t*32 + col, chunk 2 kk + hf
-    const int wm = wave >> 1, wn = wave & 1;
-    uint32_t aoff[2][KS], boff[2][KS];
+    // fragment (t, kk) of this wave: staged row base + t * 32 + col, chunk
+    // 2 kk + hf.  The swizzle depends on the row modulo 32 only, so t adds
+    // the constant t * ROW_B.
+    const int wm = wave / WN, wn = wave % WN;
+    uint32_t ak[KS], bk[KS];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            aoff[t][kk] = (uint32_t)stage_slot<CPR>(wm * 64 + t * 32 + col, 2 * kk + hf) * 16;
-            boff[t][kk] = (uint32_t)stage_slot<CPR>(wn * 64 + t * 32 + col, 2 * kk + hf) * 16;
-        }
+    for (int kk = 0; kk < KS; ++kk) {
+        ak[kk] = (uint32_t)stage_slot<CPR>(wm * TM * 32 + col, 2 * kk + hf) * 16;
+        bk[kk] = (uint32_t)stage_slot<CPR>(wn * TN * 32 + col, 2 * kk + hf) * 16;
+    }
 
-    f32x16 acc[2][2];
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < TM; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < TN; ++nt)
             acc[mt][nt] = f32x16{};
+    // the fragments of step kk + 1 are read before the MFMAs of step kk
     auto compute = [&](const unsigned char *sa, const unsigned char *sb) {
+        u32x4 a[2][TM], b[2][TN];
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            a[0][t] = *reinterpret_cast<const u32x4 *>(sa + ak[0] + t * ROW_B);
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            b[0][t] = *reinterpret_cast<const u32x4 *>(sb + bk[0] + t * ROW_B);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            u32x4 a[2], b[2];
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < KS) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                a[t] = *reinterpret_cast<const u32x4 *>(sa + aoff[t][kk]);
-                b[t] = *reinterpret_cast<const u32x4 *>(sb + boff[t][kk]);
+                for (int t = 0; t < TM; ++t)
+                    a[nxt][t] = *reinterpret_cast<const u32x4 *>(sa + ak[kk + 1] + t * ROW_B);
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    b[nxt][t] = *reinterpret_cast<const u32x4 *>(sb + bk[kk + 1] + t * ROW_B);
             }
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < TM; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt] = mfma32<DT>(a[mt], b[nt], acc[mt][nt]);
+                for (int nt = 0; nt < TN; ++nt)
+                    acc[mt][nt] = mfma32<DT>(a[cur][mt], b[cur][nt], acc[mt][nt]);
         }
     };
 
+    // stage s sits in buffer s % 2; stage s + 1 is loaded while stage s is
+    // computed, then each wave waits for its own loads and the barrier
+    // publishes every wave's (and frees buffer s % 2 for stage s + 2)
     const int nst = (K + kQpStage - 1) / kQpStage;
     load_stage(0, sa0, sb0);
     wait_vmcnt<0>();
     __syncthreads();
-    // two stages per iteration, so that every LDS offset is a constant
-    for (int s = 0;;) {
+    for (int s = 0;; s += 2) {
         if (s + 1 < nst)
             load_stage((s + 1) * kQpStage, sa1, sb1);
         compute(sa0, sb0);
+        if (s + 1 >= nst)
+            break;
         wait_vmcnt<0>();
         lds_barrier();
-        if (++s >= nst)
-            break;
-        if (s + 1 < nst)
-            load_stage((s + 1) * kQpStage, sa0, sb0);
+        if (s + 2 < nst)
+            load_stage((s + 2) * kQpStage, sa0, sb0);
         compute(sa1, sb1);
+        if (s + 2 >= nst)
+            break;
         wait_vmcnt<0>();
         lds_barrier();
-        if (++s >= nst)
-            break;
     }
+    __syncthreads(); // every wave is done with the stages
 
-    // round and write: each wave's 64 x 64 sub-tile goes row-major into LDS
-    // (waves 0, 1 in the first stage's x array, 2, 3 in its wq array), then out
-    // as 16-byte rows pieces
-    uint16_t *tile = reinterpret_cast<uint16_t *>((wave < 2 ? sa0 : sb0) + (wave & 1) * 8192);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                tile[(mt * 32 + acc_row(i, lane)) * 64 + nt * 32 + col] =
-                    to_storage<DT>(acc[mt][nt][i]);
-    wave_lds_sync();
+    // round and write, per 16-row half of each 32-row strip of the wave's
+    // tile: rows into a wave-private LDS region (16 x SW), then out as
+    // 16-byte row pieces.  Accumulator entries i = 0..7 hold rows 0..15 of
+    // the 32 x 32 tile, i = 8..15 rows 16..31.
+    uint16_t *strip = reinterpret_cast<uint16_t *>(wave < EPW ? sa0 : sa1) + (wave % EPW) * 16 * SW;
     const auto rq = make_rsrc(q, (uint32_t)T * O * 2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int c = e * 64 + lane; // 16-byte piece: row c / 8, columns 8 (c % 8) ..
-        const int r = c >> 3, cc = (c & 7) * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + r * 64 + cc);
-        const int row = m0 + wm * 64 + r;
-        const uint32_t off =
-            row < T ? ((uint32_t)row * O + n0 + wn * 64 + cc) * 2 : kOffNone;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rq, off, 0, 0);
+    for (int mt = 0; mt < TM; ++mt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int nt = 0; nt < TN; ++nt)
+#pragma unroll
+                for (int i = 8 * h; i < 8 * h + 8; ++i)
+                    strip[(acc_row(i, lane) - 16 * h) * SW + nt * 32 + col] =
+                        to_storage<DT>(acc[mt][nt][i]);
+            wave_lds_sync();
+#pragma unroll
+            for (int e = 0; e < TN; ++e) {
+                const int c = e * 64 + lane; // piece: row c / (4 TN), columns 8 (c % 4 TN) ..
+                const int r = c / (4 * TN), cc = (c % (4 * TN)) * 8;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(strip + r * SW + cc);
+                const int row = m0 + wm * TM * 32 + mt * 32 + 16 * h + r;
+                const uint32_t off =
+                    row < T ? ((uint32_t)row * O + n0 + wn * SW + cc) * 2 : kOffNone;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rq, off, 0, 0);
+            }
+            wave_lds_sync();
+        }
     }
+}
+
+template <int DT>
+hipError_t launch_qproj_dt(const uint16_t *x, const uint16_t *wq, int T, int K, int O, uint16_t *q,
+                           hipStream_t st, Timing *tm)
+{
+    const int nbm = (T + kQpTileM - 1) / kQpTileM;
+    if (O % 256 == 0) // 2 x 4 waves of 128 x 64
+        return launch_kernel(qproj_kernel<DT, 2, 4, 4, 2>, dim3(nbm * (O / 256)),
+                             dim3(kQpWaves * 64), 0, st, tm, true, true, x, wq, T, K, O, q);
+    // 4 x 2 waves of 64 x 64
+    return launch_kernel(qproj_kernel<DT, 4, 2, 2, 2>, dim3(nbm * (O / 128)), dim3(kQpWaves * 64),
+                         0, st, tm, true, true, x, wq, T, K, O, q);
 }
 
 } // namespace
 
 bool qproj_supported(int K, int O, int dtype)
 {
-    return K >= 8 && K % 8 == 0 && O % kQpTile == 0 && (dtype == kF16 || dtype == kBF16);
+    return K >= 8 && K % 8 == 0 && O % 128 == 0 && (dtype == kF16 || dtype == kBF16);
 }
 
 hipError_t launch_qproj(const void *x, const void *wq, int T, int K, int O, int dtype, void *q,
@@ -193,15 +249,12 @@ hipError_t launch_qproj(const void *x, const void *wq, int T, int K, int O, int 
 {
     if (T <= 0)
         return hipSuccess;
-    const int blocks = (T + kQpTile - 1) / kQpTile * (O / kQpTile);
     const auto *xs = static_cast<const uint16_t *>(x);
     const auto *ws = static_cast<const uint16_t *>(wq);
     auto *qs = static_cast<uint16_t *>(q);
     if (dtype == kF16)
-        return launch_kernel(qproj_kernel<kF16>, dim3(blocks), dim3(kQpWaves * 64), 0, st, tm, true,
-                             true, xs, ws, T, K, O, qs);
-    return launch_kernel(qproj_kernel<kBF16>, dim3(blocks), dim3(kQpWaves * 64), 0, st, tm, true,
-                         true, xs, ws, T, K, O, qs);
+        return launch_qproj_dt<kF16>(xs, ws, T, K, O, qs, st, tm);
+    return launch_qproj_dt<kBF16>(xs, ws, T, K, O, qs, st, tm);
 }
 
 } // namespace dsi
