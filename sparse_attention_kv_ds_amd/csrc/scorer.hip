@@ -434,13 +434,80 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     // The work-group's rows are one selection partition: list its kp best keys
     // in row order (all its rows when they are <= kp, key 0 in unused slots),
     // their number in pcount and the smallest listed key in pmin (0 when the
-    // list holds every row).  The scores go through LDS (each wave's first
-    // slot: its loads have all landed and been read) to one wave, which
-    // selects without barriers.  (Taking the best keys by rounds of wave
-    // maxima instead of the threshold search measured slower.)
+    // list holds every row).
     constexpr int ROWS = WAVES * NB * 32;
-    constexpr int E = ROWS / 64; // keys per lane
     static_assert(ROWS == kDecodePart, "a decode work-group covers one selection partition");
+    const int rows = min(ROWS, n - r0);
+    uint64_t *list = cand + (size_t)blockIdx.x * kp;
+    if (kp <= 8) {
+        // Small lists (many partitions): each wave first keeps the best kp of
+        // its own NB * 32 rows (the partition's best kp are among them), by
+        // ranking, in parallel and without a barrier; then one wave ranks the
+        // WAVES * kp survivors.  The survivors go through each wave's first
+        // slot (its loads have all landed and been read), the ranking scratch
+        // is its second.
+        static_assert(WAVES * 8 <= 64, "one survivor per lane");
+        uint32_t hi[NB], lo[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int row = wrow + b * 32 + col; // lanes 32..63 hold the same scores: no key
+            const uint64_t key = hf == 0 && row < n ? make_key(scb[b], (uint32_t)row) : 0ull;
+            hi[b] = (uint32_t)(key >> 32);
+            lo[b] = (uint32_t)key;
+        }
+        const int nv = min(max(n - wrow, 0), NB * 32); // rows of this wave
+        uint64_t tw = 1ull;
+        if (nv > kp) // (then more than kp lanes hold a key)
+            tw = wave_kth_small<NB, 32>(hi, lo, kp,
+                                        reinterpret_cast<uint64_t *>(kst1 + wave * BLK_B));
+        uint64_t *wl = reinterpret_cast<uint64_t *>(kst0 + wave * BLK_B);
+        int c = 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint64_t key = ((uint64_t)hi[b] << 32) | lo[b];
+            const bool keep = key >= tw; // (tw >= 1: no empty slot)
+            const uint64_t m = ballot(keep);
+            if (keep)
+                wl[c + mbcnt(m)] = key;
+            c += popc(m);
+        }
+        if (lane >= c && lane < 8)
+            wl[lane] = 0ull;
+        __syncthreads();
+        if (wave != 0)
+            return;
+        // survivor j = entry j % 8 of wave j / 8's list, in row order
+        const uint64_t x =
+            lane < WAVES * 8 ? reinterpret_cast<const uint64_t *>(kst0 + (lane >> 3) * BLK_B)[lane & 7]
+                             : 0ull;
+        uint64_t t = 1ull;
+        if (rows > kp) {
+            // more than kp rows: the survivors hold at least kp keys, so
+            // exactly one has kp - 1 larger ones
+            int r = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w)
+                r += rank_among(reinterpret_cast<const uint64_t *>(kst0 + w * BLK_B), 8, x);
+            t = readlane64(x, (int)__builtin_ctzll(ballot(x != 0ull && r == kp - 1)));
+        }
+        const bool keep = x != 0ull && x >= t;
+        const uint64_t m = ballot(keep);
+        if (keep)
+            list[mbcnt(m)] = x;
+        const int nc = popc(m);
+        if (lane >= nc && lane < kp)
+            list[lane] = 0ull;
+        if (lane == 0) {
+            pcount[blockIdx.x] = nc;
+            pmin[blockIdx.x] = rows > kp ? t : 0ull;
+        }
+        return;
+    }
+
+    // Longer lists: the scores go through LDS (each wave's first slot) to one
+    // wave, which finds the kp-th best key by the threshold search.  (Taking
+    // the best keys by rounds of wave maxima measured slower.)
+    constexpr int E = ROWS / 64; // keys per lane
     float *const mine = reinterpret_cast<float *>(kst0 + wave * BLK_B);
     if (hf == 0) {
 #pragma unroll
@@ -450,7 +517,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     __syncthreads();
     if (wave != 0)
         return;
-    const int rows = min(ROWS, n - r0);
     uint32_t hi[E], lo[E];
 #pragma unroll
     for (int s = 0; s < E; ++s) {
@@ -465,7 +531,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
         WaveReduce red;
         t = select_bound<E>(hi, lo, E, rows, kp, 0, red); // the kp-th best key
     }
-    uint64_t *list = cand + (size_t)blockIdx.x * kp;
     int nc = 0;
 #pragma unroll
     for (int s = 0; s < E; ++s) {

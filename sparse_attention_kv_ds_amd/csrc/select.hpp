@@ -453,6 +453,68 @@ struct WaveSelect {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Small k on one wave, without a search loop.  The k-th largest (k * E <= 64)
+// of the keys a wave holds in hi/lo (E per lane, key 0 in empty slots; keys
+// only in lanes below LANES; at least k lanes hold a key).  With L the k-th
+// largest of the lane maxima,
+// at least k keys are >= L, so the answer is >= L; and keys >= L sit only in
+// the k lanes whose maximum is >= L, so there are at most k * E of them.  Both
+// steps rank at most 64 keys, one per lane, by counting the larger ones among
+// all of them (read back from LDS as broadcasts): a fixed number of compares,
+// where a bisection would take one dependent count step per score bit.
+// scratch: 128 keys of LDS private to the wave.
+// ---------------------------------------------------------------------------
+// #{keys greater than x among arr[0 .. cnt)} (cnt <= 64, uniform; arr holds 64 keys)
+__device__ __forceinline__ int rank_among(const uint64_t *arr, int cnt, uint64_t x)
+{
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < cnt; j += 2) {
+        const uint64_t a = arr[j], b = arr[j + 1]; // (arr[j + 1] may be stale when j + 1 == cnt)
+        r += (a > x) + (j + 1 < cnt && b > x);
+    }
+    return r;
+}
+
+template <int E, int LANES = 64>
+__device__ __forceinline__ uint64_t wave_kth_small(const uint32_t (&hi)[E], const uint32_t (&lo)[E],
+                                                   int k, uint64_t *scratch)
+{
+    static_assert(E <= 64 && LANES % 2 == 0 && LANES <= 64, "keys per lane, lanes");
+    const int lane = threadIdx.x & 63;
+    uint64_t key[E];
+    uint64_t m = 0;
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+        key[s] = ((uint64_t)hi[s] << 32) | lo[s];
+        m = key[s] > m ? key[s] : m;
+    }
+    scratch[lane] = m;
+    wave_lds_sync();
+    // the lane maxima that are keys are distinct, and more than k - 1 of them
+    // are nonzero, so exactly one lane has k - 1 larger maxima
+    const int r1 = rank_among(scratch, LANES, m);
+    const uint64_t L = readlane64(m, (int)__builtin_ctzll(ballot(lane < LANES && r1 == k - 1)));
+    // the keys >= L (L >= 1: no empty slot), in slot-then-lane order
+    uint64_t *cs = scratch + 64;
+    int c = 0;
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+        const bool in = key[s] >= L;
+        const uint64_t b = ballot(in);
+        if (in)
+            cs[c + mbcnt(b)] = key[s];
+        c += popc(b);
+    }
+    wave_lds_sync();
+    const uint64_t x = lane < c ? cs[lane] : 0ull;
+    const int r2 = rank_among(cs, c, x);
+    const uint64_t t = readlane64(x, (int)__builtin_ctzll(ballot(lane < c && r2 == k - 1)));
+    wave_lds_sync(); // (the scratch may be reused after return)
+    return t;
+}
+
 __device__ __forceinline__ int block_exclusive_scan(int c, int *scan)
 {
     const int lane = threadIdx.x & 63, wave = wave_id();

@@ -144,6 +144,99 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
 // Union element e sits in slot e / NT of thread e % NT: every load reads
 // consecutive keys, and element order is row order.  kp is a power of two.
 // ---------------------------------------------------------------------------
+// The k-th largest key of the union (MS keys per thread, hi == 0: no key;
+// at least k keys) through one histogram of the scores instead of a bisection
+// with a barrier per bit: kHistBins bins spread over [min, max] of the high
+// words (bin = a monotone function of the score, so higher bins hold larger
+// keys), counted with LDS adds; one wave finds the bin that holds the k-th key
+// and how many keys lie above it; the keys of that bin (at most 64 of them)
+// are ranked one per lane.  Returns 0 when that bin holds more than 64 keys
+// (many equal or near-equal scores): the caller then bisects.
+constexpr int kHistBins = 2048;
+
+template <int MS, int NW>
+__device__ __forceinline__ uint64_t union_kth_hist(const uint32_t (&hi)[MS], const uint32_t (&lo)[MS], int k,
+                                   BlockReduce<NW> &br, uint32_t *hist, uint64_t *bc, int *info)
+{
+    constexpr int NT = NW * 64;
+    constexpr int BPL = kHistBins / 64; // bins per lane of the scanning wave
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    for (int i = tid; i < kHistBins; i += NT)
+        hist[i] = 0u;
+    if (tid == 0)
+        info[3] = 0; // keys collected from the boundary bin
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+        if (hi[s] != 0u) {
+            mn = min(mn, hi[s]);
+            mx = max(mx, hi[s]);
+        }
+    br.minmax(mn, mx); // (its barrier also orders the clearing before the adds)
+    if (mn >= mx)
+        return 0ull;
+    const float scale = (float)kHistBins / ((float)(mx - mn) + 1.0f);
+    auto bin = [&](uint32_t h) { return min(kHistBins - 1, (int)((float)(h - mn) * scale)); };
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+        if (hi[s] != 0u)
+            atomicAdd(&hist[bin(hi[s])], 1u);
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t cnt[BPL];
+        uint32_t sum = 0;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            cnt[b] = hist[lane * BPL + b];
+            sum += cnt[b];
+        }
+        // inc = keys in the bins of this lane and all higher lanes
+        uint32_t inc = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_down(inc, o);
+            if (lane + o < 64)
+                inc += y;
+        }
+        const uint32_t above_lane = inc - sum;
+        if (above_lane < (uint32_t)k && (uint32_t)k <= inc) { // exactly one lane
+            uint32_t above = above_lane;
+            bool found = false;
+#pragma unroll
+            for (int b = BPL - 1; b >= 0; --b) {
+                if (!found && above + cnt[b] >= (uint32_t)k) {
+                    info[0] = lane * BPL + b;
+                    info[1] = (int)above;
+                    info[2] = (int)cnt[b];
+                    found = true;
+                }
+                above += found ? 0u : cnt[b];
+            }
+        }
+    }
+    __syncthreads();
+    const int bb = info[0], above = info[1], cb = info[2];
+    if (cb > 64)
+        return 0ull; // (same in every thread)
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+        if (hi[s] != 0u && bin(hi[s]) == bb)
+            bc[atomicAdd(&info[3], 1)] = ((uint64_t)hi[s] << 32) | lo[s];
+    __syncthreads();
+    if (wave == 0) {
+        // the boundary bin's keys in any order; the answer has k - above - 1
+        // larger ones among them
+        const uint64_t x = lane < cb ? bc[lane] : 0ull;
+        const int r = rank_among(bc, cb, x);
+        const uint64_t hit = ballot(lane < cb && r == k - above - 1);
+        const uint64_t t = readlane64(x, (int)__builtin_ctzll(hit));
+        if (lane == 0)
+            bc[64] = t;
+    }
+    __syncthreads();
+    return bc[64];
+}
+
 template <int MAXS, int MS, int NT>
 __global__ __launch_bounds__(NT) void decode_merge_kernel(
     const float *__restrict__ S, const int32_t *__restrict__ pos, int N, int ratio, int topk,
@@ -165,6 +258,9 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     extern __shared__ uint64_t fb_buf[];
     __shared__ int red[BlockReduce<NW>::kWords];
     __shared__ int tab[MS][NW]; // kept keys per slot and wave
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint64_t bcand[65];
+    __shared__ int hinfo[4];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = wave_id();
@@ -207,7 +303,10 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     bool fallback = total < topk;
     uint64_t tU = 0;
     if (!fallback) {
-        tU = select_bound<MS>(hi, lo, MS, total, topk, 0, br); // the k-th key of the union
+        // the k-th key of the union
+        tU = union_kth_hist<MS, NW>(hi, lo, topk, br, hist, bcand, hinfo);
+        if (tU == 0ull)
+            tU = select_bound<MS>(hi, lo, MS, total, topk, 0, br);
         bool fail = false;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {

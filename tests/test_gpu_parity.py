@@ -440,11 +440,14 @@ def test_qproj32k_full_size(lib, orc):
     check_all_tokens(out, sc, d["pos"], wl.ratio, wl.N, wl.topk, "qproj32k")
 
 
-def test_decode_fallback_paths_exact(lib, orc):
+@pytest.mark.parametrize("N", [40000, 70000])
+def test_decode_fallback_paths_exact(lib, orc, N):
     """Scores rising with the row concentrate the best rows in the last partitions
     (their short candidate lists cannot be trusted), and all-equal scores make
-    every partition's list a pure tie-break; both must stay exact."""
-    N, D, H = 40000, 128, 64
+    every partition's list a pure tie-break; both must stay exact.  At 40000 rows
+    the partitions list 16 keys each (selected by the threshold search), at 70000
+    rows 8 (selected by ranking)."""
+    D, H = 128, 64
     rng = np.random.default_rng(3)
     kf = np.zeros((N, D))
     kf[:, 0] = np.floor(np.arange(N) / 40)  # non-decreasing, exact in fp16 up to 2048
@@ -455,10 +458,10 @@ def test_decode_fallback_paths_exact(lib, orc):
     w = np.ones((1, H), np.float32)
     q = synth.to_bits(qf, "f16")
     for topk in (512, 100):
-        say(f"decode rising scores k={topk}")
+        say(f"decode rising scores N={N} k={topk}")
         exact_case(lib, orc, q, k, w, np.array([4 * N - 1], np.int32), H=H, D=D, dtype="f16",
                    ratio=4, topk=topk, where="decode rising")
-    say("decode all ties")
+    say(f"decode all ties N={N}")
     exact_case(lib, orc, np.zeros_like(q), k, w, np.array([4 * N - 1], np.int32), H=H, D=D,
                dtype="f16", ratio=4, topk=512, where="decode ties")
 
