@@ -64,6 +64,7 @@ KERNEL_SOURCES = {  # kernel class -> sources whose change invalidates stored co
     "decode_score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp",
                      "sparse_attention_kv_ds_amd/csrc/select.hpp"],
     "attention": ["sparse_attention_kv_ds_amd/csrc/attention.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
+    "project": ["sparse_attention_kv_ds_amd/csrc/qproj.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -211,7 +212,8 @@ def time_projection(name: str, steps: int, warmup: int):
             "ms_per_step_with_markers": ms_marked, "kernels_ms": kernels,
             "value": wl.T / (ms * 1e-3), "unit": "query tokens/s (projection + score + top-k)",
             "roofline": {"bound": "mfma", "kernel": "qproj", "achieved": ach, "peak": peak,
-                         "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                         "unit": "TFLOP/s", "frac": ach / peak,
+                         "traffic": stored_traffic("project", name),
                          "algorithmic_flops_per_launch": flops}}
 
 
@@ -268,7 +270,8 @@ def time_decode_batch(name: str, steps: int, warmup: int):
             "sequences_per_s": B / (ms * 1e-3),
             "roofline": {"bound": "hbm", "kernel": "decode_scorer (batched)", "achieved": ach,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                         "traffic": None, "algorithmic_bytes_per_launch": algo}}
+                         "traffic": stored_traffic("decode_score", name),
+                         "algorithmic_bytes_per_launch": algo}}
 
 
 def time_attention(name: str, steps: int, warmup: int):
@@ -557,7 +560,9 @@ def _pmc_table(directory: str):
 DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
             "prefill32k": ("score", "prefill_scorer_kernel"),
             "prefill64k": ("score", "prefill_scorer_kernel"),
-            "attn32k": ("attention", "sparse_attention_kernel")}
+            "attn32k": ("attention", "sparse_attention_kernel"),
+            "decode1m_b8": ("decode_score", "decode_scorer_kernel"),
+            "qproj32k": ("project", "qproj_kernel")}
 
 
 def record_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch: str, copy_write: str):
