@@ -571,3 +571,23 @@ def test_sampled_threshold_restart(lib, orc):
         pos = np.array([N - 1, N - 2, N + 5], dtype=np.int32)
         exact_case(lib, orc, synth.to_bits(q, "f16"), synth.to_bits(k, "f16"), w, pos, H=H, D=D,
                    dtype="f16", ratio=ratio, topk=topk, where=f"restart N={N}")
+
+
+def test_long_rows_with_a_top_run_bit_exact(lib, orc):
+    """Long rows (7168..16384) whose first 64 rows -- the first run of the
+    starting-threshold sample, one row per lane -- carry the top score and the
+    rest three lower levels: the sample overweights the top, and the row has
+    thousands of equal scores at each lower level, so the selection is a pure
+    tie-break by row below the top 64.  Bit-exact against the oracle."""
+    H, D, topk, ratio = 4, 32, 512, 1
+    for N in (7168, 8192, 16384):
+        say(f"long rows with a top run N={N}")
+        k = np.zeros((N, D), dtype=np.float64)
+        j = np.arange(N)
+        k[:, 0] = np.where(j < 64, 4, j % 3)
+        q = np.zeros((3, H, D), dtype=np.float64)
+        q[:, :, 0] = 1
+        w = np.ones((3, H), dtype=np.float32)
+        pos = np.array([N - 1, N - 7, N + 5], dtype=np.int32)
+        exact_case(lib, orc, synth.to_bits(q, "f16"), synth.to_bits(k, "f16"), w, pos, H=H, D=D,
+                   dtype="f16", ratio=ratio, topk=topk, where=f"top run N={N}")
