@@ -320,29 +320,43 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     }
     if (!fallback) {
         // output position of a kept key: kept keys of earlier slots, then of
-        // earlier waves in its slot, then of lower lanes
+        // earlier waves in its slot, then of lower lanes.  Lane s of each wave
+        // handles slot s's counts (one LDS write per wave, one read of the
+        // four waves' counts, a scan across the slots), then every lane takes
+        // its slots' bases from those lanes.
+        static_assert(MS <= 64, "one slot per lane");
         uint64_t m[MS];
+        int cnt = 0; // lane s: this wave's kept keys in slot s
 #pragma unroll
         for (int s = 0; s < MS; ++s) {
             m[s] = ballot(hi[s] != 0u && (((uint64_t)hi[s] << 32) | lo[s]) >= tU);
-            if (lane == 0)
-                tab[s][wave] = popc(m[s]);
+            cnt = lane == s ? popc(m[s]) : cnt;
         }
+        if (lane < MS)
+            tab[lane][wave] = cnt;
         lds_barrier();
-        int base = 0;
-#pragma unroll
-        for (int s = 0; s < MS; ++s) {
-            int before = 0, all = 0;
+        int all = 0, before = 0;
+        if (lane < MS) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const int c = tab[s][w];
-                before += w < wave ? c : 0;
+                const int c = tab[lane][w];
                 all += c;
+                before += w < wave ? c : 0;
             }
-            if ((m[s] >> lane) & 1)
-                out[base + before + mbcnt(m[s])] = key_row(((uint64_t)hi[s] << 32) | lo[s]);
-            base += all;
         }
+        int inc = all; // kept keys of slots 0..lane, all waves
+#pragma unroll
+        for (int o = 1; o < MS; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o)
+                inc += y;
+        }
+        const int base = inc - all + before; // lane s: first position of slot s in this wave
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+            if ((m[s] >> lane) & 1)
+                out[__builtin_amdgcn_readlane(base, s) + mbcnt(m[s])] =
+                    key_row(((uint64_t)hi[s] << 32) | lo[s]);
         return;
     }
     // exact fallback: one wave re-streams every partition in row order, the
