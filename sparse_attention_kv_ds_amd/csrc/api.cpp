@@ -195,12 +195,13 @@ int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, i
              hipMalloc((void **)&ix->pmin, sizeof(uint64_t) * dsi::kDecodeMaxParts * nb) == hipSuccess;
     }
     if (!ok) {
-        (void)hipGetLastError();
-        hipFree(ix->S);
-        hipFree(ix->qbuf);
-        hipFree(ix->cand);
-        hipFree(ix->pcount);
-        hipFree(ix->pmin);
+        // (freeing what was allocated; hipFree(nullptr) is a no-op)
+        (void)hipFree(ix->S);
+        (void)hipFree(ix->qbuf);
+        (void)hipFree(ix->cand);
+        (void)hipFree(ix->pcount);
+        (void)hipFree(ix->pmin);
+        (void)hipGetLastError(); // clear the failed allocation's status
         delete ix;
         return DS_ERR_OOM;
     }
@@ -441,11 +442,11 @@ void ds_indexer_destroy(ds_indexer *ix)
         }
         for (hipEvent_t e : ix->spare)
             (void)hipEventDestroy(e);
-        hipFree(ix->S);
-        hipFree(ix->qbuf);
-        hipFree(ix->cand);
-        hipFree(ix->pcount);
-        hipFree(ix->pmin);
+        (void)hipFree(ix->S);
+        (void)hipFree(ix->qbuf);
+        (void)hipFree(ix->cand);
+        (void)hipFree(ix->pcount);
+        (void)hipFree(ix->pmin);
     }
     delete ix;
 }
