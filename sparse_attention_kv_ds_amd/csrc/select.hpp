@@ -100,17 +100,20 @@ template <int E>
 __device__ __forceinline__ int count_hi_ge(const uint32_t (&hi)[E], int nsl, uint32_t c)
 {
     int r = 0;
+    // (a guard rather than a break, so that the loop always unrolls and hi[]
+    // is only ever indexed by constants)
 #pragma unroll
     for (int s = 0; s < E; s += 4) {
-        if (s >= nsl)
-            break;
-        if (s + 4 <= E) {
-            uint64_t m0, m1, m2, m3;
-            ge_masks4(hi[s], hi[s + 1], hi[s + 2], hi[s + 3], c, m0, m1, m2, m3);
-            r += popc(m0) + popc(m1) + popc(m2) + popc(m3);
-        } else {
-            for (int t = s; t < E; ++t)
-                r += popc(ballot(hi[t] >= c));
+        if (s < nsl) {
+            if (s + 4 <= E) {
+                uint64_t m0, m1, m2, m3;
+                ge_masks4(hi[s], hi[s + 1], hi[s + 2], hi[s + 3], c, m0, m1, m2, m3);
+                r += popc(m0) + popc(m1) + popc(m2) + popc(m3);
+            } else {
+#pragma unroll
+                for (int t = s; t < E; ++t)
+                    r += popc(ballot(hi[t] >= c));
+            }
         }
     }
     return r;
