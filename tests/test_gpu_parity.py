@@ -591,3 +591,30 @@ def test_long_rows_with_a_top_run_bit_exact(lib, orc):
         pos = np.array([N - 1, N - 7, N + 5], dtype=np.int32)
         exact_case(lib, orc, synth.to_bits(q, "f16"), synth.to_bits(k, "f16"), w, pos, H=H, D=D,
                    dtype="f16", ratio=ratio, topk=topk, where=f"top run N={N}")
+
+
+def test_decode_at_the_row_limit(lib, orc):
+    """Single-token decode at the most rows the decode path takes (2048 partitions
+    of 512 rows = 1048576 rows, 256 MiB of K): the merge holds the 16384-key union
+    of 8-key lists in its widest form.  Integer-valued inputs (many equal scores:
+    the merge's histogram bin is crowded and the bisection decides) bit-exact, and
+    Gaussian inputs (the histogram decides) within the tolerance."""
+    N, H, D, topk = 1 << 20, 64, 128, 512
+    rng = np.random.default_rng(20)
+    say(f"decode at the row limit, integers, N={N}")
+    q, k, w, _ = rand_int_case(rng, 1, N, H, D, -4, 4, 4, 1, "f16")
+    for p in (4 * N - 1, 4 * (N // 2) + 1):
+        out = gpu_run(lib, q, k, w, np.array([p], np.int32), H=H, D=D, dtype="f16", ratio=4,
+                      topk=topk)
+        want = orc.score_topk(q, k, w, np.array([p], np.int32), H=H, D=D, dtype="f16", ratio=4,
+                              topk=topk, threads=16)
+        assert np.array_equal(out, want), f"row limit, integers, pos {p}"
+    say(f"decode at the row limit, gaussian, N={N}")
+    q = synth.to_bits(rng.standard_normal((1, H, D)) / np.sqrt(128.0), "f16")
+    k = synth.to_bits(rng.standard_normal((N, D)) / np.sqrt(128.0), "f16")
+    w = rng.random((1, H), dtype=np.float32)
+    pos = np.array([4 * N - 1], np.int32)
+    out, sc = gpu_run(lib, q, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk, scores=True)
+    want, osc = orc.score_topk(q, k, w, pos, H=H, D=D, dtype="f16", ratio=4, topk=topk,
+                               want_scores=True, threads=16)
+    check_tolerant(out[0], sc[0], osc[0], N, topk, "row limit, gaussian")
