@@ -266,7 +266,8 @@ def batch_run(lib, q, k, w, pos, *, H, D, dtype, ratio, topk):
 
 
 @pytest.mark.parametrize("B,N,topk,dtype", [(5, 5000, 512, "f16"), (3, 700, 512, "bf16"),
-                                            (9, 1100, 48, "f16"), (2, 300, 512, "f16")])
+                                            (9, 1100, 48, "f16"), (2, 300, 512, "f16"),
+                                            (64, 3000, 512, "bf16")])
 def test_decode_batch_integer_bit_exact(lib, orc, B, N, topk, dtype):
     """Each sequence of a batched decode call equals the oracle on that sequence
     alone; positions differ per sequence (all rows, half the rows, all-fit, none)."""
