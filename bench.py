@@ -656,7 +656,7 @@ def main():
         record_traffic(*args.record_traffic)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (the indexer kernels shard over "
+        print("bench.py: the library runs on exactly one GPU (the indexer kernels shard over "
               "query tokens or rows without any collective; only the 1-GPU path is built); "
               "use --gpus 1", file=sys.stderr)
         return 2
