@@ -110,10 +110,18 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
                     rr, j < n ? (uint32_t)j * 4 : kOffNone, 0, 0));
             }
             sel.make_room(kStreamBatch);
+            if (nb <= n) { // a whole batch of visible rows: no bound check per key
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j = base + u * 64 + lane;
-                sel.append(make_key(cur[u], (uint32_t)j), j < n);
+                for (int u = 0; u < U; ++u) {
+                    const int j = base + u * 64 + lane;
+                    sel.append(make_key(cur[u], (uint32_t)j), true);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int j = base + u * 64 + lane;
+                    sel.append(make_key(cur[u], (uint32_t)j), j < n);
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
