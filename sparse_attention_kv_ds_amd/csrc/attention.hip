@@ -130,26 +130,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     const int nb_pool = (topk + 31) >> 5;
     const int nb = nb_loc + nb_pool;
 
-    // entries outside [0, N) and the padding become -1 (empty slots); with
-    // ratio > 0 the list is every pooled row the token can see, 0 .. n-1
-    const int n_all = ratio > 0 ? visible_rows(p, ratio, N) : 0;
-    for (int e = threadIdx.x; e < 32 * nb_pool; e += WAVES * 64) {
-        int j;
-        if (ratio > 0)
-            j = e < n_all ? e : -1;
-        else
-            j = e < topk ? idx[(long long)t * topk + e] : -1;
-        ids[e] = (uint32_t)j < (uint32_t)N ? j : -1;
-    }
-
-    // this wave's 32 heads as MFMA B fragments: head col, elements 16 kk + 8 hf ..
-    const auto rq = make_rsrc(q + ((long long)t * HA + wave * 32) * D, 32u * D * 2);
-    u32x4 qf[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-        qf[kk] = buf_load16(rq, ((uint32_t)col * D + kk * 16 + hf * 8) * 2);
-    __syncthreads(); // the index list
-
+    u32x4 qf[KS]; // this wave's 32 heads as MFMA B fragments (loaded below)
     const uint32_t bytes_p = (uint32_t)N * D * 2, bytes_l = (uint32_t)L * D * 2;
 
     // Loads of a block: 1 KiB load i (0 <= i < LPB) of a tensor covers rows
@@ -311,8 +292,33 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         }
     };
 
-    if (nb > 0) {
+    // Block 0 is issued first when it holds local rows (it needs no index
+    // list), then the query fragments and the index list, so that the three
+    // are in flight together.
+    if (nb_loc > 0)
         load_block(0, ks0, vs0);
+    // this wave's 32 heads as MFMA B fragments: head col, elements 16 kk + 8 hf ..
+    const auto rq = make_rsrc(q + ((long long)t * HA + wave * 32) * D, 32u * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+        qf[kk] = buf_load16(rq, ((uint32_t)col * D + kk * 16 + hf * 8) * 2);
+    // entries outside [0, N) and the padding become -1 (empty slots); with
+    // ratio > 0 the list is every pooled row the token can see, 0 .. n-1
+    const int n_all = ratio > 0 ? visible_rows(p, ratio, N) : 0;
+    for (int e = threadIdx.x; e < 32 * nb_pool; e += WAVES * 64) {
+        int j;
+        if (ratio > 0)
+            j = e < n_all ? e : -1;
+        else
+            j = e < topk ? idx[(long long)t * topk + e] : -1;
+        ids[e] = (uint32_t)j < (uint32_t)N ? j : -1;
+    }
+
+
+    lds_barrier(); // the index list, written by every wave
+    if (nb > 0) {
+        if (nb_loc == 0)
+            load_block(0, ks0, vs0);
         wait_vmcnt<0>(); // block 0 and the query fragments
         __syncthreads();
         // two blocks per iteration, so that every stage offset is a constant
