@@ -561,6 +561,7 @@ DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
             "prefill32k": ("score", "prefill_scorer_kernel"),
             "prefill64k": ("score", "prefill_scorer_kernel"),
             "attn32k": ("attention", "sparse_attention_kernel"),
+            "attn32k_r128": ("attention", "sparse_attention_kernel"),
             "decode1m_b8": ("decode_score", "decode_scorer_kernel"),
             "qproj32k": ("project", "qproj_kernel")}
 
