@@ -434,18 +434,32 @@ hipError_t merge_one(const float *S, const int32_t *pos, int N, int ratio, int t
 // fit, and the answer is each token's rows 0 .. n_t-1, then -1, with nothing
 // scored ("How I turned one oversized DeepSeek optimization into three merged
 // oMLX PRs", section "3. Do not rank candidates when every candidate wins").
-// One thread per output entry.
+// One work-group per token.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void sequential_rows_kernel(const int32_t *__restrict__ pos, int T,
                                                               int N, int ratio, int topk,
                                                               int32_t *__restrict__ out)
 {
-    const long long total = (long long)T * topk;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
-         i += (long long)gridDim.x * 256) {
-        const int t = (int)(i / topk), e = (int)(i % topk);
-        const int n = visible_rows(pos[t], ratio, N);
-        out[i] = e < n ? e : -1;
+    // one token per work-group: its visible count once, then its row of out,
+    // four entries per 16-byte store where the row allows it
+    const int t = blockIdx.x;
+    if (t >= T)
+        return; // (never: the grid is T work-groups)
+    const int n = visible_rows(pos[t], ratio, N);
+    int32_t *o = out + (long long)t * topk;
+    if (topk % 4 == 0 && ((uintptr_t)o & 15) == 0) {
+        for (int q4 = threadIdx.x; q4 < topk / 4; q4 += 256) {
+            const int e = 4 * q4;
+            int4 v;
+            v.x = e < n ? e : -1;
+            v.y = e + 1 < n ? e + 1 : -1;
+            v.z = e + 2 < n ? e + 2 : -1;
+            v.w = e + 3 < n ? e + 3 : -1;
+            *reinterpret_cast<int4 *>(o + e) = v;
+        }
+    } else {
+        for (int e = threadIdx.x; e < topk; e += 256)
+            o[e] = e < n ? e : -1;
     }
 }
 
@@ -456,10 +470,7 @@ hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, i
 {
     if (T <= 0 || topk <= 0)
         return hipSuccess;
-    long long blocks = ((long long)T * topk + 255) / 256;
-    if (blocks > 8192)
-        blocks = 8192;
-    return launch_kernel(sequential_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, tm, true,
+    return launch_kernel(sequential_rows_kernel, dim3((unsigned)T), dim3(256), 0, st, tm, true,
                          true, pos, T, N, ratio, topk, out);
 }
 
