@@ -75,6 +75,12 @@ enum {
  *   max_tokens largest T of any call (>= 1)
  *   max_rows   largest N of any call (>= 1)
  *
+ * The kernels address K and one work-group's tile of scores through 32-bit
+ * byte ranges, so max_rows must satisfy
+ *   (round_up(max_rows, 64) + 64) * head_dim * 2          < 2^31  and
+ *   (64 / n_heads) * 4 * round_up(max_rows, 64) * 4       < 2^31
+ * (at most 8,388,480 rows at head_dim 128), else DS_ERR_UNSUPPORTED;
+ * argument, support and range checks all happen before any HIP call.
  * Allocates max_tokens * round_up(max_rows, 64) * 4 bytes of score scratch
  * plus a few MiB of selection scratch on `device`.  Returns DS_OK,
  * DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_OOM or DS_ERR_HIP.

@@ -5,7 +5,7 @@
 #include "ds_indexer.h"
 #include "internal.hpp"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <limits.h>
 #include <new>
 #include <stdint.h>
@@ -161,6 +161,10 @@ int ds_indexer_create(ds_indexer **out, int device, int n_heads, int head_dim, i
         max_tokens > INT_MAX || max_rows > INT_MAX - 64)
         return DS_ERR_INVALID_ARG;
     if (!dsi::scorer_supported(n_heads, head_dim, dtype))
+        return DS_ERR_UNSUPPORTED;
+    // every call's N is at most max_rows, so this bounds the byte ranges of
+    // every later call too
+    if (!dsi::scorer_rows_supported(n_heads, head_dim, max_rows))
         return DS_ERR_UNSUPPORTED;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess)

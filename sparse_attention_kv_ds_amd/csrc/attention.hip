@@ -31,7 +31,7 @@
 //     row-major V block by LDS transpose reads (ds_read_b64_tr_b16).
 // Output fp32, o = O / (sum of p), 0 for a token with no row.
 #include "common.hpp"
-#include "internal.hpp"
+#include "launch.hpp"
 
 namespace dsi {
 
@@ -372,12 +372,6 @@ hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
 }
 
 } // namespace
-
-bool attention_supported(int HA, int D, int dtype)
-{
-    return (HA == 32 || HA == 64 || HA == 128) && (D == 64 || D == 128) &&
-           (dtype == kF16 || dtype == kBF16);
-}
 
 hipError_t launch_sparse_attention(const AttnProblem &a, hipStream_t st, Timing *tm)
 {

@@ -4,13 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.hpp"
+
 namespace dsi {
 
 constexpr int kWave = 64;
-
-// element-type tags for q and k
-constexpr int kF16 = 1;
-constexpr int kBF16 = 2;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -1,11 +1,48 @@
 // internal.hpp -- host-side launchers of the indexer kernels (not part of the C ABI).
+// Declarations only, on the HIP runtime API types, so that the argument
+// checks of api.cpp also build with a plain host C++ compiler.
 #pragma once
 
-#include <hip/hip_ext.h>
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace dsi {
+
+// element types of q and k (the DS_F16 / DS_BF16 codes of the C ABI)
+constexpr int kF16 = 1;
+constexpr int kBF16 = 2;
+
+constexpr int kPrefillWaves = 4; // waves per prefill scorer work-group
+
+// The (head count, head dim, dtype) combinations the scorer kernels are built for.
+inline bool scorer_supported(int H, int D, int dtype)
+{
+    const bool h = H == 4 || H == 8 || H == 16 || H == 32 || H == 64;
+    const bool d = D == 32 || D == 64 || D == 128;
+    return h && d && (dtype == kF16 || dtype == kBF16);
+}
+
+// Row counts whose byte ranges fit the 32-bit buffer resources of the scorer
+// and the per-token top-k: the whole of K (rows * D * 2 bytes, plus the
+// 64-row stage past the end that reads as 0), and one work-group's tile of
+// score rows ((64 / H) * kPrefillWaves tokens of round_up(rows, 64) floats),
+// which must stay below 2^31 bytes so that the masked-store offset 2^31 lies
+// outside every such range.
+inline bool scorer_rows_supported(int H, int D, int64_t rows)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    if (H < 1 || D < 1 || rows < 0 || rows > lim)
+        return false;
+    const int64_t ld = (rows + 63) / 64 * 64;
+    const int64_t tile_tokens = (int64_t)(64 / H) * kPrefillWaves;
+    return (ld + 64) * D * 2 < lim && tile_tokens * ld * 4 < lim;
+}
+
+// q[T][O] = round(x[T][K] . wq[O][K]^T): the shapes the projection kernel takes.
+inline bool qproj_supported(int K, int O, int dtype)
+{
+    return K >= 8 && K % 8 == 0 && O % 128 == 0 && (dtype == kF16 || dtype == kBF16);
+}
 
 // Optional kernel timing.  When `start` / `stop` are set, the first kernel of
 // a launcher call records `start` as it begins and the last records `stop` as
@@ -17,32 +54,6 @@ struct Timing {
     bool started = false;
     bool stopped = false;
 };
-
-// Launch `kernel` on `st`, converting each argument to the kernel's parameter
-// type; with `tm`, record its events on this launch (`first` / `last`: this
-// launch opens / closes the timed step).
-template <class... P, class... A>
-hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
-                         Timing *tm, bool first, bool last, A &&...args)
-{
-    hipEvent_t e0 = tm && first ? tm->start : nullptr;
-    hipEvent_t e1 = tm && last ? tm->stop : nullptr;
-    // the runtime's last-error slot may still hold the result of an unrelated
-    // earlier call (a query answered "not ready", say): clear it, so that the
-    // check below reports this launch only
-    (void)hipGetLastError();
-    if (e0 || e1)
-        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u,
-                              static_cast<P>(args)...);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, lds, st, static_cast<P>(args)...);
-    const hipError_t e = hipGetLastError();
-    if (e == hipSuccess && tm) {
-        tm->started |= e0 != nullptr;
-        tm->stopped |= e1 != nullptr;
-    }
-    return e;
-}
 
 struct Problem {
     const void *q;       // [T][H][D] raw fp16/bf16 bits
@@ -61,8 +72,6 @@ constexpr int kDecodeMaxParts = kDecodeUnion / 8;
 // most sequences of one batched decode call (each owns kDecodeUnion candidate
 // slots and kDecodeMaxParts partition entries of the workspace)
 constexpr int kDecodeMaxBatch = 64;
-
-bool scorer_supported(int H, int D, int dtype);
 
 // Scores of every token with more than min_rows visible rows, written to
 // S[t * ldS + j] for j < n_t (other entries untouched).
@@ -115,7 +124,6 @@ hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, i
                                   int32_t *out, hipStream_t st, Timing *tm = nullptr);
 
 // q[T][O] = round(x[T][K] . wq[O][K]^T) in dtype (qproj.hip)
-bool qproj_supported(int K, int O, int dtype);
 hipError_t launch_qproj(const void *x, const void *wq, int T, int K, int O, int dtype, void *q,
                         hipStream_t st, Timing *tm = nullptr);
 
@@ -137,7 +145,11 @@ struct AttnProblem {
     float *out;           // [T][HA][D] fp32
 };
 
-bool attention_supported(int HA, int D, int dtype);
+inline bool attention_supported(int HA, int D, int dtype)
+{
+    return (HA == 32 || HA == 64 || HA == 128) && (D == 64 || D == 128) &&
+           (dtype == kF16 || dtype == kBF16);
+}
 
 hipError_t launch_sparse_attention(const AttnProblem &a, hipStream_t st, Timing *tm = nullptr);
 

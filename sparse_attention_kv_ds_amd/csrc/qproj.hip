@@ -20,7 +20,7 @@
 // Work-groups are ordered so that the tiles of one XCD share an eighth of the
 // weight rows, which then stay in that XCD's L2.
 #include "common.hpp"
-#include "internal.hpp"
+#include "launch.hpp"
 
 namespace dsi {
 
@@ -238,11 +238,6 @@ hipError_t launch_qproj_dt(const uint16_t *x, const uint16_t *wq, int T, int K, 
 }
 
 } // namespace
-
-bool qproj_supported(int K, int O, int dtype)
-{
-    return K >= 8 && K % 8 == 0 && O % 128 == 0 && (dtype == kF16 || dtype == kBF16);
-}
 
 hipError_t launch_qproj(const void *x, const void *wq, int T, int K, int O, int dtype, void *q,
                         hipStream_t st, Timing *tm)

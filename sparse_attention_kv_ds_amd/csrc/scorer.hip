@@ -17,14 +17,13 @@
 // tile are 16 different heads of one row j) plus one exchange between the two
 // half-waves.
 #include "common.hpp"
-#include "internal.hpp"
+#include "launch.hpp"
 #include "select.hpp"
 
 namespace dsi {
 
 namespace {
 
-constexpr int kPrefillWaves = 4;    // waves per prefill work-group
 constexpr int kChunkRows = 2048;    // compressed rows per prefill work-group (multiple of 64)
 constexpr int kStageRows = 64;      // K rows per LDS stage (two 32-row blocks)
 
@@ -611,13 +610,6 @@ template <int H, int D, int DT> struct DecodeF {
 };
 
 } // namespace
-
-bool scorer_supported(int H, int D, int dtype)
-{
-    const bool h = H == 4 || H == 8 || H == 16 || H == 32 || H == 64;
-    const bool d = D == 32 || D == 64 || D == 128;
-    return h && d && (dtype == kF16 || dtype == kBF16);
-}
 
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
                                  hipStream_t st, Timing *tm)

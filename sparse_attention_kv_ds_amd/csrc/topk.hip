@@ -17,7 +17,7 @@
 // key: bisection over the score bits until at most 64 candidates remain in the
 // boundary band, then one bitonic sort of that band across the lanes of a wave.
 #include "common.hpp"
-#include "internal.hpp"
+#include "launch.hpp"
 #include "select.hpp"
 
 namespace dsi {

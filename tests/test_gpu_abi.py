@@ -1,0 +1,216 @@
+"""The C ABI's status paths on a live handle, on the GPU.
+
+Every rejected call below is one that tests/abi_host/abi_host_check.cpp shows
+returns before any launch (the same api.cpp, built for the host); here they
+run against the real library with real device buffers: misaligned pointers
+are offsets inside valid allocations, and a rejected call must leave its
+output untouched.  Accepted calls at the edges of the handle's capacity must
+succeed and give valid results.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+H, D, TOPK, MAXT, MAXN = 64, 128, 512, 64, 4096
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from sparse_attention_kv_ds_amd import indexer
+    return indexer
+
+
+@pytest.fixture(scope="module")
+def handle(lib):
+    st, h = lib.ds_indexer_create(0, H, D, lib.DS_F16, TOPK, MAXT, MAXN)
+    assert st == lib.DS_OK
+    yield h
+    lib.ds_indexer_destroy(h)
+
+
+@pytest.fixture(scope="module")
+def bufs():
+    """Device buffers large enough for every call below (zeros: all scores 0)."""
+    b = {"q": torch.zeros((MAXT + 1) * H * D + 64, dtype=torch.int16, device=DEV),
+         "k": torch.zeros((MAXN + 1) * D + 64, dtype=torch.int16, device=DEV),
+         "w": torch.zeros((MAXT + 1) * H + 16, dtype=torch.float32, device=DEV),
+         "pos": torch.full((MAXT + 16,), 4 * MAXN - 1, dtype=torch.int32, device=DEV),
+         "out": torch.full(((MAXT + 1) * (TOPK + 1) + 16,), -7, dtype=torch.int32, device=DEV),
+         "sc": torch.zeros((MAXT + 1) * (MAXN + 1) + 16, dtype=torch.float32, device=DEV)}
+    return b
+
+
+def ptrs(b):
+    return {k: v.data_ptr() for k, v in b.items()}
+
+
+def stream():
+    return torch.cuda.current_stream(DEV).cuda_stream
+
+
+def rejected(lib, bufs, want, fn, what):
+    bufs["out"].fill_(-7)
+    torch.cuda.synchronize(DEV)
+    st = fn()
+    torch.cuda.synchronize(DEV)
+    assert st == want, f"{what}: status {st}, want {want}"
+    assert bool((bufs["out"] == -7).all()), f"{what}: output written by a rejected call"
+
+
+def test_score_topk_status_paths(lib, handle, bufs):
+    p = ptrs(bufs)
+    s = stream()
+
+    def call(q=p["q"], k=p["k"], w=p["w"], pos=p["pos"], T=4, N=MAXN, ratio=4, topk=TOPK,
+             out=p["out"], h=handle):
+        return lib.ds_indexer_score_topk(h, q, k, w, pos, T, N, ratio, topk, out, s)
+
+    inv, cap = lib.DS_ERR_INVALID_ARG, lib.DS_ERR_CAPACITY
+    say("score_topk: argument errors")
+    for what, kw in (("null handle", dict(h=None)), ("T < 0", dict(T=-1)), ("N < 0", dict(N=-1)),
+                     ("ratio 0", dict(ratio=0)), ("q NULL", dict(q=None)),
+                     ("k NULL", dict(k=None)), ("w NULL", dict(w=None)),
+                     ("pos NULL", dict(pos=None)), ("out NULL", dict(out=None)),
+                     ("q misaligned", dict(q=p["q"] + 8)), ("k misaligned", dict(k=p["k"] + 8)),
+                     ("w misaligned", dict(w=p["w"] + 2)), ("pos misaligned", dict(pos=p["pos"] + 2)),
+                     ("out misaligned", dict(out=p["out"] + 2)), ("topk 0", dict(topk=0)),
+                     ("topk < 0", dict(topk=-3))):
+        rejected(lib, bufs, inv, lambda: call(**kw), what)
+    say("score_topk: capacity errors")
+    for what, kw in (("T above max_tokens", dict(T=MAXT + 1)),
+                     ("N above max_rows", dict(N=MAXN + 1)),
+                     ("topk above max_topk", dict(topk=TOPK + 1))):
+        rejected(lib, bufs, cap, lambda: call(**kw), what)
+    rejected(lib, bufs, inv, lambda: call(q=None, T=MAXT + 1), "argument error before capacity")
+    say("score_topk: accepted at the capacity edges")
+    for T in (0, 1, MAXT):
+        bufs["out"].fill_(-7)
+        assert call(T=T) == lib.DS_OK
+        torch.cuda.synchronize(DEV)
+        if T:
+            # all scores 0: the tie rule keeps rows 0 .. topk-1
+            got = bufs["out"][:T * TOPK].view(T, TOPK).cpu().numpy()
+            assert (got == np.arange(TOPK)[None, :]).all(), f"T={T}"
+    assert call(k=None, N=0) == lib.DS_OK  # no rows: no K needed, every entry -1
+    torch.cuda.synchronize(DEV)
+    assert bool((bufs["out"][:4 * TOPK] == -1).all())
+
+
+def test_batch_status_paths(lib, handle, bufs):
+    p = ptrs(bufs)
+    s = stream()
+
+    def call(q=p["q"], k=p["k"], B=2, N=MAXN, topk=TOPK, out=p["out"], h=handle):
+        return lib.ds_indexer_score_topk_batch(h, q, k, p["w"], p["pos"], B, N, 4, topk, out, s)
+
+    inv, cap = lib.DS_ERR_INVALID_ARG, lib.DS_ERR_CAPACITY
+    say("score_topk_batch: argument and capacity errors")
+    for what, want, kw in (("null handle", inv, dict(h=None)), ("q NULL", inv, dict(q=None)),
+                           ("out NULL", inv, dict(out=None)), ("B < 0", inv, dict(B=-1)),
+                           ("k misaligned", inv, dict(k=p["k"] + 4)), ("topk 0", inv, dict(topk=0)),
+                           ("B above max_tokens", cap, dict(B=MAXT + 1)),
+                           ("N above max_rows", cap, dict(N=MAXN + 1)),
+                           ("topk above max_topk", cap, dict(topk=TOPK + 1))):
+        rejected(lib, bufs, want, lambda: call(**kw), what)
+    assert call(B=0) == lib.DS_OK
+    # more sequences than one batched call takes (64), on a handle with room for more tokens
+    st, wide = lib.ds_indexer_create(0, H, D, lib.DS_F16, TOPK, 100, 1024)
+    assert st == lib.DS_OK
+    try:
+        big_k = torch.zeros(65 * 1024 * D, dtype=torch.int16, device=DEV)
+        rejected(lib, bufs, cap, lambda: lib.ds_indexer_score_topk_batch(
+            wide, p["q"], big_k.data_ptr(), p["w"], p["pos"], 65, 1024, 4, TOPK, p["out"], s),
+            "B above 64")
+        assert lib.ds_indexer_score_topk_batch(wide, p["q"], big_k.data_ptr(), p["w"], p["pos"],
+                                               64, 1024, 4, TOPK, p["out"], s) == lib.DS_OK
+        torch.cuda.synchronize(DEV)
+    finally:
+        lib.ds_indexer_destroy(wide)
+    # a handle whose rows exceed the single-token path (2048 partitions of 512)
+    st, big = lib.ds_indexer_create(0, H, D, lib.DS_F16, TOPK, 2, (1 << 20) + 1)
+    assert st == lib.DS_OK
+    try:
+        rejected(lib, bufs, lib.DS_ERR_UNSUPPORTED, lambda: lib.ds_indexer_score_topk_batch(
+            big, p["q"], p["k"], p["w"], p["pos"], 2, MAXN, 4, TOPK, p["out"], s),
+            "no single-token path")
+    finally:
+        lib.ds_indexer_destroy(big)
+
+
+def test_scores_status_paths(lib, handle, bufs):
+    p = ptrs(bufs)
+    s = stream()
+
+    def call(sc=p["sc"], T=4, N=MAXN, q=p["q"]):
+        return lib.ds_indexer_scores(handle, q, p["k"], p["w"], p["pos"], T, N, 4, sc, s)
+
+    say("scores: argument and capacity errors")
+    assert lib.ds_indexer_scores(None, p["q"], p["k"], p["w"], p["pos"], 4, MAXN, 4, p["sc"],
+                                 s) == lib.DS_ERR_INVALID_ARG
+    assert call(sc=None) == lib.DS_ERR_INVALID_ARG
+    assert call(sc=p["sc"] + 2) == lib.DS_ERR_INVALID_ARG
+    assert call(q=p["q"] + 2) == lib.DS_ERR_INVALID_ARG
+    assert call(T=MAXT + 1) == lib.DS_ERR_CAPACITY
+    assert call(N=MAXN + 1) == lib.DS_ERR_CAPACITY
+    assert call(T=0) == lib.DS_OK and call(N=0) == lib.DS_OK
+    bufs["sc"].fill_(5.0)
+    assert call(T=MAXT) == lib.DS_OK
+    torch.cuda.synchronize(DEV)
+    assert bool((bufs["sc"][:MAXT * MAXN] == 0).all())  # every row visible, every score 0
+
+
+def test_projection_status_paths(lib, handle, bufs):
+    p = ptrs(bufs)
+    s = stream()
+    x = torch.zeros(MAXT * 1536 + 64, dtype=torch.int16, device=DEV)
+    wq = torch.zeros(H * D * 1536 + 64, dtype=torch.int16, device=DEV)
+    px, pw = x.data_ptr(), wq.data_ptr()
+
+    def proj(x=px, w=pw, T=4, din=1536, q=p["q"], h=handle):
+        return lib.ds_indexer_project_q(h, x, w, T, din, q, s)
+
+    inv, uns, cap = lib.DS_ERR_INVALID_ARG, lib.DS_ERR_UNSUPPORTED, lib.DS_ERR_CAPACITY
+    say("project_q: argument, support and capacity errors")
+    for want, kw in ((inv, dict(h=None)), (inv, dict(T=-1)), (inv, dict(din=0)),
+                     (inv, dict(x=None)), (inv, dict(w=None)), (inv, dict(q=None)),
+                     (inv, dict(x=px + 8)), (inv, dict(q=p["q"] + 4)),
+                     (uns, dict(din=12)), (uns, dict(T=64, din=1 << 24)),
+                     (uns, dict(din=1 << 17)), (cap, dict(T=MAXT + 1))):
+        assert proj(**kw) == want, kw
+    assert proj(T=0) == lib.DS_OK
+    assert proj(T=MAXT) == lib.DS_OK
+    torch.cuda.synchronize(DEV)
+
+    def fused(T=4, N=MAXN, din=1536, topk=TOPK, out=p["out"]):
+        return lib.ds_indexer_project_score_topk(handle, px, pw, p["k"], p["w"], p["pos"], T, N,
+                                                 din, 4, topk, out, s)
+    say("project_score_topk: errors and the capacity edge")
+    for what, want, kw in (("out NULL", inv, dict(out=None)), ("topk 0", inv, dict(topk=0)),
+                           ("d_in 20", uns, dict(din=20)), ("T above", cap, dict(T=MAXT + 1)),
+                           ("topk above", cap, dict(topk=TOPK + 1))):
+        rejected(lib, bufs, want, lambda: fused(**kw), what)
+    assert fused(T=MAXT) == lib.DS_OK
+    torch.cuda.synchronize(DEV)
+    got = bufs["out"][:MAXT * TOPK].view(MAXT, TOPK).cpu().numpy()
+    assert (got == np.arange(TOPK)[None, :]).all()  # x = 0: q = 0, all scores 0
+
+
+def test_create_range_limits_before_any_allocation(lib):
+    """Row counts beyond the kernels' 32-bit byte ranges are refused (no memory is
+    allocated for them); the largest accepted one creates and destroys."""
+    st, h = lib.ds_indexer_create(0, 64, 128, lib.DS_F16, 512, 1, 8388481)
+    assert st == lib.DS_ERR_UNSUPPORTED and h is None
+    st, h = lib.ds_indexer_create(0, 4, 32, lib.DS_F16, 512, 1, 8388545)
+    assert st == lib.DS_ERR_UNSUPPORTED and h is None
+    st, h = lib.ds_indexer_create(0, 64, 128, lib.DS_F16, 512, 1, 8388480)
+    assert st == lib.DS_OK
+    lib.ds_indexer_destroy(h)
