@@ -17,15 +17,22 @@ chunk's indices (2048 tokens x 64 heads over a 128-row local window plus 512
 listed pooled rows each), and times the CPU oracle on a bounded token sample of
 the headline workload.
 
-The step time is taken over K calls with nothing else on the stream.  The
-per-kernel durations come from a second timed pass of K calls in which the
-library has each of its kernels record HIP events from its own dispatch
-(ds_indexer_timing: start of the first kernel of a step, end of the last, on
-the call's stream); launches that carry events are dispatched more slowly, so
-that pass's step time is reported apart.
+Every workload is warmed up for at least --warmup calls AND at least
+--warmup-ms milliseconds of back-to-back calls (the GPU needs some tens of
+milliseconds of work to reach its steady clock, whatever the call count), and
+the warm-up actually done is reported.  The step time is then taken over
+exactly K calls between two device synchronisations, with nothing else on the
+stream; a second pass of K calls with an event between consecutive calls gives
+the median and minimum single-call time.  The per-kernel durations come from a
+third pass of K calls in which the library has each of its kernels record HIP
+events from its own dispatch (ds_indexer_timing: start of the first kernel of a
+step, end of the last, on the call's stream); launches that carry events are
+dispatched more slowly, so that pass's step time is reported apart.  The
+headline workload is timed again at the end of the run as a bracketing control
+(machine-speed drift between the first and the last measurement).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults K = 50, W = 200: the
-                       GPU needs some tens of milliseconds of work to reach its full clock)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-ms M]
+                       (defaults K = 50, W = 200, M = 300)
        python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|decode1m_b8|qproj32k|attn32k|attn32k_r128
                                                                  (one workload, for profilers)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
@@ -57,7 +64,7 @@ METRIC = "indexer scored pairs/sec + query tokens/sec at 32k/64k context; decode
 PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0                               # MI355X HBM3E
 HEADLINE = "prefill32k"
-SECONDARY = ("prefill64k", "decode1m", "prefill2k")
+SECONDARY = ("prefill8k", "prefill64k", "decode1m", "prefill2k")
 DECODE_K_BUFFERS = 8
 KERNEL_SOURCES = {  # kernel class -> sources whose change invalidates stored counters
     "score": ["sparse_attention_kv_ds_amd/csrc/scorer.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
@@ -97,7 +104,61 @@ def upload(d, dev):
             torch.from_numpy(d["pos"]).to(dev))
 
 
-def time_workload(name: str, steps: int, warmup: int):
+WARMUP_MS = 300.0  # default least warm-up time per workload
+
+
+def warm_up(call, warmup: int, warmup_ms: float, dev):
+    """At least `warmup` calls and at least `warmup_ms` of back-to-back calls
+    (issued in chunks of about 10 ms between synchronisations); returns
+    (calls, milliseconds) actually spent."""
+    import torch
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    n, chunk = 0, 2
+    while True:
+        for _ in range(chunk):
+            call(n)
+            n += 1
+        torch.cuda.synchronize(dev)
+        el = (time.perf_counter() - t0) * 1e3
+        if n >= warmup and el >= warmup_ms:
+            return n, el
+        chunk = max(1, min(2000, int(10.0 / max(el / n, 1e-3))))
+
+
+def timed_calls(call, steps: int, dev, first: int = 0):
+    """Exactly `steps` calls between two device synchronisations; the average
+    milliseconds per call from events around them."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    a.record()
+    for i in range(steps):
+        call(first + i)
+    b.record()
+    torch.cuda.synchronize(dev)
+    return a.elapsed_time(b) / steps
+
+
+def per_call_stats(call, steps: int, dev):
+    """`steps` calls with an event between consecutive calls: the median and the
+    minimum of the single-call durations (each includes one event record)."""
+    import statistics
+
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize(dev)
+    ev[0].record()
+    for i in range(steps):
+        call(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize(dev)
+    d = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return {"median_ms": statistics.median(d), "min_ms": min(d), "max_ms": max(d)}
+
+
+def time_workload(name: str, steps: int, warmup: int, warmup_ms: float = WARMUP_MS):
     """Time `steps` calls of one workload; returns a result dict."""
     import torch
     from sparse_attention_kv_ds_amd import synth
@@ -113,28 +174,21 @@ def time_workload(name: str, steps: int, warmup: int):
                for i in range(DECODE_K_BUFFERS - 1)]
     out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
     ix = Indexer(wl.H, wl.D, wl.dtype, wl.topk, wl.T, wl.N, device=0)
-    def timed_steps():
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize(dev)
-        t0.record()
-        for i in range(steps):
-            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
-        t1.record()
-        torch.cuda.synchronize(dev)
-        return t0.elapsed_time(t1) / steps
+
+    def call(i):
+        ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
 
     try:
-        for i in range(warmup):
-            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=out)
+        nw, wms = warm_up(call, warmup, warmup_ms, dev)
         # the step time without per-kernel events (launches that record them are
         # dispatched more slowly) ...
-        ms = timed_steps()
+        ms = timed_calls(call, steps, dev)
+        stats = per_call_stats(call, steps, dev)
         # ... then the same steps again with the kernels recording HIP events from
         # their own dispatch, for the kernel durations
         ix.timing(True)
         ix.timing_read()
-        ms_marked = timed_steps()
+        ms_marked = timed_calls(call, steps, dev)
         per = ix.timing_read()
         ix.timing(False)
     finally:
@@ -142,10 +196,13 @@ def time_workload(name: str, steps: int, warmup: int):
     kernels = {c: {"avg_ms": v[0] / v[1], "launches": v[1]} for c, v in per.items() if v[1]}
     pairs = visible_pairs(wl)
     res = {"workload": name, "ms_per_step": ms, "ms_per_step_with_markers": ms_marked,
+           "step_stats": stats, "warmup_calls": nw, "warmup_ms": wms,
            "pairs": pairs, "tokens": wl.T,
            "pairs_per_s": pairs / (ms * 1e-3), "query_tokens_per_s": wl.T / (ms * 1e-3),
            "kernels": kernels, "wl": wl}
-    log(f"[bench] {name}: {ms * 1e3:.1f} us/step ({ms_marked * 1e3:.1f} with kernel markers), "
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step (median {stats['median_ms'] * 1e3:.1f}, "
+        f"min {stats['min_ms'] * 1e3:.1f}; {ms_marked * 1e3:.1f} with kernel markers; "
+        f"warm-up {nw} calls, {wms:.0f} ms), "
         + ", ".join(f"{c} {v['avg_ms'] * 1e3:.1f} us" for c, v in kernels.items()))
     return res
 
@@ -158,7 +215,7 @@ DECODE_BATCH = "decode1m_b8"
 PROJECTION = "qproj32k"
 
 
-def time_projection(name: str, steps: int, warmup: int):
+def time_projection(name: str, steps: int, warmup: int, warmup_ms: float = WARMUP_MS):
     """Time `steps` calls of the query projection fused ahead of the indexer on
     the 32k chunk (projection, then score + top-k, in one call)."""
     import numpy as np
@@ -176,27 +233,16 @@ def time_projection(name: str, steps: int, warmup: int):
     out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
     ix = Indexer(wl.H, wl.D, d["dtype"], wl.topk, wl.T, wl.N, device=0)
 
-    def call():
+    def call(i):
         ix.project_score_topk(up["x"], up["wq"], up["k"], w, pos, wl.ratio, wl.topk, out=out)
 
-    def timed_steps():
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize(dev)
-        t0.record()
-        for _ in range(steps):
-            call()
-        t1.record()
-        torch.cuda.synchronize(dev)
-        return t0.elapsed_time(t1) / steps
-
     try:
-        for _ in range(warmup):
-            call()
-        ms = timed_steps()
+        nw, wms = warm_up(call, warmup, warmup_ms, dev)
+        ms = timed_calls(call, steps, dev)
+        stats = per_call_stats(call, steps, dev)
         ix.timing(True)
         ix.timing_read()
-        ms_marked = timed_steps()
+        ms_marked = timed_calls(call, steps, dev)
         per = ix.timing_read()
         ix.timing(False)
     finally:
@@ -209,7 +255,8 @@ def time_projection(name: str, steps: int, warmup: int):
         + ", ".join(f"{c} {v * 1e3:.1f} us" for c, v in kernels.items())
         + f"; projection {ach:.0f} TFLOP/s ({ach / peak * 100:.1f} % of {d['dtype']} MFMA peak)")
     return {"workload": name, "dtype": d["dtype"], "ms_per_step": ms,
-            "ms_per_step_with_markers": ms_marked, "kernels_ms": kernels,
+            "ms_per_step_with_markers": ms_marked, "step_stats": stats, "warmup_calls": nw,
+            "warmup_ms": wms, "kernels_ms": kernels,
             "value": wl.T / (ms * 1e-3), "unit": "query tokens/s (projection + score + top-k)",
             "roofline": {"bound": "mfma", "kernel": "qproj", "achieved": ach, "peak": peak,
                          "unit": "TFLOP/s", "frac": ach / peak,
@@ -217,7 +264,7 @@ def time_projection(name: str, steps: int, warmup: int):
                          "algorithmic_flops_per_launch": flops}}
 
 
-def time_decode_batch(name: str, steps: int, warmup: int):
+def time_decode_batch(name: str, steps: int, warmup: int, warmup_ms: float = WARMUP_MS):
     """Time `steps` batched decode calls (B sequences of 262144 rows: 512 MiB of K,
     above the last-level cache, so every call streams K from HBM)."""
     import numpy as np
@@ -235,24 +282,16 @@ def time_decode_batch(name: str, steps: int, warmup: int):
     out = torch.empty((B, wl.topk), dtype=torch.int32, device=dev)
     ix = Indexer(wl.H, wl.D, wl.dtype, wl.topk, B, wl.N, device=0)
 
-    def timed_steps():
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize(dev)
-        t0.record()
-        for _ in range(steps):
-            ix.score_topk_batch(q, k, w, pos, wl.ratio, wl.topk, out=out)
-        t1.record()
-        torch.cuda.synchronize(dev)
-        return t0.elapsed_time(t1) / steps
+    def call(i):
+        ix.score_topk_batch(q, k, w, pos, wl.ratio, wl.topk, out=out)
 
     try:
-        for _ in range(warmup):
-            ix.score_topk_batch(q, k, w, pos, wl.ratio, wl.topk, out=out)
-        ms = timed_steps()
+        nw, wms = warm_up(call, warmup, warmup_ms, dev)
+        ms = timed_calls(call, steps, dev)
+        stats = per_call_stats(call, steps, dev)
         ix.timing(True)
         ix.timing_read()
-        ms_marked = timed_steps()
+        ms_marked = timed_calls(call, steps, dev)
         per = ix.timing_read()
         ix.timing(False)
     finally:
@@ -265,7 +304,8 @@ def time_decode_batch(name: str, steps: int, warmup: int):
         f"kernel markers), " + ", ".join(f"{c} {v * 1e3:.1f} us" for c, v in kernels.items())
         + f"; scorer {ach:.0f} GB/s ({ach / PEAK_HBM_GBS * 100:.1f} % of HBM)")
     return {"workload": name, "dtype": wl.dtype, "sequences": B, "ms_per_step": ms,
-            "ms_per_step_with_markers": ms_marked, "kernels_ms": kernels,
+            "ms_per_step_with_markers": ms_marked, "step_stats": stats, "warmup_calls": nw,
+            "warmup_ms": wms, "kernels_ms": kernels,
             "value": algo / (ms * 1e-3) / 1e9, "unit": "GB/s (whole batched decode call, K from HBM)",
             "sequences_per_s": B / (ms * 1e-3),
             "roofline": {"bound": "hbm", "kernel": "decode_scorer (batched)", "achieved": ach,
@@ -274,7 +314,7 @@ def time_decode_batch(name: str, steps: int, warmup: int):
                          "algorithmic_bytes_per_launch": algo}}
 
 
-def time_attention(name: str, steps: int, warmup: int):
+def time_attention(name: str, steps: int, warmup: int, warmup_ms: float = WARMUP_MS):
     """Time `steps` calls of the sparse attention (one kernel per call) on one
     workload; the duration of a call is events around back-to-back calls on
     the stream the kernel runs on."""
@@ -292,7 +332,7 @@ def time_attention(name: str, steps: int, warmup: int):
     pos = torch.from_numpy(d["pos"]).to(dev)
     out = torch.empty((wl.T, wl.HA, wl.DV), dtype=torch.float32, device=dev)
 
-    def call():
+    def call(i):
         if wl.ratio > 0:  # every visible pooled row, no index list
             sparse_attention_all(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], pos, ratio=wl.ratio,
                                  window=wl.window, scale=wl.scale, dtype=wl.dtype, out=out)
@@ -300,17 +340,9 @@ def time_attention(name: str, steps: int, warmup: int):
             sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], idx, pos,
                              window=wl.window, scale=wl.scale, dtype=wl.dtype, out=out)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize(dev)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        call()
-    b.record()
-    torch.cuda.synchronize(dev)
-    ms = a.elapsed_time(b) / steps
+    nw, wms = warm_up(call, warmup, warmup_ms, dev)
+    ms = timed_calls(call, steps, dev)
+    stats = per_call_stats(call, steps, dev)
     # rows attended per token: the local window (clamped to positions 0..L-1)
     # plus the listed pooled rows
     p = wl.positions.astype(np.int64)
@@ -329,7 +361,8 @@ def time_attention(name: str, steps: int, warmup: int):
            + d["idx"].nbytes + wl.T * 4 + wl.T * wl.HA * wl.DV * 4)
     log(f"[bench] {name}: {ms * 1e3:.1f} us/call, {rows / wl.T:.0f} rows per token, "
         f"{ach:.0f} TFLOP/s ({ach / peak * 100:.1f} % of {wl.dtype} MFMA peak)")
-    return {"workload": name, "dtype": wl.dtype, "ms_per_step": ms,
+    return {"workload": name, "dtype": wl.dtype, "ms_per_step": ms, "step_stats": stats,
+            "warmup_calls": nw, "warmup_ms": wms,
             "value": wl.T / (ms * 1e-3), "unit": "query tokens/s",
             "rows_attended_per_token": rows / wl.T,
             "roofline": {"bound": "mfma", "kernel": "sparse_attention", "achieved": ach,
@@ -380,19 +413,29 @@ def roofline(res):
             "algorithmic_flops_per_launch": flops}
 
 
-def cpu_baseline(name: str, budget_s: float = 12.0):
-    """The oracle, as it stands, on a bounded token sample of the same workload."""
+def cpu_threads():
+    """(host cores this process may run on, threads the oracle uses): every core of
+    the affinity mask, or the process's CPU share when OMP_NUM_THREADS sets a
+    smaller one (a GPU machine hands each GPU's jobs a share of its cores)."""
+    try:
+        host = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(host, int(share)) if share.isdigit() and int(share) > 0 else host
+    return host, max(1, threads)
+
+
+def oracle_rate(name: str, threads: int, budget_s: float):
+    """The oracle, as it stands, on `threads` threads over an evenly spaced token
+    sample of one workload, repeated until about `budget_s` seconds have passed:
+    (pairs/s, tokens in the sample, passes, pairs, seconds)."""
     import numpy as np
     from oracle import oracle
     from sparse_attention_kv_ds_amd import synth
 
     d = synth.make(name)
     wl = d["wl"]
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
     orc = oracle.load()
     p = wl.positions.astype(np.int64)
     n_t = np.clip((p + 1) // wl.ratio, 0, wl.N)
@@ -400,23 +443,44 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
     def run(toks):
         t = time.perf_counter()
         orc.score_topk(d["q"], d["k"], d["w"], d["pos"], H=wl.H, D=wl.D, dtype=wl.dtype,
-                       ratio=wl.ratio, topk=wl.topk, tokens=toks, threads=cores)
+                       ratio=wl.ratio, topk=wl.topk, tokens=toks, threads=threads)
         return time.perf_counter() - t
 
-    probe = np.linspace(0, wl.T - 1, 2 * cores).astype(np.int64)
+    probe = np.linspace(0, wl.T - 1, min(wl.T, 2 * threads)).astype(np.int64)
     tp = run(probe)
     count = int(min(wl.T, max(len(probe), len(probe) * budget_s / max(tp, 1e-3))))
     toks = np.linspace(0, wl.T - 1, count).astype(np.int64)
-    # the whole sample, repeated until about `budget_s` of CPU time has passed
     el, reps = 0.0, 0
     while reps == 0 or el < budget_s:
         el += run(toks)
         reps += 1
     pairs = int(n_t[toks].sum()) * reps
-    log(f"[bench] cpu oracle: {count} tokens x {reps}, {pairs} pairs in {el:.2f} s on {cores} threads")
-    return {"value": pairs / el, "unit": "pairs/s", "cores": cores, "kind": "oracle",
-            "sample": f"{count} of {wl.T} query tokens of {name} (evenly spaced), {reps} pass(es), "
-                      f"{pairs} scored pairs, fp64 scoring + full sort, {el:.1f} s wall"}
+    return pairs / el, count, reps, pairs, el
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The oracle on the host's CPU share over a bounded sample of the headline
+    workload, plus 1-thread runs on the tiny, 8k and decode workloads."""
+    host, threads = cpu_threads()
+    from sparse_attention_kv_ds_amd import synth
+    T = synth.WORKLOADS[name].T
+    rate, count, reps, pairs, el = oracle_rate(name, threads, budget_s)
+    log(f"[bench] cpu oracle: {count} tokens x {reps}, {pairs} pairs in {el:.2f} s on {threads} "
+        f"threads ({host} host cores)")
+    single = {}
+    for wname, b in (("tiny", 1.0), ("prefill8k", 4.0), ("decode1m", 1.0)):
+        r1, c1, n1, p1, e1 = oracle_rate(wname, 1, b)
+        single[wname] = {"value": r1, "unit": "pairs/s", "sample_tokens": c1, "passes": n1,
+                         "pairs": p1, "seconds": e1}
+        log(f"[bench] cpu oracle, 1 thread: {wname} {r1:.3g} pairs/s ({c1} tokens x {n1})")
+    return {"value": rate, "unit": "pairs/s", "cores": threads, "host_cores": host,
+            "kind": "oracle",
+            "sample": f"{count} of {T} query tokens of {name} (evenly spaced), {reps} pass(es), "
+                      f"{pairs} scored pairs, fp64 scoring + full sort, {el:.1f} s wall on "
+                      f"{threads} threads",
+            "threads_rule": "every core of the affinity mask, or the CPU share OMP_NUM_THREADS "
+                            "sets when smaller",
+            "single_thread": single}
 
 
 def copy_calibration(mib: int = 512, reps: int = 3):
@@ -632,6 +696,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup-ms", type=float, default=WARMUP_MS,
+                    help="least warm-up time per workload, whatever --warmup says")
     ap.add_argument("--only", choices=[HEADLINE, *SECONDARY, ATTN_WORKLOAD, *ATTN_SECONDARY,
                                        DECODE_BATCH, PROJECTION])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -673,25 +739,26 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    wms = args.warmup_ms
     if args.only == PROJECTION:
-        print(json.dumps(time_projection(args.only, args.steps, args.warmup)))
+        print(json.dumps(time_projection(args.only, args.steps, args.warmup, wms)))
         return 0
     if args.only == DECODE_BATCH:
-        res = time_decode_batch(args.only, args.steps, args.warmup)
+        res = time_decode_batch(args.only, args.steps, args.warmup, wms)
         print(json.dumps(res))
         return 0
     if args.only in (ATTN_WORKLOAD, *ATTN_SECONDARY):
-        res = time_attention(args.only, args.steps, args.warmup)
+        res = time_attention(args.only, args.steps, args.warmup, wms)
         print(json.dumps({k: v for k, v in res.items()}))
         return 0
     if args.only:
-        res = time_workload(args.only, args.steps, args.warmup)
+        res = time_workload(args.only, args.steps, args.warmup, wms)
         print(json.dumps({"workload": args.only, "ms_per_step": res["ms_per_step"],
-                          "kernels": res["kernels"]}))
+                          "step_stats": res["step_stats"], "kernels": res["kernels"]}))
         return 0
 
-    head = time_workload(HEADLINE, args.steps, args.warmup)
-    sec = [time_workload(n, args.steps, args.warmup) for n in SECONDARY]
+    head = time_workload(HEADLINE, args.steps, args.warmup, wms)
+    sec = [time_workload(n, args.steps, args.warmup, wms) for n in SECONDARY]
     line = {
         "metric": METRIC,
         "value": head["pairs_per_s"],
@@ -701,6 +768,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
         "ms_per_step_with_markers": head["ms_per_step_with_markers"],
+        "step_stats": head["step_stats"],
+        "warmup_calls": head["warmup_calls"],
+        "warmup_ms": head["warmup_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -720,6 +790,8 @@ def main():
         wl = r["wl"]
         entry = {"workload": r["workload"], "dtype": wl.dtype, "ms_per_step": r["ms_per_step"],
                  "ms_per_step_with_markers": r["ms_per_step_with_markers"],
+                 "step_stats": r["step_stats"], "warmup_calls": r["warmup_calls"],
+                 "warmup_ms": r["warmup_ms"],
                  "kernels_ms": {c: v["avg_ms"] for c, v in r["kernels"].items()},
                  "roofline": roofline(r)}
         if wl.T == 1:
@@ -735,11 +807,16 @@ def main():
         line["secondary"].append(entry)
     # the consumer of the indices (sparse attention over the selected rows)
     # several sequences of one query token each in one call (batched decode)
-    line["secondary"].append(time_decode_batch(DECODE_BATCH, args.steps, min(args.warmup, 50)))
+    line["secondary"].append(time_decode_batch(DECODE_BATCH, args.steps, min(args.warmup, 50), wms))
     # the query projection fused ahead of the indexer
-    line["secondary"].append(time_projection(PROJECTION, args.steps, min(args.warmup, 50)))
+    line["secondary"].append(time_projection(PROJECTION, args.steps, min(args.warmup, 50), wms))
     for name in (ATTN_WORKLOAD, *ATTN_SECONDARY):
-        line["secondary"].append(time_attention(name, args.steps, min(args.warmup, 50)))
+        line["secondary"].append(time_attention(name, args.steps, min(args.warmup, 50), wms))
+    # bracketing control: the headline again, after everything else
+    ctl = time_workload(HEADLINE, args.steps, args.warmup, wms)
+    line["control_rerun"] = {"workload": HEADLINE, "ms_per_step": ctl["ms_per_step"],
+                             "value": ctl["pairs_per_s"], "step_stats": ctl["step_stats"],
+                             "drift_vs_first": ctl["ms_per_step"] / head["ms_per_step"] - 1.0}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(HEADLINE)
     print(json.dumps(line))
