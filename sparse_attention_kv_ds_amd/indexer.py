@@ -371,34 +371,12 @@ def sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, *, window: i
     [N, D], k_local/v_local [L, D] (fp16/bf16 or their raw bits), idx [T, topk]
     int32, pos [T] int32, all contiguous on one device; returns out [T, HA, D]
     float32.  Work is enqueued on torch's current stream of that device."""
-    import torch
-    dev = q.device
-    T, HA, D = q.shape
-    N, L = k_pool.shape[0], k_local.shape[0]
+    T, HA, D, code, out, stream = _attention_args(q, k_pool, v_pool, k_local, v_local, idx, pos,
+                                                  dtype, out)
     topk = idx.shape[1] if idx.dim() == 2 else 0
-    if dtype is None:
-        dtype = q.dtype
-    code = _dtype_code(dtype)
-    for name, t_ in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("k_local", k_local),
-                     ("v_local", v_local), ("idx", idx), ("pos", pos)):
-        if t_.device != dev or not t_.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
-    for name, t_ in (("k_pool", k_pool), ("v_pool", v_pool), ("k_local", k_local),
-                     ("v_local", v_local)):
-        if t_.element_size() != 2 or (t_.numel() and tuple(t_.shape[1:]) != (D,)):
-            raise ValueError(f"{name} must be [rows, {D}] with 16-bit elements")
-    if idx.dtype != torch.int32 or pos.dtype != torch.int32 or tuple(pos.shape) != (T,):
-        raise ValueError("idx [T, topk] and pos [T] must be int32")
-    if out is None:
-        out = torch.empty((T, HA, D), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-
-    def ptr(t_):
-        return t_.data_ptr() if t_.numel() else None
-
-    st = ds_sparse_attention(ptr(q), ptr(k_pool), ptr(v_pool), ptr(k_local), ptr(v_local),
-                             ptr(idx), pos.data_ptr(), T, N, L, HA, D, code, topk, window,
-                             float(scale), out.data_ptr(), stream)
+    st = ds_sparse_attention(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_local), _ptr(v_local),
+                             _ptr(idx), pos.data_ptr(), T, k_pool.shape[0], k_local.shape[0], HA,
+                             D, code, topk, window, float(scale), out.data_ptr(), stream)
     if st != DS_OK:
         raise IndexerError(st, "ds_sparse_attention")
     return out

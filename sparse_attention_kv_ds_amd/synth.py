@@ -18,9 +18,9 @@ Draw order for one workload, from numpy.random.default_rng(seed): q, then k,
 then w (for power-of-two weights: the signs, then the exponents).
   * "int":   q, k integers uniform on {-4..4}, stored exactly in fp16;
              w = (+1 or -1) * 2^-n with n uniform on {0,1,2,3}, float32.
-  * "gauss": q, k = N(0,1) / sqrt(128) drawn in float64, rounded to nearest
-             even into float32 and then into the storage type (fp16 or
-             bf16); w uniform on [0, 1) drawn as float32.
+  * "gauss": q, k = N(0,1) / sqrt(128) drawn in float64 and rounded once, to
+             nearest even, into the storage type (fp16 or bf16); w uniform on
+             [0, 1) drawn as float32.
 Positions are consecutive: pos = p0, p0+1, ..., p0+T-1 (int32).
 """
 from __future__ import annotations
@@ -106,22 +106,28 @@ def make_decode_batch(name: str):
     return {"q": np.stack(qs), "k": np.stack(ks), "w": np.stack(ws), "pos": pos, "wl": wl, "B": B}
 
 
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to nearest-even bfloat16; return the raw uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+# significand bits (with the leading one), least normal exponent and largest
+# finite value of the two storage types
+_FORMATS = {"f16": (11, -14, 65504.0), "bf16": (8, -126, 3.3895313892515355e38)}
 
 
 def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values to nearest-even float32, then into fp16 / bf16 storage;
-    return the raw uint16 bits."""
-    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    """Round float64 values to the nearest fp16 / bf16 value (ties to even, one
+    rounding, overflow to infinity); return the raw uint16 bits."""
+    if dtype not in _FORMATS:
+        raise ValueError(dtype)
+    p, emin, fmax = _FORMATS[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, e2 = np.frexp(x)                          # |x| = m 2^e2, m in [0.5, 1)
+        e = np.maximum(e2.astype(np.int64) - 1, emin)  # exponent of x's binade (subnormals: emin)
+        ulp = np.ldexp(1.0, (e - (p - 1)).astype(np.int32))
+        r = np.rint(x / ulp) * ulp                   # exact: scaling by powers of two
+        r = np.where(np.abs(r) > fmax, np.copysign(np.inf, x), r)
+        r = np.where(np.isfinite(x), r, x)
     if dtype == "f16":
-        return x32.astype(np.float16).view(np.uint16)
-    if dtype == "bf16":
-        return f32_to_bf16_bits(x32)
-    raise ValueError(dtype)
+        return r.astype(np.float16).view(np.uint16)  # exact: r is an fp16 value
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def draw(T: int, N: int, H: int, D: int, dtype: str, dist: str, seed: int = 0,

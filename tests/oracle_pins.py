@@ -632,12 +632,19 @@ def pin_attn_all_constant_keys_mean(orc: Oracle):
                 (W, p, got[t, 0, 0], float(want))
 
 
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to nearest-even bfloat16 on the bit patterns (add
+    0x7FFF plus the lowest kept bit, then drop the low half); raw uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def pin_round_to_storage_types(orc: Oracle):
     """Rounding a double into fp16 / bf16 (the step after the query projection):
     every finite pattern round-trips; every midpoint between neighbours rounds
     to the even pattern and a nudge either way picks the nearer one -- checked
     against numpy's float16 conversion, and for bf16 against rounding the exact
-    float32 value of the midpoint (synth's bit-level converter)."""
+    float32 value of the midpoint (the bit-level converter below)."""
     f16 = np.arange(0x7C00, dtype=np.uint16)            # +0 .. largest finite
     vals = f16.view(np.float16).astype(np.float64)
     for b, v in zip(f16[::37], vals[::37]):
@@ -657,7 +664,7 @@ def pin_round_to_storage_types(orc: Oracle):
     for i in range(0, len(bmids), 17):
         m = bmids[i]
         for x in (m, np.nextafter(m, 0.0), np.nextafter(m, np.inf)):
-            want = int(synth.f32_to_bf16_bits(np.array([x], dtype=np.float32))[0]) \
+            want = int(f32_to_bf16_bits(np.array([x], dtype=np.float32))[0]) \
                 if float(np.float32(x)) == x else None
             if want is not None:
                 assert orc.double_to_bf16(x) == want, (x, hex(orc.double_to_bf16(x)), hex(want))
@@ -680,7 +687,7 @@ def pin_project_q_exact(orc: Oracle):
                         dtype="f16")
     assert np.array_equal(got, exact.astype(np.float16).view(np.uint16))
     got = orc.project_q(synth.to_bits(xi, "bf16"), synth.to_bits(wi, "bf16"), dtype="bf16")
-    assert np.array_equal(got, synth.f32_to_bf16_bits(exact.astype(np.float32)))
+    assert np.array_equal(got, f32_to_bf16_bits(exact.astype(np.float32)))
     xg = synth.to_bits(rng.standard_normal((T, 64)), "f16")
     wg = synth.to_bits(rng.standard_normal((O, 64)) * 0.1, "f16")
     ref = (xg.view(np.float16).astype(np.float64) @ wg.view(np.float16).astype(np.float64).T)
