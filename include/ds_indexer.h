@@ -115,6 +115,35 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
                           int32_t *out, void *stream);
 
 /*
+ * ds_indexer_score_topk without a handle and without allocating anything, for
+ * callers that cannot allocate device memory: work captured into a HIP graph,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same operation,
+ * arguments, layout, kernels and results as ds_indexer_score_topk; the head
+ * count, head dim and dtype come as arguments (n_heads, head_dim, dtype as in
+ * ds_indexer_create) and the call runs on the CURRENT HIP device, where every
+ * pointer must live.
+ *
+ * Its scratch is one fixed device array per GPU (in the library, held from the
+ * first call on that GPU until the process ends): 16,777,216 fp32 score
+ * entries (64 MiB) plus one sequence's selection lists (152 KiB).  Limits:
+ *   topk <= 2048, T <= INT_MAX, and, unless N <= topk or the single-token
+ *   path applies (T == 1 and N <= 1048576), T * round_up(N, 64) <= 16777216
+ *   (e.g. 2048 tokens x 8192 rows); beyond them DS_ERR_CAPACITY.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (two streams, two host threads) race and give wrong results; serialise
+ * them.  No kernel reads scratch that the same call did not write first, so
+ * nothing is cleared between calls.  No device memory is allocated or freed,
+ * and no host synchronisation happens.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED (heads, dim, dtype or
+ * rows outside the ranges ds_indexer_create accepts), DS_ERR_CAPACITY or
+ * DS_ERR_HIP.
+ */
+int ds_indexer_score_topk_noalloc(const void *q, const void *k, const float *w,
+                                  const int32_t *pos, int64_t T, int64_t N, int n_heads,
+                                  int head_dim, int dtype, int ratio, int topk, int32_t *out,
+                                  void *stream);
+
+/*
  * Batched decode: B independent sequences of one query token each, in one
  * call -- the single-token path (T == 1) for every sequence at once, so that
  * several sequences share one K stream across the GPU.  Each sequence's result

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libds_indexer.so")
-SOURCES = ["api.cpp", "scorer.hip", "topk.hip", "attention.hip", "qproj.hip"]
+SOURCES = ["api.cpp", "scorer.hip", "topk.hip", "attention.hip", "qproj.hip", "static_scratch.hip"]
 # Extra flags per source.  The scorer is built without NaN semantics: its
 # inputs are finite by contract, and with NaNs honoured every ReLU (fmaxf)
 # costs an extra canonicalising instruction.

@@ -108,7 +108,7 @@ hipEvent_t take_event(ds_indexer *ix)
 template <class F>
 hipError_t timed(ds_indexer *ix, int cls, F &&launch)
 {
-    if (!ix->timing)
+    if (!ix || !ix->timing)
         return launch(nullptr);
     dsi::Timing tm;
     tm.start = take_event(ix);
@@ -145,6 +145,57 @@ dsi::Problem problem(const ds_indexer *ix, const void *q, const void *k, const f
     p.D = ix->D;
     p.dtype = ix->dtype;
     return p;
+}
+
+// The device scratch one score + top-k call works in: score rows (ldS floats
+// per token) and the single-token path's partition lists.
+struct Work {
+    float *S;
+    long long ldS;
+    uint64_t *cand;
+    int *pcount;
+    uint64_t *pmin;
+    bool decode_ok; // the single-token kernels may be used (N small enough)
+};
+
+// The launches of one score + top-k call whose arguments have been checked
+// (T > 0).  ix only carries the per-kernel timing switch (NULL: no timing).
+hipError_t launch_score_topk(ds_indexer *ix, const Work &wk, const dsi::Problem &p, int topk,
+                             int32_t *out, hipStream_t s)
+{
+    const int T = p.T, N = p.N;
+    if (N <= topk) {
+        // every row of K fits in topk, so every token's visible rows do: the
+        // sequential rows, with no scorer and no selection launched
+        return timed(ix, T == 1 ? DS_KERNEL_DECODE_SELECT : DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
+            return dsi::launch_sequential_rows(p.pos, T, N, p.ratio, topk, out, s, tm);
+        });
+    }
+    hipError_t e;
+    if (T == 1 && wk.decode_ok) {
+        dsi::DecodeLists dl;
+        dl.kp = decode_kp(N, topk);
+        dl.cand = wk.cand;
+        dl.pcount = wk.pcount;
+        dl.pmin = wk.pmin;
+        e = timed(ix, DS_KERNEL_DECODE_SCORE, [&](dsi::Timing *tm) {
+            return dsi::launch_decode_scorer(p, topk, wk.S, dl, s, tm);
+        });
+        if (e == hipSuccess)
+            e = timed(ix, DS_KERNEL_DECODE_SELECT, [&](dsi::Timing *tm) {
+                return dsi::launch_decode_select(wk.S, p.pos, N, p.ratio, topk, dl, out, s, tm);
+            });
+    } else {
+        e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
+            return dsi::launch_prefill_scorer(p, topk, wk.S, wk.ldS, s, tm);
+        });
+        if (e == hipSuccess)
+            e = timed(ix, DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
+                return dsi::launch_topk_stream(wk.S, wk.ldS, p.pos, T, N, p.ratio, topk, out, s,
+                                               tm);
+            });
+    }
+    return e;
 }
 
 } // namespace
@@ -229,38 +280,63 @@ int ds_indexer_score_topk(ds_indexer *ix, const void *q, const void *k, const fl
     DeviceGuard g(ix->device);
     if (!g.ok)
         return DS_ERR_HIP;
-    hipStream_t s = (hipStream_t)stream;
-    const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
-    hipError_t e;
-    if (N <= topk) {
-        // every row of K fits in topk, so every token's visible rows do: the
-        // sequential rows, with no scorer and no selection launched
-        e = timed(ix, T == 1 ? DS_KERNEL_DECODE_SELECT : DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
-            return dsi::launch_sequential_rows(pos, (int)T, (int)N, ratio, topk, out, s, tm);
-        });
-    } else if (T == 1 && ix->decode_ok) {
-        dsi::DecodeLists dl;
-        dl.kp = decode_kp(N, topk);
-        dl.cand = ix->cand;
-        dl.pcount = ix->pcount;
-        dl.pmin = ix->pmin;
-        e = timed(ix, DS_KERNEL_DECODE_SCORE, [&](dsi::Timing *tm) {
-            return dsi::launch_decode_scorer(p, topk, ix->S, dl, s, tm);
-        });
-        if (e == hipSuccess)
-            e = timed(ix, DS_KERNEL_DECODE_SELECT, [&](dsi::Timing *tm) {
-                return dsi::launch_decode_select(ix->S, pos, (int)N, ratio, topk, dl, out, s, tm);
-            });
-    } else {
-        e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
-            return dsi::launch_prefill_scorer(p, topk, ix->S, ix->ldS, s, tm);
-        });
-        if (e == hipSuccess)
-            e = timed(ix, DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
-                return dsi::launch_topk_stream(ix->S, ix->ldS, pos, (int)T, (int)N, ratio, topk,
-                                               out, s, tm);
-            });
-    }
+    const Work wk{ix->S, ix->ldS, ix->cand, ix->pcount, ix->pmin, ix->decode_ok};
+    const hipError_t e = launch_score_topk(ix, wk, problem(ix, q, k, w, pos, T, N, ratio), topk,
+                                           out, (hipStream_t)stream);
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_indexer_score_topk_noalloc(const void *q, const void *k, const float *w,
+                                  const int32_t *pos, int64_t T, int64_t N, int n_heads,
+                                  int head_dim, int dtype, int ratio, int topk, int32_t *out,
+                                  void *stream)
+{
+    if (T < 0 || N < 0 || ratio < 1 || topk < 1)
+        return DS_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !w || !pos || !out))
+        return DS_ERR_INVALID_ARG;
+    if (T > 0 && N > 0 && !k)
+        return DS_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(pos, 4) ||
+        !aligned(out, 4))
+        return DS_ERR_INVALID_ARG;
+    if (!dsi::scorer_supported(n_heads, head_dim, dtype))
+        return DS_ERR_UNSUPPORTED;
+    if (N > INT_MAX - 64 || !dsi::scorer_rows_supported(n_heads, head_dim, N))
+        return DS_ERR_UNSUPPORTED;
+    // the fixed scratch: score rows for T * round_up(N, 64) <= kStaticScores
+    // (the single-token path needs N of them), then the partition lists
+    const long long ldS = (N + 63) / 64 * 64;
+    const bool decode = T == 1 && N <= kDecodeMaxRows;
+    if (topk > kMaxTopk || T > INT_MAX ||
+        (N > topk && !decode && T * ldS > dsi::kStaticScores))
+        return DS_ERR_CAPACITY;
+    if (T == 0)
+        return DS_OK;
+    int dev = 0;
+    void *base = nullptr;
+    if (hipGetDevice(&dev) != hipSuccess || dsi::static_scratch(dev, &base) != hipSuccess)
+        return DS_ERR_HIP;
+    unsigned char *b = static_cast<unsigned char *>(base);
+    Work wk;
+    wk.S = reinterpret_cast<float *>(b);
+    wk.ldS = ldS;
+    wk.cand = reinterpret_cast<uint64_t *>(b + dsi::kStaticScores * 4);
+    wk.pmin = wk.cand + dsi::kDecodeUnion;
+    wk.pcount = reinterpret_cast<int *>(wk.pmin + dsi::kDecodeMaxParts);
+    wk.decode_ok = N <= kDecodeMaxRows;
+    dsi::Problem p;
+    p.q = q;
+    p.k = k;
+    p.w = w;
+    p.pos = pos;
+    p.T = (int)T;
+    p.N = (int)N;
+    p.ratio = ratio;
+    p.H = n_heads;
+    p.D = head_dim;
+    p.dtype = dtype;
+    const hipError_t e = launch_score_topk(nullptr, wk, p, topk, out, (hipStream_t)stream);
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 

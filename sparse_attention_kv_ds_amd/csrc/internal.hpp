@@ -73,6 +73,18 @@ constexpr int kDecodeMaxParts = kDecodeUnion / 8;
 // slots and kDecodeMaxParts partition entries of the workspace)
 constexpr int kDecodeMaxBatch = 64;
 
+// The allocation-free entry point's scratch (static_scratch.hip): one device
+// array per GPU holding kStaticScores fp32 score entries (64 MiB), then one
+// sequence's partition lists (kDecodeUnion keys, kDecodeMaxParts smallest
+// keys and counts).
+constexpr long long kStaticScores = 1LL << 24;
+constexpr size_t kStaticScratchBytes =
+    (size_t)kStaticScores * 4 + (size_t)kDecodeUnion * 8 + (size_t)kDecodeMaxParts * (8 + 4);
+
+// The address of that array on `device`, which must be the current device;
+// looked up once per device and kept until the process ends.
+hipError_t static_scratch(int device, void **ptr);
+
 // Scores of every token with more than min_rows visible rows, written to
 // S[t * ldS + j] for j < n_t (other entries untouched).
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,

@@ -35,7 +35,8 @@ KERNEL_CLASS_NAMES = ("score", "select", "decode_score", "decode_select", "proje
 EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
            "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all",
-           "ds_indexer_score_topk_batch", "ds_indexer_project_q", "ds_indexer_project_score_topk")
+           "ds_indexer_score_topk_batch", "ds_indexer_project_q", "ds_indexer_project_score_topk",
+           "ds_indexer_score_topk_noalloc")
 
 
 class IndexerError(RuntimeError):
@@ -63,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.ds_indexer_project_q.argtypes = [P, P, P, I64, I64, P, P]
     lib.ds_indexer_project_score_topk.restype = I
     lib.ds_indexer_project_score_topk.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, P, P]
+    lib.ds_indexer_score_topk_noalloc.restype = I
+    lib.ds_indexer_score_topk_noalloc.argtypes = [P, P, P, P, I64, I64, I, I, I, I, I, P, P]
     lib.ds_indexer_score_topk_batch.restype = I
     lib.ds_indexer_score_topk_batch.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P]
     lib.ds_indexer_destroy.restype = None
@@ -104,6 +107,12 @@ def ds_indexer_create(device: int, n_heads: int, head_dim: int, dtype: int, max_
 
 def ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream) -> int:
     return _lib.ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream)
+
+
+def ds_indexer_score_topk_noalloc(q, k, w, pos, T, N, n_heads, head_dim, dtype, ratio, topk,
+                                  out, stream) -> int:
+    return _lib.ds_indexer_score_topk_noalloc(q, k, w, pos, T, N, n_heads, head_dim, dtype,
+                                              ratio, topk, out, stream)
 
 
 def ds_indexer_project_q(handle, x, wq, T, d_in, q, stream) -> int:

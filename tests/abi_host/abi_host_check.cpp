@@ -287,6 +287,43 @@ void timing_checks(ds_indexer *ix)
     CHECK(fake::launches.size() == 2 && !fake::launches[0].timed && !fake::launches[1].timed);
 }
 
+void noalloc_checks()
+{
+    // no handle: the heads, dim and dtype are arguments; scratch is the fixed array
+    auto call = [&](const void *q, const void *k, int64_t T, int64_t N, int H, int D, int dt,
+                    int topk, int32_t *out) {
+        return ds_indexer_score_topk_noalloc(q, k, W, POS, T, N, H, D, dt, 4, topk, out, nullptr);
+    };
+    const int allocs = fake::live_allocations;
+    REJECT(DS_ERR_INVALID_ARG, call(Q, K, -1, 4096, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_INVALID_ARG, call(Q, K, 4, -1, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_INVALID_ARG, call(Q, K, 4, 4096, 64, 128, DS_F16, 0, OUT));
+    REJECT(DS_ERR_INVALID_ARG, call(nullptr, K, 4, 4096, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_INVALID_ARG, call(Q, nullptr, 4, 4096, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_INVALID_ARG, call(Q, K, 4, 4096, 64, 128, DS_F16, 512, nullptr));
+    REJECT(DS_ERR_INVALID_ARG, call(off(Q, 8), K, 4, 4096, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_INVALID_ARG, call(Q, K, 4, 4096, 64, 128, DS_F16, 512, off(OUT, 2)));
+    REJECT(DS_ERR_UNSUPPORTED, call(Q, K, 4, 4096, 48, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_UNSUPPORTED, call(Q, K, 4, 4096, 64, 128, 9, 512, OUT));
+    REJECT(DS_ERR_UNSUPPORTED, call(Q, K, 4, 8388481, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_CAPACITY, call(Q, K, 4, 4096, 64, 128, DS_F16, 2049, OUT));
+    // score rows beyond the fixed 2^24 entries
+    REJECT(DS_ERR_CAPACITY, call(Q, K, 2048, 8193, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_CAPACITY, call(Q, K, 2049, 8192, 64, 128, DS_F16, 512, OUT));
+    REJECT(DS_ERR_CAPACITY, call(Q, K, 1, 16777217, 64, 32, DS_F16, 512, OUT));
+    ACCEPT(({}), call(Q, K, 0, 4096, 64, 128, DS_F16, 512, OUT));
+    ACCEPT(({"prefill_scorer", "topk_stream"}), call(Q, K, 2048, 8192, 64, 128, DS_F16, 512, OUT));
+    ACCEPT(({"prefill_scorer", "topk_stream"}), call(Q, K, 4, 4096, 4, 32, DS_BF16, 100, OUT));
+    // one token: the decode kernels up to their row limit, the prefill ones beyond
+    ACCEPT(({"decode_scorer", "decode_select"}), call(Q, K, 1, 1 << 20, 64, 128, DS_F16, 512, OUT));
+    ACCEPT(({"prefill_scorer", "topk_stream"}),
+           call(Q, K, 1, (1 << 20) + 1, 64, 128, DS_F16, 512, OUT));
+    // every row fits: no scratch needed beyond the limits
+    ACCEPT(({"sequential_rows"}), call(Q, K, 100000, 300, 64, 128, DS_F16, 512, OUT));
+    CHECK(fake::live_allocations == allocs); // nothing allocated
+    CHECK(fake::scratch_lookups > 0);
+}
+
 void attention_checks()
 {
     auto call = [&](int64_t T, const int32_t *idx, int topk, float scale, float *out) {
@@ -330,6 +367,7 @@ int main()
     scores_checks(ix, big);
     projection_checks(ix);
     timing_checks(ix);
+    noalloc_checks();
     attention_checks();
     ds_indexer_destroy(ix);
     ds_indexer_destroy(wide);

@@ -17,6 +17,7 @@ int live_allocations = 0;
 int device_count = 1;
 bool fail_device_count = false;
 bool fail_launches = false;
+int scratch_lookups = 0;
 
 void reset()
 {
@@ -170,6 +171,18 @@ hipError_t launch_qproj(const void *, const void *, int T, int K, int O, int, vo
 hipError_t launch_fill(float *, long long n, float, hipStream_t)
 {
     return fake::record("fill", n, 0, 0, 1, nullptr);
+}
+
+hipError_t static_scratch(int device, void **ptr)
+{
+    // (one block the size of the library's array, reserved once)
+    static void *block = aligned_alloc(256, (kStaticScratchBytes + 255) / 256 * 256);
+    *ptr = nullptr;
+    if (device < 0 || device >= fake::device_count || !block)
+        return hipErrorInvalidDevice;
+    fake::scratch_lookups++;
+    *ptr = block;
+    return hipSuccess;
 }
 
 hipError_t launch_sparse_attention(const AttnProblem &a, hipStream_t, Timing *tm)

@@ -25,6 +25,7 @@ extern int live_allocations;    // hipMalloc'd blocks not yet freed
 extern int device_count;        // what hipGetDeviceCount reports
 extern bool fail_device_count;  // hipGetDeviceCount returns an error
 extern bool fail_launches;      // every launcher returns an error
+extern int scratch_lookups;     // static_scratch calls
 
 void reset();
 

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
                                            "ds_indexer_timing_read", "ds_sparse_attention",
                                            "ds_sparse_attention_all",
                                            "ds_indexer_score_topk_batch", "ds_indexer_project_q",
-                                           "ds_indexer_project_score_topk"])
+                                           "ds_indexer_project_score_topk",
+                                           "ds_indexer_score_topk_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(ix):
