@@ -282,9 +282,10 @@ __device__ __forceinline__ uint64_t band_extreme(const uint32_t (&hi)[E], const 
 // k <= #{keys >= L} <= k + slack (a bound, not necessarily a key).  With
 // slack == 0: returns the k-th largest key itself.
 //
-// The search starts from the bits that the smallest and largest high words
-// (scores) share, then bisects the high word keeping [v, u) with at least k
-// keys at or above v and fewer than k at or above u.  It stops early within
+// The search bisects the high word (the score) between the smallest and the
+// largest one, keeping [v, u) with at least k keys at or above v and fewer
+// than k at or above u (a band started at the keys' own range needs fewer
+// steps than one aligned to a power of two around it).  It stops early within
 // the slack, or (exact case) as soon as the k-th key is the largest or the
 // smallest of the band [v, u), which one reduction then finds.  Only equal
 // scores across the boundary need the low word (the row), bisected from the
@@ -303,19 +304,16 @@ __device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const 
             mx = max(mx, hi[s]);
         }
     red.minmax(mn, mx);
-    // every key's high word is in [v, u), v <= mn, mx < u
-    const int top = mn == mx ? -1 : 31 - __builtin_clz(mn ^ mx);
-    const uint32_t span = top < 0 ? 1u : (2u << top); // 0 when top == 31 (whole range)
-    const uint32_t v0 = top < 0 ? mn : (mn & ~(span - 1u));
-    uint32_t v = v0;
-    uint64_t u = (uint64_t)v0 + (span ? span : (1ull << 32));
+    // every key's high word is in [v, u): the band starts as [mn, mx] itself
+    uint32_t v = mn;
+    uint64_t u = (uint64_t)mx + 1;
     int cv = tot; // #{keys with high word >= v}
     int cu = 0;   // #{keys with high word >= u}
 #pragma unroll 1
-    for (int b = top; b >= 0; --b) {
+    while (u - v > 1) {
         if (slack > 0 ? cv <= k + slack : (k - cu == 1 || k == cv))
             break;
-        const uint32_t c = v | (1u << b);
+        const uint32_t c = (uint32_t)(v + ((u - v) >> 1)); // v < c < u
         const int cc = red.sum(count_hi_ge<E>(hi, nsl, c));
         if (cc >= k) {
             v = c;
