@@ -599,6 +599,30 @@ def test_long_rows_with_a_top_run_bit_exact(lib, orc):
                    dtype="f16", ratio=ratio, topk=topk, where=f"top run N={N}")
 
 
+@pytest.mark.parametrize("N,topk", [(8192, 512), (16384, 512), (5000, 100), (2048, 512)])
+def test_concentrated_and_tied_rows_exact(lib, orc, N, topk):
+    """64 index heads, rows of 2048..16384: scores rising with the row (every
+    top row at the end of the row, against the sampled starting threshold),
+    all-equal scores (a pure tie-break by row: the top rows all at the start),
+    a ReLU that cuts every score to 0, and one token of ordinary integer data.
+    Bit-exact against the oracle."""
+    H, D, ratio = 64, 128, 1
+    rng = np.random.default_rng(N + topk)
+    kf = np.zeros((N, D))
+    kf[:, 0] = np.floor(np.arange(N) / 8)                 # rising, exact in fp16 up to 2048
+    kf[:, 1:] = rng.integers(-1, 2, size=(N, D - 1))
+    qf = np.zeros((4, H, D))
+    qf[0, :, 0] = 1                                       # rising scores
+    qf[2, :, :] = rng.integers(-4, 5, size=(H, D))         # ordinary integer data
+    qf[3, :, 0] = -1                                      # ReLU cuts everything: all scores 0
+    w = np.ones((4, H), np.float32)
+    w[2] = np.ldexp(1.0, -rng.integers(0, 4, size=H)).astype(np.float32)
+    pos = np.array([N - 1, N - 1, N + 3, N - 1], np.int32)  # token 1: q = 0, all scores 0
+    say(f"rising / ties / integer / relu-cut rows, N={N} k={topk}")
+    exact_case(lib, orc, synth.to_bits(qf, "f16"), synth.to_bits(kf, "f16"), w, pos, H=H, D=D,
+               dtype="f16", ratio=ratio, topk=topk, where=f"concentrated rows N={N} k={topk}")
+
+
 def test_decode_at_the_row_limit(lib, orc):
     """Single-token decode at the most rows the decode path takes (2048 partitions
     of 512 rows = 1048576 rows, 256 MiB of K): the merge holds the 16384-key union
