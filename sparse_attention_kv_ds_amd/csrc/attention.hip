@@ -20,7 +20,10 @@
 // in blocks of 32: the local rows first (their last block padded), then the
 // index list in order, so that every block reads one tensor pair.  Each
 // block's K and V rows go straight from memory into LDS (buffer loads with the
-// LDS bit), the next block's while the current one is computed.
+// LDS bit): V of the next block during the whole of the current one, K of the
+// next block once every wave holds the current block's K fragments.  One K
+// stage and two V stages (24 KiB at D = 128) plus the index list leave room
+// for six work-groups, three waves per SIMD, per CU.
 //   * S^T = K_blk . Q^T on the 32x32x16 MFMA: each lane then holds 16 keys of
 //     one head, so the softmax statistics of a head live in one lane pair.
 //   * Online softmax in base 2 with a lazy rescale: the running exponent base
@@ -91,8 +94,9 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
     }
 }
 
-template <int WAVES, int D, int DT>
-__global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
+// IDS: capacity of the index list in LDS (entries; at least 32 ceil(topk / 32))
+template <int WAVES, int D, int DT, int IDS>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void sparse_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kp,
     const uint16_t *__restrict__ vp, const uint16_t *__restrict__ kl,
     const uint16_t *__restrict__ vl, const int32_t *__restrict__ idx,
@@ -106,16 +110,26 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     constexpr int RPL = 64 / CPR;         // rows per 1 KiB load
     constexpr int BLK_B = 32 * D * 2;     // bytes of 32 rows
     constexpr int LPB = BLK_B / 1024;     // 1 KiB loads per block and tensor
+    // the row stored for an empty slot: its rows start at byte 2^31, past
+    // every tensor (each holds fewer than 2^30 / D rows, under 2^31 bytes),
+    // and its 16-byte loads end well below 2^32
+    constexpr uint32_t kNoRow = 0x80000000u / (2 * D);
 
-    __shared__ int32_t ids[kAttnMaxTopk];
+    __shared__ int32_t ids[IDS];
     // one array per stage and tensor, so that the compiler can tell that the
     // loads into one stage do not touch the fragment reads of the other
     __shared__ __attribute__((aligned(1024))) unsigned char ks0[BLK_B];
-    __shared__ __attribute__((aligned(1024))) unsigned char ks1[BLK_B];
     __shared__ __attribute__((aligned(1024))) unsigned char vs0[BLK_B];
     __shared__ __attribute__((aligned(1024))) unsigned char vs1[BLK_B];
 
-    const int t = blockIdx.x;
+    // work-groups go to the 8 XCDs in turn: give each XCD one contiguous run
+    // of tokens, so that the overlapping local windows of neighbouring tokens
+    // meet in the same L2
+    int t;
+    {
+        const int T = gridDim.x, w = blockIdx.x, x = w & 7, q8 = T >> 3, r8 = T & 7;
+        t = x * q8 + min(x, r8) + (w >> 3);
+    }
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int col = lane & 31;
@@ -145,24 +159,27 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
     const int i0 = wave * NI;
     const int pc = lane % CPR;
 
-    // this lane's row of each of its loads of block b, -1 for an empty slot
-    // (the pooled rows come from the index list in one round of LDS reads)
-    auto block_rows = [&](int b, int (&row)[NI]) {
+    // this lane's row of each of its loads of block b, kNoRow for an empty
+    // slot (the pooled rows come from the index list in one round of LDS
+    // reads).  kNoRow * CPR * 16 lies past every tensor's range, so an empty
+    // slot's load is dropped by the range check with no compare of its own.
+    auto block_rows = [&](int b, uint32_t (&row)[NI]) {
         if (b < nb_loc) {
 #pragma unroll
             for (int n = 0; n < NI; ++n) {
                 const int k = 32 * b + (i0 + n) * RPL + lane / CPR;
-                row[n] = k < n_loc ? lo + k : -1;
+                row[n] = k < n_loc ? (uint32_t)(lo + k) : kNoRow;
             }
         } else {
-            const int32_t *e = ids + 32 * (b - nb_loc) + i0 * RPL + lane / CPR;
+            const uint32_t *e =
+                reinterpret_cast<const uint32_t *>(ids) + 32 * (b - nb_loc) + i0 * RPL + lane / CPR;
 #pragma unroll
             for (int n = 0; n < NI; ++n)
                 row[n] = e[n * RPL];
         }
     };
     // this wave's loads of block b of K (isk) or V, rows `row`, into stage st
-    auto issue = [&](int b, const int (&row)[NI], unsigned char *st, bool isk) {
+    auto issue = [&](int b, const uint32_t (&row)[NI], unsigned char *st, bool isk) {
         const bool local = b < nb_loc;
         const uint16_t *base = pick(isk, pick(local, kl, kp), pick(local, vl, vp));
         const auto r = make_rsrc(base, local ? bytes_l : bytes_p);
@@ -170,17 +187,11 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         for (int n = 0; n < NI; ++n) {
             const int rr = (i0 + n) * RPL + lane / CPR; // row slot in the block
             const int c = isk ? pc ^ ((rr / (16 / CPR)) % CPR) : pc ^ (4 * vswz<D>(rr));
-            const uint32_t off = row[n] >= 0 ? ((uint32_t)row[n] * CPR + c) * 16 : kOffNone;
-            buf_load16_lds(r, st + (i0 + n) * 1024, off);
+            buf_load16_lds(r, st + (i0 + n) * 1024, row[n] * (CPR * 16) + (uint32_t)c * 16);
         }
     };
-    auto load_rows = [&](int b, unsigned char *st, bool isk) {
-        int row[NI];
-        block_rows(b, row);
-        issue(b, row, st, isk);
-    };
     auto load_block = [&](int b, unsigned char *kst, unsigned char *vst) {
-        int row[NI];
+        uint32_t row[NI];
         block_rows(b, row);
         issue(b, row, kst, true);
         issue(b, row, vst, false);
@@ -215,16 +226,20 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         voffd[d] = ((uint32_t)(4 * (g >> 1) + (Lg >> 2)) * D + 32 * (d ^ vsw_lane) + 16 * (g & 1) +
                     4 * (Lg & 3)) * 2;
 
-    auto compute_block = [&](int b, const unsigned char *kst, const unsigned char *vst) {
-        // valid keys of the block (bit r), the same in every lane
+    // block b from K stage kst and V stage vst; k_done() runs once this
+    // wave's K fragments are in registers
+    auto compute_block = [&](int b, const unsigned char *kst, const unsigned char *vst,
+                             auto &&k_done) {
+        // valid keys of the block (bit r), the same in every lane; a block with
+        // no valid key goes through with every score -inf (its p are all 0):
+        // an early exit here would give the accumulators a second home across
+        // the loop and cost registers
         bool valid;
         if (b < nb_loc)
             valid = 32 * b + col < n_loc;
         else
-            valid = ids[32 * (b - nb_loc) + col] >= 0;
+            valid = (uint32_t)ids[32 * (b - nb_loc) + col] != kNoRow;
         const uint64_t vm = ballot(lane < 32 && valid);
-        if (vm == 0)
-            return; // nothing to attend in this block
         // S^T: lane holds head col, keys 8 (i / 4) + 4 hf + i % 4
         f32x16 s = f32x16{};
 #pragma unroll
@@ -232,6 +247,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             const u32x4 kf = *reinterpret_cast<const u32x4 *>(kst + koff[kk]);
             s = mfma32<DT>(kf, qf[kk], s);
         }
+        k_done();
         // empty key slots (partial blocks only) score -inf
         if ((uint32_t)vm != 0xFFFFFFFFu) {
             const uint32_t mh = (uint32_t)(vm >> (4 * hf));
@@ -302,7 +318,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
         qf[kk] = buf_load16(rq, ((uint32_t)col * D + kk * 16 + hf * 8) * 2);
-    // entries outside [0, N) and the padding become -1 (empty slots); with
+    // entries outside [0, N) and the padding become kNoRow (empty slots); with
     // ratio > 0 the list is every pooled row the token can see, 0 .. n-1
     const int n_all = ratio > 0 ? visible_rows(p, ratio, N) : 0;
     for (int e = threadIdx.x; e < 32 * nb_pool; e += WAVES * 64) {
@@ -311,7 +327,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             j = e < n_all ? e : -1;
         else
             j = e < topk ? idx[(long long)t * topk + e] : -1;
-        ids[e] = (uint32_t)j < (uint32_t)N ? j : -1;
+        ids[e] = (uint32_t)j < (uint32_t)N ? j : (int32_t)kNoRow;
     }
 
 
@@ -321,20 +337,32 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
             load_block(0, ks0, vs0);
         wait_vmcnt<0>(); // block 0 and the query fragments
         __syncthreads();
-        // two blocks per iteration, so that every stage offset is a constant
-        for (int b = 0;;) {
-            if (b + 1 < nb)
-                load_block(b + 1, ks1, vs1);
-            compute_block(b, ks0, vs0);
+        // block b: V of block b + 1 loads into the other V stage from the
+        // start; K of block b + 1 into the one K stage once every wave holds
+        // the K fragments of block b (the barrier in the hook)
+        auto step = [&](int b, const unsigned char *vc, unsigned char *vn) {
+            const bool more = b + 1 < nb;
+            uint32_t row[NI];
+            if (more) {
+                block_rows(b + 1, row);
+                issue(b + 1, row, vn, false);
+            }
+            compute_block(b, ks0, vc, [&] {
+                lds_barrier();
+                if (more)
+                    issue(b + 1, row, ks0, true);
+            });
             wait_vmcnt<0>();
             lds_barrier();
+        };
+        // two blocks per iteration, so that both V stages are named arrays
+        // and the compiler can tell the loads into one from the reads of the
+        // other
+        for (int b = 0;;) {
+            step(b, vs0, vs1);
             if (++b >= nb)
                 break;
-            if (b + 1 < nb)
-                load_block(b + 1, ks0, vs0);
-            compute_block(b, ks1, vs1);
-            wait_vmcnt<0>();
-            lds_barrier();
+            step(b, vs1, vs0);
             if (++b >= nb)
                 break;
         }
@@ -357,18 +385,26 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attention_kernel(
         }
 }
 
+template <int WAVES, int D, int DT, int IDS>
+hipError_t attn_launch(const AttnProblem &a, float scale_log2, hipStream_t st, Timing *tm)
+{
+    return launch_kernel(sparse_attention_kernel<WAVES, D, DT, IDS>, dim3(a.T), dim3(WAVES * 64),
+                         0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
+                         a.L, a.topk, a.ratio, a.window, scale_log2, a.out);
+}
+
 template <int WAVES, int D>
 hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
 {
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    // the index list, padded to whole blocks of 32
+    // the index list, padded to whole blocks of 32: a short list keeps the
+    // LDS of a work-group at 26 KiB (D = 128), six per CU
+    const bool small = a.topk <= 512;
     if (a.dtype == kF16)
-        return launch_kernel(sparse_attention_kernel<WAVES, D, kF16>, dim3(a.T), dim3(WAVES * 64),
-                             0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos,
-                             a.N, a.L, a.topk, a.ratio, a.window, scale_log2, a.out);
-    return launch_kernel(sparse_attention_kernel<WAVES, D, kBF16>, dim3(a.T), dim3(WAVES * 64),
-                         0, st, tm, true, true, a.q, a.kp, a.vp, a.kl, a.vl, a.idx, a.pos, a.N,
-                         a.L, a.topk, a.ratio, a.window, scale_log2, a.out);
+        return small ? attn_launch<WAVES, D, kF16, 512>(a, scale_log2, st, tm)
+                     : attn_launch<WAVES, D, kF16, kAttnMaxTopk>(a, scale_log2, st, tm);
+    return small ? attn_launch<WAVES, D, kBF16, 512>(a, scale_log2, st, tm)
+                 : attn_launch<WAVES, D, kBF16, kAttnMaxTopk>(a, scale_log2, st, tm);
 }
 
 } // namespace
