@@ -35,6 +35,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-ms M]
                        (defaults K = 50, W = 200, M = 300)
        python bench.py --only prefill32k|prefill64k|decode1m|prefill2k|decode1m_b8|qproj32k|attn32k|attn32k_r128
                                                                  (one workload, for profilers)
+       python bench.py --phases WORKLOAD                        (per-phase durations from the
+                       timestamped build, libds_indexer_stamps.so)
        python bench.py --copy-calibration                       (plain copy kernel, for counters)
        python bench.py --ceilings                               (vendor GEMM and plain-copy
                        rates with the workloads' value distributions)
@@ -691,6 +693,118 @@ def summarize_trace(directory: str):
               f"{r[6]} | {r[7]} | {r[8]} | {r[9]} | {r[10]} |")
 
 
+def phases(name: str, warmup_ms: float = WARMUP_MS):
+    """Per-phase durations of one workload's kernels, from the timestamped build
+    of the library (libds_indexer_stamps.so, selected through DS_INDEXER_LIB
+    before the binding loads; its kernels record the GPU's 100 MHz real-time
+    counter at the phase boundaries listed in ds_indexer.h).  After the warm-up,
+    three calls are taken one at a time and their records read back; each line
+    gives a phase's 10th percentile / median / 90th percentile / maximum over
+    the work-groups or tokens, in microseconds."""
+    import ctypes
+    import numpy as np
+    import torch
+    from sparse_attention_kv_ds_amd import indexer, synth
+
+    if os.path.basename(indexer.LIB_PATH) != "libds_indexer_stamps.so":
+        raise SystemExit("--phases needs the stamps build (DS_INDEXER_LIB)")
+    dev = torch.device("cuda", 0)
+    rec = np.zeros(4096 * 8, dtype=np.uint64)
+
+    def read(unit):
+        st = indexer.ds_indexer_stamps_read(unit, rec.ctypes.data, rec.nbytes)
+        assert st == indexer.DS_OK, st
+        return rec.reshape(4096, 8).astype(np.int64)
+
+    def pct(x):
+        x = np.asarray(x, dtype=np.float64) / 100.0  # 100 MHz ticks -> us
+        return [round(float(v), 2) for v in (np.percentile(x, 10), np.median(x),
+                                              np.percentile(x, 90), x.max())]
+
+    out = {"workload": name, "unit": "us (p10, median, p90, max)", "calls": []}
+    if name in (ATTN_WORKLOAD, *ATTN_SECONDARY):
+        from sparse_attention_kv_ds_amd.indexer import sparse_attention, sparse_attention_all
+        d = synth.make_attention(name)
+        wl = d["wl"]
+        t = {k: torch.from_numpy(np.ascontiguousarray(d[k]).view(np.int16)).to(dev)
+             for k in ("q", "kp", "vp", "kl", "vl")}
+        idx = torch.from_numpy(d["idx"]).to(dev)
+        pos = torch.from_numpy(d["pos"]).to(dev)
+        o = torch.empty((wl.T, wl.HA, wl.DV), dtype=torch.float32, device=dev)
+
+        def call(i):
+            if wl.ratio > 0:
+                sparse_attention_all(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], pos,
+                                     ratio=wl.ratio, window=wl.window, scale=wl.scale,
+                                     dtype=wl.dtype, out=o)
+            else:
+                sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"], idx, pos,
+                                 window=wl.window, scale=wl.scale, dtype=wl.dtype, out=o)
+        warm_up(call, 20, warmup_ms, dev)
+        for c in range(3):
+            call(0)
+            r = read(indexer.DS_STAMPS_ATTENTION)[:wl.T]
+            t0 = r[:, 0].min()
+            nb = np.ceil(np.minimum(wl.window, wl.positions + 1) / 32) + np.ceil(
+                (wl.topk if wl.ratio == 0 else np.minimum(np.maximum((wl.positions + 1) // max(wl.ratio, 1), 0), wl.N)) / 32)
+            mid = np.linspace(0, (r[:, 3] - t0).max(), 64)
+            inflight = [int(((r[:, 0] - t0 <= x) & (r[:, 3] - t0 > x)).sum()) for x in mid[8:56]]
+            out["calls"].append({
+                "start": pct(r[:, 0] - t0), "first_block": pct(r[:, 1] - r[:, 0]),
+                "blocks": pct(r[:, 2] - r[:, 1]), "per_block": pct((r[:, 2] - r[:, 1]) / nb),
+                "output": pct(r[:, 3] - r[:, 2]), "token": pct(r[:, 3] - r[:, 0]),
+                "end": pct(r[:, 3] - t0), "tokens_in_flight_median": int(np.median(inflight))})
+    else:
+        from sparse_attention_kv_ds_amd.indexer import Indexer
+        d = synth.make(name)
+        wl = d["wl"]
+        q, k, w, pos = upload(d, dev)
+        ks = [k]
+        if wl.T == 1:
+            ks += [torch.roll(k, shifts=997 * (i + 1), dims=0).contiguous()
+                   for i in range(DECODE_K_BUFFERS - 1)]
+        o = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
+        ix = Indexer(wl.H, wl.D, wl.dtype, wl.topk, wl.T, wl.N, device=0)
+
+        def call(i):
+            ix.score_topk(q, ks[i % len(ks)], w, pos, wl.ratio, wl.topk, out=o)
+        try:
+            warm_up(call, 20, warmup_ms, dev)
+            for c in range(3):
+                call(c)
+                if wl.T == 1:
+                    n = min(max((int(wl.positions[0]) + 1) // wl.ratio, 0), wl.N)
+                    P = (n + 511) // 512
+                    r = read(indexer.DS_STAMPS_DECODE_SCORE)[:P]
+                    m = read(indexer.DS_STAMPS_MERGE)[0]
+                    t0 = r[:, 0].min()
+                    se = r[:, 2:6].max(axis=1)
+                    out["calls"].append({
+                        "scorer_start": pct(r[:, 0] - t0), "first_blocks": pct(r[:, 1] - r[:, 0]),
+                        "stream": pct(se - r[:, 1]), "partition_list": pct(r[:, 6] - se),
+                        "scorer_end": pct(r[:, 6] - t0),
+                        "merge": {"start_after_scorer_end": round((m[0] - r[:, 6].max()) / 100, 2),
+                                  "load_lists": round((m[1] - m[0]) / 100, 2),
+                                  "kth_key": round((m[2] - m[1]) / 100, 2),
+                                  "check": round((m[3] - m[2]) / 100, 2),
+                                  "output": round((m[4] - m[3]) / 100, 2)}})
+                else:
+                    n = np.clip((wl.positions.astype(np.int64) + 1) // wl.ratio, 0, wl.N)
+                    sel = n > wl.topk
+                    r = read(indexer.DS_STAMPS_TOPK)[:wl.T][sel]
+                    t0 = r[:, 0].min()
+                    out["calls"].append({
+                        "tokens": int(sel.sum()), "start": pct(r[:, 0] - t0),
+                        "starting_threshold": pct(r[:, 1] - r[:, 0]), "stream": pct(r[:, 2] - r[:, 1]),
+                        "final_selection": pct(r[:, 3] - r[:, 2]), "write": pct(r[:, 4] - r[:, 3]),
+                        "token": pct(r[:, 4] - r[:, 0]), "end": pct(r[:, 4] - t0)})
+        finally:
+            ix.close()
+    for i, c in enumerate(out["calls"]):
+        log(f"[phases] {name} call {i}: " + "; ".join(f"{k} {v}" for k, v in c.items()))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -703,6 +817,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
+    ap.add_argument("--phases", choices=["prefill8k", HEADLINE, "prefill64k", "decode1m",
+                                         ATTN_WORKLOAD, *ATTN_SECONDARY],
+                    help="per-phase durations from the timestamped build")
     ap.add_argument("--summarize-pmc")
     ap.add_argument("--summarize-trace")
     ap.add_argument("--summarize-mfma")
@@ -710,6 +827,12 @@ def main():
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     args = ap.parse_args()
 
+    if args.phases:
+        # the timestamped build, selected before anything loads the binding
+        os.environ.setdefault("DS_INDEXER_LIB", os.path.join(
+            ROOT, "sparse_attention_kv_ds_amd", "libds_indexer_stamps.so"))
+        print(json.dumps(phases(args.phases, args.warmup_ms)))
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
         return 0

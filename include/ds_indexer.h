@@ -38,6 +38,12 @@
  *     the clamp above defines every value (negative => nothing visible).
  *   - Inputs are assumed finite; for non-finite q, k or w the output is
  *     unspecified (but the call stays in bounds and terminates).
+ *   - Debugging: with DS_INDEXER_DEBUG set in the environment (to anything
+ *     but "" or "0"; read at every launch), each kernel launch is followed by
+ *     a synchronisation of the call's stream, so that a failing kernel makes
+ *     the call that launched it return DS_ERR_HIP.  That blocks the host
+ *     inside the call and is not allowed under stream capture: tests and
+ *     debugging only.
  */
 #ifndef DS_INDEXER_H
 #define DS_INDEXER_H
@@ -254,6 +260,42 @@ int ds_indexer_timing_read(ds_indexer *ix, double *ms, int64_t *launches);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ds_indexer_status_str(int status);
+
+/*
+ * Phase timestamps of the kernels' last launches, for profiling (how long each
+ * stage of a kernel takes, per work-group or token).  Only the separate stamps
+ * build of the library (libds_indexer_stamps.so, the same sources compiled
+ * with DSI_STAMPS) records them; every other build returns DS_ERR_UNSUPPORTED
+ * and touches nothing.
+ *
+ *   unit   which kernel's records:
+ *            DS_STAMPS_DECODE_SCORE  decode scorer, record = work-group of 512
+ *                                    rows (sequence b's at b * ceil(N / 512)):
+ *                                    0 start, 1 query and first K blocks in
+ *                                    LDS, 2..5 each wave's last block scored,
+ *                                    6 partition list written
+ *            DS_STAMPS_TOPK          prefill top-k, record = token: 0 start,
+ *                                    1 starting threshold, 2 row streamed,
+ *                                    3 final selection, 4 rows written
+ *            DS_STAMPS_MERGE         decode merge, record = sequence: 0 start,
+ *                                    1 lists loaded, 2 k-th key of the union,
+ *                                    3 exactness checked, 4 rows written
+ *                                    (5 instead after an exact re-stream)
+ *            DS_STAMPS_ATTENTION     sparse attention, record = token: 0 start,
+ *                                    1 first block and query landed, 2 last
+ *                                    block done, 3 output stores issued
+ *   host   host memory receiving `bytes` bytes: records of 8 uint64 entries,
+ *          each a reading of the GPU's 100 MHz real-time counter (entries a
+ *          launch did not write keep older values); at most 4096 records
+ *   bytes  at most 4096 * 64
+ *
+ * Synchronous: waits for the device's work to finish, then copies.  Returns
+ * DS_ERR_INVALID_ARG for an unknown unit, NULL host or bytes out of range,
+ * DS_ERR_HIP if the copy fails.
+ */
+enum { DS_STAMPS_DECODE_SCORE = 0, DS_STAMPS_TOPK = 1, DS_STAMPS_MERGE = 2,
+       DS_STAMPS_ATTENTION = 3 };
+int ds_indexer_stamps_read(int unit, void *host, int64_t bytes);
 
 /*
  * Sparse attention over the selected rows: the consumer of the indices.

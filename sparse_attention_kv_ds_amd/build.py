@@ -17,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libds_indexer.so")
+# the same sources with DSI_STAMPS: kernels also record phase timestamps
+# (ds_indexer_stamps_read); for the phase breakdowns only, never the product
+LIB_STAMPS = os.path.join(HERE, "libds_indexer_stamps.so")
 SOURCES = ["api.cpp", "scorer.hip", "topk.hip", "attention.hip", "qproj.hip", "static_scratch.hip"]
 # Extra flags per source.  The scorer is built without NaN semantics: its
 # inputs are finite by contract, and with NaNs honoured every ReLU (fmaxf)
@@ -36,19 +39,24 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, defines=()) -> None:
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
 
 
-def build_library(out: str = LIB) -> str:
-    """Compile every HIP source for gfx950 and link libds_indexer.so."""
+def build_library(out: str = LIB, stamps: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libds_indexer.so (with
+    stamps: the timestamped build, libds_indexer_stamps.so)."""
+    if stamps and out == LIB:
+        out = LIB_STAMPS
+    defines = ("DSI_STAMPS",) if stamps else ()
     with tempfile.TemporaryDirectory(prefix="dsi_build_") as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
         with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            list(ex.map(_compile, SOURCES, objs))
+            list(ex.map(lambda src, obj: _compile(src, obj, defines), SOURCES, objs))
         tmp_out = os.path.join(tmp, "libds_indexer.so")
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,3 +69,4 @@ def build_library(out: str = LIB) -> str:
 
 if __name__ == "__main__":
     print(build_library())
+    print(build_library(stamps=True))

@@ -604,6 +604,30 @@ int ds_sparse_attention_all(const void *q, const void *k_pool, const void *v_poo
                           head_dim, dtype, N, ratio, window, scale, out, stream);
 }
 
+int ds_indexer_stamps_read(int unit, void *host, int64_t bytes)
+{
+#ifdef DSI_STAMPS
+    if (unit < 0 || unit >= dsi::kStampUnits || !host || bytes < 0 ||
+        bytes > (int64_t)dsi::kStampRecords * 64)
+        return DS_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return DS_ERR_HIP;
+    hipError_t e = hipSuccess;
+    switch (unit) {
+    case dsi::kStampDecodeScore: e = dsi::stamps_read_decode(host, (size_t)bytes); break;
+    case dsi::kStampTopk: e = dsi::stamps_read_topk(host, (size_t)bytes); break;
+    case dsi::kStampMerge: e = dsi::stamps_read_merge(host, (size_t)bytes); break;
+    default: e = dsi::stamps_read_attention(host, (size_t)bytes); break;
+    }
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+#else
+    (void)unit;
+    (void)host;
+    (void)bytes;
+    return DS_ERR_UNSUPPORTED;
+#endif
+}
+
 const char *ds_indexer_status_str(int status)
 {
     switch (status) {

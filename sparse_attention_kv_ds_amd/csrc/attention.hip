@@ -42,6 +42,10 @@ namespace {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// phase timestamps (stamps build only), record = token: 0 start, 1 first block
+// and the query fragments landed, 2 last block done, 3 output stores issued
+DSI_STAMP_ARRAY(attn_stamps);
+
 // 4 x 16-bit of the transposed LDS read: within each group of 16 lanes, lane
 // i receives element i % 4 of the 8-byte chunk addressed by lane 4 e + i / 4,
 // for e = 0..3.
@@ -134,6 +138,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
     const int wave = wave_id();
     const int col = lane & 31;
     const int hf = lane >> 5;
+    DSI_STAMP(attn_stamps, t, 0, threadIdx.x == 0);
     const int p = pos[t];
     int lo = 0, n_loc = 0;
     if (p >= 0 && window > 0) {
@@ -337,6 +342,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
             load_block(0, ks0, vs0);
         wait_vmcnt<0>(); // block 0 and the query fragments
         __syncthreads();
+        DSI_STAMP(attn_stamps, t, 1, threadIdx.x == 0);
         // block b: V of block b + 1 loads into the other V stage from the
         // start; K of block b + 1 into the one K stage once every wave holds
         // the K fragments of block b (the barrier in the hook)
@@ -368,6 +374,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
         }
     }
 
+    DSI_STAMP(attn_stamps, t, 2, threadIdx.x == 0);
     // o = O / l for head col (the two halves' parts of l added)
     float l = add_other_half(l_part);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -383,6 +390,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
             v.w = o[d][4 * r + 3] * inv;
             *reinterpret_cast<float4 *>(ot + 32 * d + 8 * r + 4 * hf) = v;
         }
+    DSI_STAMP(attn_stamps, t, 3, threadIdx.x == 0);
 }
 
 template <int WAVES, int D, int DT, int IDS>
@@ -408,6 +416,13 @@ hipError_t attn_one(const AttnProblem &a, hipStream_t st, Timing *tm)
 }
 
 } // namespace
+
+#ifdef DSI_STAMPS
+hipError_t stamps_read_attention(void *host, size_t bytes)
+{
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(attn_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 hipError_t launch_sparse_attention(const AttnProblem &a, hipStream_t st, Timing *tm)
 {

@@ -194,4 +194,25 @@ __device__ __forceinline__ float add_other_half(float v)
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Phase timestamps, compiled in only with DSI_STAMPS (the separate stamps
+// build behind the phase breakdowns): DSI_STAMP_ARRAY(a) defines the device
+// array `a` of kStampRecords records of 8 entries in the source file that uses
+// it, and DSI_STAMP(a, i, ph, cond) writes the 100 MHz real-time counter to
+// entry ph of record i from the lanes where cond holds (records past the end
+// are dropped).  Without DSI_STAMPS both expand to nothing.
+#ifdef DSI_STAMPS
+#define DSI_STAMP_ARRAY(a) __device__ unsigned long long a[kStampRecords * 8]
+#define DSI_STAMP(a, i, ph, cond)                                                 \
+    do {                                                                          \
+        const long long i_ = (i);                                                 \
+        if ((cond) && i_ < kStampRecords)                                         \
+            a[i_ * 8 + (ph)] = __builtin_amdgcn_s_memrealtime();                  \
+    } while (0)
+#else
+#define DSI_STAMP_ARRAY(a) static_assert(true, "")
+#define DSI_STAMP(a, i, ph, cond) \
+    do {                          \
+    } while (0)
+#endif
+
 } // namespace dsi

@@ -63,6 +63,19 @@ struct Problem {
     int T, N, ratio, H, D, dtype;
 };
 
+// Phase timestamps (builds with DSI_STAMPS only): records of 8 entries of the
+// 100 MHz real-time counter, one array per kernel family, kStampRecords
+// records each (record = work-group, token or sequence, as the kernel states).
+constexpr int kStampRecords = 4096;
+enum { kStampDecodeScore = 0, kStampTopk = 1, kStampMerge = 2, kStampAttention = 3, kStampUnits = 4 };
+#ifdef DSI_STAMPS
+// copy the first `bytes` of one family's array to host memory (synchronous)
+hipError_t stamps_read_decode(void *host, size_t bytes);    // scorer.hip
+hipError_t stamps_read_topk(void *host, size_t bytes);      // topk.hip
+hipError_t stamps_read_merge(void *host, size_t bytes);     // topk.hip
+hipError_t stamps_read_attention(void *host, size_t bytes); // attention.hip
+#endif
+
 // rows per decode-selection partition (one decode work-group)
 constexpr int kDecodePart = 512;
 // largest candidate union the decode merge holds in registers (64 per thread)

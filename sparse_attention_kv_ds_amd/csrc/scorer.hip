@@ -259,6 +259,11 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 // K loads marked non-temporal: every byte of K is read once per call
 constexpr int kStreamAux = 2;
 
+// phase timestamps of the decode scorer (stamps build only), record = work-group
+// (blockIdx.y * gridDim.x + blockIdx.x): 0 start, 1 query and first blocks in
+// LDS, 2 + w wave w's last block scored, 6 partition list written
+DSI_STAMP_ARRAY(decode_stamps);
+
 template <int H, int D, int DT, int WAVES, int NB>
 __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
@@ -266,6 +271,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     uint64_t *__restrict__ cand, int *__restrict__ pcount, uint64_t *__restrict__ pmin,
     long long ldS)
 {
+    const long long stamp_rec = (long long)blockIdx.y * gridDim.x + blockIdx.x;
+    DSI_STAMP(decode_stamps, stamp_rec, 0, threadIdx.x == 0);
     // sequence blockIdx.y of a batched call (0 for a single token)
     {
         const int sb = blockIdx.y;
@@ -352,6 +359,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     // here and in every wave
     wait_vmcnt<(NB > 1 ? 2 : 1) * KPB>();
     lds_barrier();
+    DSI_STAMP(decode_stamps, stamp_rec, 1, threadIdx.x == 0);
     u32x4 a[MT][KS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -427,6 +435,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
         // rows >= n dropped
         buf_store_f32(rs, hf == 0 ? (uint32_t)(wrow + b * 32 + col) * 4 : kOffNone, sc);
     }
+    DSI_STAMP(decode_stamps, stamp_rec, 2 + wave, lane == 0 && wave < 4);
     if (cand == nullptr)
         return;
 
@@ -500,6 +509,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
             pcount[blockIdx.x] = nc;
             pmin[blockIdx.x] = rows > kp ? t : 0ull;
         }
+        DSI_STAMP(decode_stamps, stamp_rec, 6, lane == 0);
         return;
     }
 
@@ -546,6 +556,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
         pcount[blockIdx.x] = nc;
         pmin[blockIdx.x] = rows > kp ? t : 0ull;
     }
+    DSI_STAMP(decode_stamps, stamp_rec, 6, lane == 0);
 }
 
 __global__ void fill_kernel(float *__restrict__ p, long long n, float v)
@@ -627,6 +638,13 @@ hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const 
     return dispatch<DecodeF>(p.H, p.D, p.dtype, p, min_rows, S, &dl, st, tm, B, ldS);
 }
 
+#ifdef DSI_STAMPS
+hipError_t stamps_read_decode(void *host, size_t bytes)
+{
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(decode_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
+
 hipError_t launch_fill(float *p, long long n, float v, hipStream_t st)
 {
     if (n <= 0)
@@ -636,7 +654,7 @@ hipError_t launch_fill(float *p, long long n, float v, hipStream_t st)
         blocks = 4096;
     (void)hipGetLastError(); // (see launch_kernel)
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
-    return hipGetLastError();
+    return after_launch(hipGetLastError(), st);
 }
 
 } // namespace dsi

@@ -39,6 +39,14 @@ int select_slots(int topk, int batch)
 constexpr int kStreamU = 16;
 constexpr int kStreamBatch = kStreamU * 64;
 
+// phase timestamps (stamps build only).  Prefill top-k, record = token: 0
+// start, 1 starting threshold found, 2 row streamed, 3 final selection done,
+// 4 rows written.  Decode merge, record = sequence: 0 start, 1 lists loaded
+// and counted, 2 k-th key of the union found, 3 exactness checked, 4 rows
+// written (or 5 after the exact re-stream).
+DSI_STAMP_ARRAY(topk_stamps);
+DSI_STAMP_ARRAY(merge_stamps);
+
 // ---------------------------------------------------------------------------
 // prefill: one wave per token over its row S[t][0..n_t); the next 512 scores
 // are always in flight while the current 512 are pushed.
@@ -56,6 +64,7 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
     const int t = blockIdx.x * wpb + wave;
     if (t >= T)
         return;
+    DSI_STAMP(topk_stamps, t, 0, lane == 0);
     const int n = visible_rows(pos[t], ratio, N);
     int32_t *o = out + (long long)t * topk;
     if (n <= topk) { // all rows fit: the sequential rows, no scoring needed
@@ -96,6 +105,7 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
         WaveReduce red;
         lower = uniform64(select_bound<16>(hi, lo, 16, NS, r, r / 4 + 1, red));
     }
+    DSI_STAMP(topk_stamps, t, 1, lane == 0);
     WaveSelect<MAXS> sel;
 #pragma unroll 1
     for (;;) {
@@ -137,9 +147,12 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
             cur[u] = __uint_as_float(
                 __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
     }
+    DSI_STAMP(topk_stamps, t, 2, lane == 0);
     sel.finish();
+    DSI_STAMP(topk_stamps, t, 3, lane == 0);
     for (int i = lane; i < topk; i += 64)
         o[i] = key_row(sel.buf[i]);
+    DSI_STAMP(topk_stamps, t, 4, lane == 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -272,6 +285,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = wave_id();
+    DSI_STAMP(merge_stamps, blockIdx.x, 0, tid == 0);
     const int32_t p0 = pos[0];
     const int Pmax = (N + kDecodePart - 1) / kDecodePart;
     const int Umax = Pmax * kp; // <= MS * NT
@@ -308,6 +322,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     }
     BlockReduce<NW> br{red, &tab[0][0], 0};
     const int total = br.sum(wave_sum(have));
+    DSI_STAMP(merge_stamps, blockIdx.x, 1, tid == 0);
     bool fallback = total < topk;
     uint64_t tU = 0;
     if (!fallback) {
@@ -315,6 +330,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
         tU = union_kth_hist<MS, NW>(hi, lo, topk, br, hist, bcand, hinfo);
         if (tU == 0ull)
             tU = select_bound<MS>(hi, lo, MS, total, topk, 0, br);
+        DSI_STAMP(merge_stamps, blockIdx.x, 2, tid == 0);
         bool fail = false;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
@@ -326,6 +342,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
         }
         fallback = br.sum(popc(ballot(fail))) > 0;
     }
+    DSI_STAMP(merge_stamps, blockIdx.x, 3, tid == 0);
     if (!fallback) {
         // output position of a kept key: kept keys of earlier slots, then of
         // earlier waves in its slot, then of lower lanes.  Lane s of each wave
@@ -365,6 +382,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
             if ((m[s] >> lane) & 1)
                 out[__builtin_amdgcn_readlane(base, s) + mbcnt(m[s])] =
                     key_row(((uint64_t)hi[s] << 32) | lo[s]);
+        DSI_STAMP(merge_stamps, blockIdx.x, 4, tid == 0);
         return;
     }
     // exact fallback: one wave re-streams every partition in row order, the
@@ -398,6 +416,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     sel.finish();
     for (int i = lane; i < topk; i += 64)
         out[i] = key_row(sel.buf[i]);
+    DSI_STAMP(merge_stamps, blockIdx.x, 5, lane == 0);
 }
 
 template <int MAXS>
@@ -464,6 +483,18 @@ __global__ __launch_bounds__(256) void sequential_rows_kernel(const int32_t *__r
 }
 
 } // namespace
+
+#ifdef DSI_STAMPS
+hipError_t stamps_read_topk(void *host, size_t bytes)
+{
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(topk_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+
+hipError_t stamps_read_merge(void *host, size_t bytes)
+{
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(merge_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, int topk,
                                   int32_t *out, hipStream_t st, Timing *tm)

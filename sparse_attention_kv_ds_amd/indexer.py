@@ -14,7 +14,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libds_indexer.so")
+# DS_INDEXER_LIB selects another build of the same library (the timestamped
+# libds_indexer_stamps.so for phase breakdowns); default: the product build
+LIB_PATH = os.environ.get("DS_INDEXER_LIB") or os.path.join(HERE, "libds_indexer.so")
 
 DS_F16 = 1
 DS_BF16 = 2
@@ -36,7 +38,11 @@ EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
            "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all",
            "ds_indexer_score_topk_batch", "ds_indexer_project_q", "ds_indexer_project_score_topk",
-           "ds_indexer_score_topk_noalloc")
+           "ds_indexer_score_topk_noalloc", "ds_indexer_stamps_read")
+DS_STAMPS_DECODE_SCORE = 0
+DS_STAMPS_TOPK = 1
+DS_STAMPS_MERGE = 2
+DS_STAMPS_ATTENTION = 3
 
 
 class IndexerError(RuntimeError):
@@ -81,6 +87,8 @@ def _load() -> ctypes.CDLL:
     lib.ds_sparse_attention.restype = I
     lib.ds_sparse_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                         ctypes.c_float, P, P]
+    lib.ds_indexer_stamps_read.restype = I
+    lib.ds_indexer_stamps_read.argtypes = [I, P, I64]
     lib.ds_sparse_attention_all.restype = I
     lib.ds_sparse_attention_all.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                             ctypes.c_float, P, P]
@@ -107,6 +115,10 @@ def ds_indexer_create(device: int, n_heads: int, head_dim: int, dtype: int, max_
 
 def ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream) -> int:
     return _lib.ds_indexer_score_topk(handle, q, k, w, pos, T, N, ratio, topk, out, stream)
+
+
+def ds_indexer_stamps_read(unit, host, nbytes) -> int:
+    return _lib.ds_indexer_stamps_read(unit, host, nbytes)
 
 
 def ds_indexer_score_topk_noalloc(q, k, w, pos, T, N, n_heads, head_dim, dtype, ratio, topk,

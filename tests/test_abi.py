@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
                                            "ds_sparse_attention_all",
                                            "ds_indexer_score_topk_batch", "ds_indexer_project_q",
                                            "ds_indexer_project_score_topk",
-                                           "ds_indexer_score_topk_noalloc"])
+                                           "ds_indexer_score_topk_noalloc",
+                                           "ds_indexer_stamps_read"])
 
 
 def test_every_declared_symbol_is_exported(ix):
@@ -50,6 +51,20 @@ def test_binding_names_match_the_header(ix):
     assert set(ix.EXPORTS) == set(declared_functions())
 
 
+def test_stamps_only_in_the_stamps_build(ix):
+    """The product build records no timestamps: the reader refuses without
+    touching the device.  The stamps build exports the same entry points."""
+    if os.path.basename(ix.LIB_PATH) != "libds_indexer.so":
+        pytest.skip("another build selected through DS_INDEXER_LIB")
+    buf = ctypes.create_string_buffer(64)
+    assert ix.ds_indexer_stamps_read(0, ctypes.addressof(buf), 64) == ix.DS_ERR_UNSUPPORTED
+    stamps = os.path.join(os.path.dirname(ix.LIB_PATH), "libds_indexer_stamps.so")
+    assert os.path.exists(stamps), "build() also builds the stamps library"
+    dyn = subprocess.run(["nm", "-D", "--defined-only", stamps], capture_output=True, text=True,
+                         check=True).stdout
+    assert set(re.findall(r"\bT (ds_[a-z_]+)\b", dyn)) == set(declared_functions())
+
+
 def test_status_strings(ix):
     for code in (0, -1, -2, -3, -4, -5):
         s = ix.ds_indexer_status_str(code)
@@ -62,7 +77,8 @@ def test_header_constants_match_binding(ix):
     for name in ("DS_F16", "DS_BF16", "DS_OK", "DS_ERR_INVALID_ARG", "DS_ERR_UNSUPPORTED",
                  "DS_ERR_CAPACITY", "DS_ERR_HIP", "DS_ERR_OOM", "DS_KERNEL_SCORE",
                  "DS_KERNEL_SELECT", "DS_KERNEL_DECODE_SCORE", "DS_KERNEL_DECODE_SELECT",
-                 "DS_KERNEL_PROJECT", "DS_KERNEL_CLASSES"):
+                 "DS_KERNEL_PROJECT", "DS_KERNEL_CLASSES", "DS_STAMPS_DECODE_SCORE",
+                 "DS_STAMPS_TOPK", "DS_STAMPS_MERGE", "DS_STAMPS_ATTENTION"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert m and int(m.group(1)) == getattr(ix, name), name
 

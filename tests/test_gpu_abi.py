@@ -214,3 +214,32 @@ def test_create_range_limits_before_any_allocation(lib):
     st, h = lib.ds_indexer_create(0, 64, 128, lib.DS_F16, 512, 1, 8388480)
     assert st == lib.DS_OK
     lib.ds_indexer_destroy(h)
+
+
+def test_debug_sync_mode(lib, handle, bufs, monkeypatch):
+    """DS_INDEXER_DEBUG=1: every launch is synchronised and checked inside the
+    call; the calls still succeed and give the same bytes as without it."""
+    from sparse_attention_kv_ds_amd import synth
+    d = synth.make("tiny")
+    wl = d["wl"]
+    q = torch.from_numpy(d["q"].view(np.int16)).to(DEV)
+    k = torch.from_numpy(d["k"].view(np.int16)).to(DEV)
+    w = torch.from_numpy(d["w"]).to(DEV)
+    pos = torch.from_numpy(d["pos"]).to(DEV)
+    got = {}
+    for mode in ("0", "1"):
+        say(f"DS_INDEXER_DEBUG={mode}: score_topk and sparse attention")
+        monkeypatch.setenv("DS_INDEXER_DEBUG", mode)
+        with lib.Indexer(wl.H, wl.D, wl.dtype, wl.topk, wl.T, wl.N) as ix:
+            got[mode] = ix.score_topk(q, k, w, pos, wl.ratio, wl.topk).cpu().numpy()
+        a = synth.make_attention("attn_tiny")
+        t = {kk: torch.from_numpy(np.ascontiguousarray(a[kk]).view(np.int16)).to(DEV)
+             for kk in ("q", "kp", "vp", "kl", "vl")}
+        o = lib.sparse_attention(t["q"], t["kp"], t["vp"], t["kl"], t["vl"],
+                                 torch.from_numpy(a["idx"]).to(DEV),
+                                 torch.from_numpy(a["pos"]).to(DEV), window=a["wl"].window,
+                                 scale=a["wl"].scale, dtype=a["wl"].dtype)
+        got[mode + "a"] = o.cpu().numpy()
+    monkeypatch.delenv("DS_INDEXER_DEBUG")
+    assert np.array_equal(got["0"], got["1"])
+    assert np.array_equal(got["0a"], got["1a"])
