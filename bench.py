@@ -192,6 +192,15 @@ def time_workload(name: str, steps: int, warmup: int, warmup_ms: float = WARMUP_
         ix.timing_read()
         ms_marked = timed_calls(call, steps, dev)
         per = ix.timing_read()
+        stream_only = None
+        if wl.T == 1:
+            # the decode stream alone: the same scorer without its partition
+            # lists, as ds_indexer_scores runs it (its kernel timed the same way)
+            srow = torch.empty((1, wl.N), dtype=torch.float32, device=dev)
+            timed_calls(lambda i: ix.scores(q, ks[i % len(ks)], w, pos, wl.ratio, out=srow),
+                        steps, dev)
+            st_per = ix.timing_read()
+            stream_only = st_per["decode_score"][0] / max(st_per["decode_score"][1], 1)
         ix.timing(False)
     finally:
         ix.close()
@@ -201,7 +210,7 @@ def time_workload(name: str, steps: int, warmup: int, warmup_ms: float = WARMUP_
            "step_stats": stats, "warmup_calls": nw, "warmup_ms": wms,
            "pairs": pairs, "tokens": wl.T,
            "pairs_per_s": pairs / (ms * 1e-3), "query_tokens_per_s": wl.T / (ms * 1e-3),
-           "kernels": kernels, "wl": wl}
+           "kernels": kernels, "wl": wl, "stream_only_ms": stream_only}
     log(f"[bench] {name}: {ms * 1e3:.1f} us/step (median {stats['median_ms'] * 1e3:.1f}, "
         f"min {stats['min_ms'] * 1e3:.1f}; {ms_marked * 1e3:.1f} with kernel markers; "
         f"warm-up {nw} calls, {wms:.0f} ms), "
@@ -921,6 +930,12 @@ def main():
             rf = entry["roofline"]
             entry.update({"value": rf["achieved"], "unit": "GB/s (decode scorer, K from HBM)",
                           "end_to_end_GBps": rf["algorithmic_bytes_per_launch"] / (r["ms_per_step"] * 1e-3) / 1e9})
+            if r.get("stream_only_ms"):
+                so = r["stream_only_ms"]
+                entry["stream_only"] = {
+                    "what": "the same scorer without its partition lists (ds_indexer_scores)",
+                    "ms": so, "GBps": rf["algorithmic_bytes_per_launch"] / (so * 1e-3) / 1e9,
+                    "frac": rf["algorithmic_bytes_per_launch"] / (so * 1e-3) / 1e9 / PEAK_HBM_GBS}
         elif "score" not in r["kernels"]:  # whole-call skip: nothing is scored
             entry.update({"value": r["query_tokens_per_s"],
                           "unit": "query tokens/s (every row fits: sequential rows, no scoring)"})

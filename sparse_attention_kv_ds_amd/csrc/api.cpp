@@ -468,10 +468,16 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
     const dsi::Problem p = problem(ix, q, k, w, pos, T, N, ratio);
     hipError_t e = dsi::launch_fill(scores, T * N, -__builtin_huge_valf(), s);
     if (e == hipSuccess) {
+        // (timed like the scorers of a score + top-k call: the decode stream
+        // alone, without its partition lists, is measured this way)
         if (T == 1 && ix->decode_ok)
-            e = dsi::launch_decode_scorer(p, 0, scores, dsi::DecodeLists{}, s);
+            e = timed(ix, DS_KERNEL_DECODE_SCORE, [&](dsi::Timing *tm) {
+                return dsi::launch_decode_scorer(p, 0, scores, dsi::DecodeLists{}, s, tm);
+            });
         else
-            e = dsi::launch_prefill_scorer(p, 0, scores, (long long)N, s);
+            e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
+                return dsi::launch_prefill_scorer(p, 0, scores, (long long)N, s, tm);
+            });
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
