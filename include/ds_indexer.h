@@ -276,7 +276,10 @@ const char *ds_indexer_status_str(int status);
  *                                    6 partition list written
  *            DS_STAMPS_TOPK          prefill top-k, record = token: 0 start,
  *                                    1 starting threshold, 2 row streamed,
- *                                    3 final selection, 4 rows written
+ *                                    3 final selection, 4 rows written;
+ *                                    counts, not times: 5 keys buffered after
+ *                                    the stream, 6 streams of the row * 65536
+ *                                    + searches run while streaming
  *            DS_STAMPS_MERGE         decode merge, record = sequence: 0 start,
  *                                    1 lists loaded, 2 k-th key of the union,
  *                                    3 exactness checked, 4 rows written

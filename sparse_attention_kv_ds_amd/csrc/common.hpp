@@ -208,8 +208,19 @@ __device__ __forceinline__ float add_other_half(float v)
         if ((cond) && i_ < kStampRecords)                                         \
             a[i_ * 8 + (ph)] = __builtin_amdgcn_s_memrealtime();                  \
     } while (0)
+// DSI_STAMP_VALUE(a, i, ph, cond, v): the same, recording the value v (a
+// count, not a time)
+#define DSI_STAMP_VALUE(a, i, ph, cond, v)                                        \
+    do {                                                                          \
+        const long long i_ = (i);                                                 \
+        if ((cond) && i_ < kStampRecords)                                         \
+            a[i_ * 8 + (ph)] = (unsigned long long)(v);                           \
+    } while (0)
 #else
 #define DSI_STAMP_ARRAY(a) static_assert(true, "")
+#define DSI_STAMP_VALUE(a, i, ph, cond, v) \
+    do {                                   \
+    } while (0)
 #define DSI_STAMP(a, i, ph, cond) \
     do {                          \
     } while (0)

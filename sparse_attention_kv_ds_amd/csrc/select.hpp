@@ -355,6 +355,9 @@ struct WaveSelect {
     int slack;    // a streaming shrink keeps between k and k + slack keys
     int cnt;      // keys in buf (wave-uniform)
     uint64_t tau; // keys <= tau cannot be among the k best (wave-uniform)
+#ifdef DSI_STAMPS
+    int shrinks = 0; // (stamps build: searches run while streaming)
+#endif
 
     // Keys arrive in batches of at most `batch` (a multiple of 64) between
     // make_room() calls; requires CAP >= k + batch + 64.
@@ -400,6 +403,9 @@ struct WaveSelect {
     // accesses stay in program order.
     __device__ __forceinline__ void shrink(int sl)
     {
+#ifdef DSI_STAMPS
+        shrinks += sl > 0;
+#endif
         wave_lds_sync();
         const int lane = threadIdx.x & 63;
         const int nsl = (cnt + 63) >> 6;

@@ -20,6 +20,8 @@
 #include "launch.hpp"
 #include "select.hpp"
 
+#include <type_traits>
+
 namespace dsi {
 
 namespace {
@@ -41,7 +43,9 @@ constexpr int kStreamBatch = kStreamU * 64;
 
 // phase timestamps (stamps build only).  Prefill top-k, record = token: 0
 // start, 1 starting threshold found, 2 row streamed, 3 final selection done,
-// 4 rows written.  Decode merge, record = sequence: 0 start, 1 lists loaded
+// 4 rows written; values: 5 keys buffered at the end of the stream, 6 the
+// number of streams of the row (1, or 2 after a restart) times 65536 plus the
+// searches run while streaming.  Decode merge, record = sequence: 0 start, 1 lists loaded
 // and counted, 2 k-th key of the union found, 3 exactness checked, 4 rows
 // written (or 5 after the exact re-stream).
 DSI_STAMP_ARRAY(topk_stamps);
@@ -82,19 +86,24 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
     for (int u = 0; u < U; ++u)
         cur[u] = __uint_as_float(
             __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
-    // Starting threshold from a sample of the row (16 runs of 64 consecutive
-    // rows, evenly spaced): a bound L that about r sampled keys reach, r chosen
-    // so that about 1.5 k keys of the whole row are expected to reach L -- most
-    // of the row is then dropped at the first compare and the buffer rarely
-    // fills.  The result does not depend on the estimate: when fewer than k keys
-    // of the row reach L, the row is streamed again from threshold 0.
-    uint64_t lower = 0;
-    constexpr int NS = 16 * 64; // sample size, 16 keys per lane
-    if (n >= 4 * NS) {
-        uint32_t hi[16], lo[16];
+    // Starting threshold from a sample of the row (runs of 64 consecutive
+    // rows, evenly spaced: 16 runs for rows of 4096 and more, 4 for rows of
+    // 1024..4095, none below): a bound L that about r sampled keys reach, r
+    // chosen so that about 1.5 k keys of the whole row are expected to reach L
+    // -- most of the row is then dropped at the first compare, the buffer
+    // rarely fills, and the final search has about 1.5 k keys to look at
+    // rather than the whole row.  The result does not depend on the estimate:
+    // when fewer than k keys of the row reach L, the row is streamed again
+    // from threshold 0.
+    // (the run count is a template constant, so that the sample's loads issue
+    // back to back and the search's counts have no bound checks)
+    auto sample_bound = [&](auto runs_c) -> uint64_t {
+        constexpr int R = decltype(runs_c)::value;
+        constexpr int NS = R * 64; // sample size
+        uint32_t hi[R], lo[R];
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const int j = (int)((long long)s * (n - 64) / 15) + lane;
+        for (int s = 0; s < R; ++s) {
+            const int j = (int)((long long)s * (n - 64) / (R - 1)) + lane;
             const uint64_t key = make_key(
                 __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)j * 4, 0, 0)),
                 (uint32_t)j);
@@ -103,12 +112,23 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
         }
         const int r = min(NS, (int)((long long)topk * NS * 3 / (2LL * n)) + 8);
         WaveReduce red;
-        lower = uniform64(select_bound<16>(hi, lo, 16, NS, r, r / 4 + 1, red));
-    }
+        return uniform64(select_bound<R>(hi, lo, R, NS, r, r / 4 + 1, red));
+    };
+    uint64_t lower = 0;
+    if (n >= 4 * 1024)
+        lower = sample_bound(std::integral_constant<int, 16>{});
+    else if (n >= 4 * 256)
+        lower = sample_bound(std::integral_constant<int, 4>{});
     DSI_STAMP(topk_stamps, t, 1, lane == 0);
     WaveSelect<MAXS> sel;
+#ifdef DSI_STAMPS
+    int streams = 0;
+#endif
 #pragma unroll 1
     for (;;) {
+#ifdef DSI_STAMPS
+        ++streams;
+#endif
         sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, lower, kStreamBatch);
 #pragma unroll 1
         for (int base = 0; base < n; base += U * 64) {
@@ -148,6 +168,10 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
                 __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
     }
     DSI_STAMP(topk_stamps, t, 2, lane == 0);
+    DSI_STAMP_VALUE(topk_stamps, t, 5, lane == 0, sel.cnt);
+#ifdef DSI_STAMPS
+    DSI_STAMP_VALUE(topk_stamps, t, 6, lane == 0, (long long)streams * 65536 + sel.shrinks);
+#endif
     sel.finish();
     DSI_STAMP(topk_stamps, t, 3, lane == 0);
     for (int i = lane; i < topk; i += 64)

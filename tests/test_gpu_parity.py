@@ -579,6 +579,30 @@ def test_sampled_threshold_restart(lib, orc):
                    dtype="f16", ratio=ratio, topk=topk, where=f"restart N={N}")
 
 
+def test_sampled_threshold_restart_short_rows(lib, orc):
+    """Rows of 1024..4095, sampled with 4 runs of 64 rows: the sampled runs (at
+    s (n - 64) / 3, s = 0..3) carry the top score and every other row a lower
+    one, so the estimate is the top score, which only 256 < k rows reach: the
+    row must be streamed again from threshold 0.  Bit-exact against the
+    oracle either way."""
+    H, D, topk, ratio = 4, 32, 512, 1
+    for N in (1024, 2048, 3000, 4095):
+        say(f"sampled threshold restart, short rows: n = {N}")
+        j = np.arange(N)
+        top = np.zeros(N, dtype=bool)
+        for r in range(4):
+            a = r * (N - 64) // 3
+            top[a:a + 64] = True
+        k = np.zeros((N, D), dtype=np.float64)
+        k[:, 0] = np.where(top, 8, j % 5)
+        q = np.zeros((3, H, D), dtype=np.float64)
+        q[:, :, 0] = 1
+        w = np.ones((3, H), dtype=np.float32)
+        pos = np.array([N - 1, N - 1, N + 2], dtype=np.int32)
+        exact_case(lib, orc, synth.to_bits(q, "f16"), synth.to_bits(k, "f16"), w, pos, H=H, D=D,
+                   dtype="f16", ratio=ratio, topk=topk, where=f"short-row restart N={N}")
+
+
 def test_long_rows_with_a_top_run_bit_exact(lib, orc):
     """Long rows (7168..16384) whose first 64 rows -- the first run of the
     starting-threshold sample, one row per lane -- carry the top score and the
