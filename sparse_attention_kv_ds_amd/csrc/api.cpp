@@ -187,12 +187,12 @@ hipError_t launch_score_topk(ds_indexer *ix, const Work &wk, const dsi::Problem 
             });
     } else {
         e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
-            return dsi::launch_prefill_scorer(p, topk, wk.S, wk.ldS, s, tm);
+            return dsi::launch_prefill_scorer(p, topk, wk.S, wk.ldS, true, s, tm);
         });
         if (e == hipSuccess)
             e = timed(ix, DS_KERNEL_SELECT, [&](dsi::Timing *tm) {
-                return dsi::launch_topk_stream(wk.S, wk.ldS, p.pos, T, N, p.ratio, topk, out, s,
-                                               tm);
+                return dsi::launch_topk_stream(reinterpret_cast<const uint16_t *>(wk.S), wk.ldS,
+                                               p.pos, T, N, p.ratio, topk, out, s, tm);
             });
     }
     return e;
@@ -476,7 +476,7 @@ int ds_indexer_scores(ds_indexer *ix, const void *q, const void *k, const float 
             });
         else
             e = timed(ix, DS_KERNEL_SCORE, [&](dsi::Timing *tm) {
-                return dsi::launch_prefill_scorer(p, 0, scores, (long long)N, s, tm);
+                return dsi::launch_prefill_scorer(p, 0, scores, (long long)N, false, s, tm);
             });
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;

@@ -148,6 +148,18 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// the low 16 bits of v
+__device__ __forceinline__ void buf_store_u16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, 0);
+}
+
+// 16 bits, zero-extended (0 past the end of the resource)
+__device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 // 16 bytes per lane from r at byte offset off straight into LDS: lane l's
 // bytes land at lds + 16 l (lds must be the same in every lane).  The load is
 // counted by vmcnt and its data is in LDS once that count says it completed.

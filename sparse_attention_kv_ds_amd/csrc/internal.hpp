@@ -98,10 +98,13 @@ constexpr size_t kStaticScratchBytes =
 // looked up once per device and kept until the process ends.
 hipError_t static_scratch(int device, void **ptr);
 
-// Scores of every token with more than min_rows visible rows, written to
-// S[t * ldS + j] for j < n_t (other entries untouched).
+// Scores of every token with more than min_rows visible rows, for j < n_t
+// (other entries untouched): split == false, fp32 at S[t * ldS + j]; split,
+// the split scores of launch_topk_stream in token t's 4 ldS bytes at
+// S + t * ldS: row j's high 16 bits of ordered_score(s[t][j]) at byte
+// 128 (j / 32) + 2 (j % 32), its low 16 bits 64 bytes further on.
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
-                                 hipStream_t st, Timing *tm = nullptr);
+                                 bool split, hipStream_t st, Timing *tm = nullptr);
 
 // Per-partition candidate lists of the single-token selection: partition p
 // (rows p * kDecodePart ..) lists its exact best kp keys in row order in
@@ -129,10 +132,11 @@ hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const 
                                 hipStream_t st, Timing *tm = nullptr, int B = 1,
                                 long long ldS = 0);
 
-// Per-token streaming top-k over S rows (one wave per token); skip path for
-// tokens whose visible rows all fit.
-hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos, int T, int N,
-                              int ratio, int topk, int32_t *out, hipStream_t st,
+// Per-token streaming top-k over the split scores the prefill scorer writes
+// (token t's at S16 + 2 t ldS, laid out as launch_prefill_scorer says); one
+// wave per token; skip path for tokens whose visible rows all fit.
+hipError_t launch_topk_stream(const uint16_t *S16, long long ldS, const int32_t *pos, int T,
+                              int N, int ratio, int topk, int32_t *out, hipStream_t st,
                               Timing *tm = nullptr);
 
 // Single-token selection over S[0..n) from the partitions' candidate lists

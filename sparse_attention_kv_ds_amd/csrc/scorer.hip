@@ -43,8 +43,18 @@ constexpr int kStageRows = 64;      // K rows per LDS stage (two 32-row blocks)
 // (one accumulator pair per wave keeps the kernel at three waves per SIMD, so
 // that other waves' MFMAs cover each wave's epilogue).  Rows past N read as 0
 // and masked score stores are dropped (buffer-resource ranges).
+//
+// Output: with SPLIT == false, token t's scores as fp32 at S + t ldS.  With
+// SPLIT, split scores for the streaming top-k: token t's 4 ldS bytes at
+// S + t ldS hold, for every 32-row block, 64 bytes with the high 16 bits of
+// the block's ordered scores (ordered_score) followed by 64 bytes with their
+// low 16 bits, so that the selection reads half the bytes and fetches the
+// low halves only for the rows it cannot order by the high ones.  The same
+// bytes are written either way, in whole 128-byte pieces; with one token per
+// wave the two half-waves store the two halves of a block (one store
+// instruction per block, as for fp32).
 // ---------------------------------------------------------------------------
-template <int H, int D, int DT, int WAVES, int SR>
+template <int H, int D, int DT, int WAVES, int SR, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ pos, int T, int N, int ratio, int min_rows, int chunk_rows,
@@ -110,12 +120,17 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     // tokens this lane stores: half-wave hf stores tokens hf, hf+2, ... of the
     // wave (H >= 8) or tokens 2g + hf of each 8-token tile (H == 4)
     constexpr int NST = H == 4 ? 8 : (TPW + 1) / 2;
+    // store instructions per block: one per token slot, two (one per half)
+    // for split scores when a lane holds a whole token's score
+    constexpr int NSTORE = SPLIT && TPW > 1 ? 2 * NST : NST;
     int st_n[NST], st_tok[NST];
 #pragma unroll
     for (int e = 0; e < NST; ++e) {
         int tk;
         if constexpr (H == 4)
             tk = (e >> 2) * 8 + 2 * (e & 3) + hf;
+        else if constexpr (SPLIT && TPW == 1)
+            tk = 0; // both half-waves store the wave's one token (one half each)
         else
             tk = 2 * e + hf;
         st_tok[e] = wave * TPW + tk;
@@ -148,6 +163,11 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
         boff[kk] = (uint32_t)stage_slot<CPR>(col, 2 * kk + hf) * 16;
+
+    // (split scores, one token per wave: the shift that leaves this half-wave's
+    // 16 bits of an ordered score at the bottom)
+    const uint32_t lo_shift = hf ? 0u : 16u;
+    (void)lo_shift;
 
     // Lane-local partial sums of the epilogue: slot = token of the lane (see
     // st_tok), two interleaved sums per slot for instruction-level parallelism.
@@ -198,7 +218,24 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
                 }
             }
             const bool ok = (unsigned)j < (unsigned)st_n[e];
-            buf_store_f32(rs, ok ? (uint32_t)((st_tok[e] * ldS + j) * 4) : kOffNone, v);
+            if constexpr (!SPLIT) {
+                buf_store_f32(rs, ok ? (uint32_t)((st_tok[e] * ldS + j) * 4) : kOffNone, v);
+            } else {
+                // ordered_score(v) without its -0 fold: v is never -0 (every
+                // sum here starts from +0, and a round-to-nearest sum or
+                // fused multiply-add reaches -0 only from -0 operands)
+                const uint32_t b = __float_as_uint(v);
+                const uint32_t ov = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+                // this block's 128 bytes: high halves at +2 col, low halves at +64 + 2 col
+                const uint32_t hi_off = (uint32_t)((st_tok[e] * ldS + jb) * 4 + col * 2);
+                if constexpr (TPW == 1) {
+                    // (both halves hold v: the lower stores the high bits)
+                    buf_store_u16(rs, ok ? hi_off + 64u * hf : kOffNone, ov >> lo_shift);
+                } else {
+                    buf_store_u16(rs, ok ? hi_off : kOffNone, ov >> 16);
+                    buf_store_u16(rs, ok ? hi_off + 64u : kOffNone, ov);
+                }
+            }
         }
     };
 
@@ -215,7 +252,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     // score stores issued after them, NST per block, may still be in flight),
     // then every wave's have
     auto stage_done = [&]() {
-        wait_vmcnt<SR / 32 * NST>();
+        wait_vmcnt<SR / 32 * NSTORE>();
         lds_barrier();
     };
 
@@ -567,12 +604,16 @@ __global__ void fill_kernel(float *__restrict__ p, long long n, float v)
 }
 
 template <int H, int D, int DT>
-hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, hipStream_t st,
-                       Timing *tm)
+hipError_t prefill_one(const Problem &p, int min_rows, float *S, long long ldS, bool split,
+                       hipStream_t st, Timing *tm)
 {
     constexpr int TPB = (64 / H) * kPrefillWaves;
     const dim3 grid((p.T + TPB - 1) / TPB, (p.N + kChunkRows - 1) / kChunkRows);
-    return launch_kernel(prefill_scorer_kernel<H, D, DT, kPrefillWaves, kStageRows>, grid,
+    if (split)
+        return launch_kernel(prefill_scorer_kernel<H, D, DT, kPrefillWaves, kStageRows, true>,
+                             grid, dim3(kPrefillWaves * 64), 0, st, tm, true, true, p.q, p.k, p.w,
+                             p.pos, p.T, p.N, p.ratio, min_rows, kChunkRows, S, ldS);
+    return launch_kernel(prefill_scorer_kernel<H, D, DT, kPrefillWaves, kStageRows, false>, grid,
                          dim3(kPrefillWaves * 64), 0, st, tm, true, true, p.q, p.k, p.w, p.pos,
                          p.T, p.N, p.ratio, min_rows, kChunkRows, S, ldS);
 }
@@ -606,10 +647,10 @@ hipError_t dispatch(int H, int D, int dt, A... args)
 }
 
 template <int H, int D, int DT> struct PrefillF {
-    static hipError_t run(const Problem &p, int m, float *S, long long ld, hipStream_t st,
-                          Timing *tm)
+    static hipError_t run(const Problem &p, int m, float *S, long long ld, bool split,
+                          hipStream_t st, Timing *tm)
     {
-        return prefill_one<H, D, DT>(p, m, S, ld, st, tm);
+        return prefill_one<H, D, DT>(p, m, S, ld, split, st, tm);
     }
 };
 template <int H, int D, int DT> struct DecodeF {
@@ -623,11 +664,11 @@ template <int H, int D, int DT> struct DecodeF {
 } // namespace
 
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
-                                 hipStream_t st, Timing *tm)
+                                 bool split, hipStream_t st, Timing *tm)
 {
     if (p.T <= 0 || p.N <= 0)
         return hipSuccess;
-    return dispatch<PrefillF>(p.H, p.D, p.dtype, p, min_rows, S, ldS, st, tm);
+    return dispatch<PrefillF>(p.H, p.D, p.dtype, p, min_rows, S, ldS, split, st, tm);
 }
 
 hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *S, const DecodeLists &dl,

@@ -337,6 +337,18 @@ __device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const 
     return ((uint64_t)v << 32) | red.template nth<E, LO>(hi, lo, v, need);
 }
 
+// #{keys greater than x among arr[0 .. cnt)} (cnt <= 64, uniform; arr holds 64 keys)
+__device__ __forceinline__ int rank_among(const uint64_t *arr, int cnt, uint64_t x)
+{
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < cnt; j += 2) {
+        const uint64_t a = arr[j], b = arr[j + 1]; // (arr[j + 1] may be stale when j + 1 == cnt)
+        r += (a > x) + (j + 1 < cnt && b > x);
+    }
+    return r;
+}
+
 // Low words of a wave's LDS key buffer, read on demand: slot s of this lane,
 // at a constant offset from the lane's first key.
 struct LdsLow {
@@ -355,13 +367,23 @@ struct WaveSelect {
     int slack;    // a streaming shrink keeps between k and k + slack keys
     int cnt;      // keys in buf (wave-uniform)
     uint64_t tau; // keys <= tau cannot be among the k best (wave-uniform)
+    // Coarse keys: the high word holds only the top 16 bits of the ordered
+    // score, so keys with the same high word are not in score order.  A
+    // streaming shrink then keeps whole high words (a bound with low word 0);
+    // when that is impossible within the slack (a single high word straddles
+    // the boundary with more than the slack's worth of keys) it sets `failed`
+    // and leaves the buffer as it was, and the caller starts again with exact
+    // keys.
+    bool coarse;
+    bool failed;
 #ifdef DSI_STAMPS
     int shrinks = 0; // (stamps build: searches run while streaming)
 #endif
 
     // Keys arrive in batches of at most `batch` (a multiple of 64) between
     // make_room() calls; requires CAP >= k + batch + 64.
-    __device__ __forceinline__ void init(uint64_t *b, int kk, uint64_t lower, int batch)
+    __device__ __forceinline__ void init(uint64_t *b, int kk, uint64_t lower, int batch,
+                                         bool coarse_keys = false)
     {
         buf = b;
         k = kk;
@@ -370,6 +392,8 @@ struct WaveSelect {
         slack = slack > 0 ? slack : 0;
         cnt = 0;
         tau = lower ? lower - 1 : 0;
+        coarse = coarse_keys;
+        failed = false;
     }
 
     // before a batch of up to `incoming` keys
@@ -429,6 +453,12 @@ struct WaveSelect {
             L = uniform64(select_bound<MAXS>(hi, LdsLow{mine}, nsl, cnt, k, sl, red));
         else
             L = uniform64(select_bound<MAXS>(hi, lo_r, nsl, cnt, k, sl, red));
+        // (a bound within the slack is a whole high word, low word 0, or 1:
+        // keep everything; any other bound is a key, which splits a high word)
+        if (coarse && sl > 0 && (uint32_t)L != 0u && L != 1ull) {
+            failed = true;
+            return;
+        }
         int nc = 0;
 #pragma unroll
         for (int s = 0; s < MAXS; ++s) {
@@ -458,6 +488,129 @@ struct WaveSelect {
             shrink(0);
         wave_lds_sync();
     }
+
+    // The same for coarse keys (at least k, whole high words kept by every
+    // shrink).  The high word h holding the k-th key is found by bisection;
+    // the keys above h are in, those below out.  Only the keys of h itself
+    // need their exact order: their ordered scores are completed with the low
+    // 16 bits, low_of(row).  With at most 64 such keys they are ranked one
+    // per lane (scratch: 64 keys of LDS private to the wave) and the best
+    // ones lifted to high word h + 1; otherwise the keys above h are lifted to
+    // (h + 1) << 16, above every completed one, and the exact search keeps k.
+    // Either way the buffer ends with exactly the k best, in row order.
+    template <class LOW>
+    __device__ __forceinline__ void finish_coarse(const LOW &low_of, uint64_t *scratch)
+    {
+        wave_lds_sync();
+        if (cnt <= k)
+            return;
+        const int lane = threadIdx.x & 63;
+        const int nsl = (cnt + 63) >> 6;
+        const uint64_t *mine = buf + lane;
+        const int rem = cnt - lane;
+        uint32_t hi[MAXS];
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s)
+            hi[s] = s * 64 < rem ? (uint32_t)(mine[s * 64] >> 32) : 0u;
+        WaveReduce red;
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s)
+            if (hi[s] != 0u) {
+                mn = min(mn, hi[s]);
+                mx = max(mx, hi[s]);
+            }
+        red.minmax(mn, mx);
+        // #{high >= v} = cv >= k > cu = #{high >= u}
+        uint32_t v = mn, u = mx + 1;
+        int cv = cnt, cu = 0;
+#pragma unroll 1
+        while (u - v > 1 && cv != k) {
+            const uint32_t c = v + ((u - v) >> 1);
+            const int cc = count_hi_ge<MAXS>(hi, nsl, c);
+            if (cc >= k) {
+                v = c;
+                cv = cc;
+            } else {
+                u = c;
+                cu = cc;
+            }
+        }
+        const uint32_t h = v; // unless cv == k, u == v + 1 and h holds the k-th key
+        uint32_t keep_from = v; // the answer: the keys with high word >= keep_from
+        if (cv != k && cv - cu <= 64) {
+            const int nb = cv - cu, need = k - cu; // 1 <= need < nb
+            // the buffer slots of the keys of h, in order, one per lane
+            uint32_t *bidx = reinterpret_cast<uint32_t *>(scratch);
+            int c = 0;
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s) {
+                if (s < nsl) {
+                    const bool in = hi[s] == h;
+                    const uint64_t m = ballot(in);
+                    if (in)
+                        bidx[c + mbcnt(m)] = (uint32_t)(s * 64 + lane);
+                    c += popc(m);
+                }
+            }
+            wave_lds_sync();
+            const bool has = lane < nb;
+            const uint32_t ix = has ? bidx[lane] : 0u;
+            const uint64_t key = has ? buf[ix] : 0ull;
+            const uint32_t lo16 = has ? low_of(0xFFFFFFFFu - (uint32_t)key) : 0u;
+            const uint64_t ex = has ? ((uint64_t)((h << 16) | lo16) << 32) | (uint32_t)key : 0ull;
+            wave_lds_sync(); // (the slots are read before the scratch is reused)
+            scratch[lane] = ex;
+            wave_lds_sync();
+            const int above = rank_among(scratch, nb, ex);
+            if (has && above < need)
+                buf[ix] = ((uint64_t)(h + 1) << 32) | (uint32_t)key;
+            wave_lds_sync();
+            keep_from = h + 1;
+        } else if (cv != k) {
+            uint32_t low16[MAXS];
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s) {
+                low16[s] = 0u;
+                if (s < nsl && ballot(hi[s] == h))
+                    low16[s] = hi[s] == h ? low_of(0xFFFFFFFFu - (uint32_t)mine[s * 64]) : 0u;
+            }
+            int nc = 0;
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s) {
+                if (s < nsl) {
+                    const uint32_t lw = (uint32_t)mine[s * 64];
+                    const bool keep = hi[s] != 0u && hi[s] >= h;
+                    const uint32_t nh = hi[s] == h ? (h << 16) | low16[s] : (h + 1) << 16;
+                    const uint64_t m = ballot(keep);
+                    if (keep)
+                        buf[nc + mbcnt(m)] = ((uint64_t)nh << 32) | lw;
+                    nc += popc(m);
+                }
+            }
+            wave_lds_sync();
+            cnt = nc;
+            coarse = false; // every key left is exact, or above every one that is
+            shrink(0);
+            wave_lds_sync();
+            return;
+        }
+        // keep the keys with high word >= keep_from (re-read: some were lifted)
+        int nc = 0;
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            if (s < nsl) {
+                const uint64_t key = s * 64 < rem ? mine[s * 64] : 0ull;
+                const bool keep = (uint32_t)(key >> 32) >= keep_from;
+                const uint64_t m = ballot(keep);
+                if (keep)
+                    buf[nc + mbcnt(m)] = key;
+                nc += popc(m);
+            }
+        }
+        wave_lds_sync();
+        cnt = nc;
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -472,18 +625,6 @@ struct WaveSelect {
 // where a bisection would take one dependent count step per score bit.
 // scratch: 128 keys of LDS private to the wave.
 // ---------------------------------------------------------------------------
-// #{keys greater than x among arr[0 .. cnt)} (cnt <= 64, uniform; arr holds 64 keys)
-__device__ __forceinline__ int rank_among(const uint64_t *arr, int cnt, uint64_t x)
-{
-    int r = 0;
-#pragma unroll 8
-    for (int j = 0; j < cnt; j += 2) {
-        const uint64_t a = arr[j], b = arr[j + 1]; // (arr[j + 1] may be stale when j + 1 == cnt)
-        r += (a > x) + (j + 1 < cnt && b > x);
-    }
-    return r;
-}
-
 template <int E, int LANES = 64>
 __device__ __forceinline__ uint64_t wave_kth_small(const uint32_t (&hi)[E], const uint32_t (&lo)[E],
                                                    int k, uint64_t *scratch)

@@ -52,11 +52,25 @@ DSI_STAMP_ARRAY(topk_stamps);
 DSI_STAMP_ARRAY(merge_stamps);
 
 // ---------------------------------------------------------------------------
-// prefill: one wave per token over its row S[t][0..n_t); the next 512 scores
-// are always in flight while the current 512 are pushed.
+// prefill: one wave per token over the high halves of its ordered scores
+// (u16 entries S16[2 t ldS + j], j < n_t); the next 1024 are always in flight
+// while the current 1024 are pushed.  The keys are coarse: (high 16 bits of
+// the ordered score, row).  A coarse key order is the score order wherever
+// the high halves differ, so the streaming shrinks keep whole high halves and
+// only the rows that share the boundary's high half need their low halves
+// (WaveSelect::finish_coarse).  A row where that boundary holds more keys
+// than the buffer's slack (many equal or nearly equal scores) is streamed
+// again with exact keys from both halves.
 // ---------------------------------------------------------------------------
+// the selection key of (the 32-bit ordered score or its high half, row)
+__device__ __forceinline__ uint64_t key_of(uint32_t ord, uint32_t row)
+{
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - row);
+}
+
 template <int MAXS>
-__global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restrict__ S, long long ldS,
+__global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__restrict__ S16,
+                                                          long long ldS,
                                                           const int32_t *__restrict__ pos, int T,
                                                           int N, int ratio, int topk,
                                                           int32_t *__restrict__ out)
@@ -76,25 +90,29 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
             o[i] = i < n ? i : -1;
         return;
     }
-    const float *row = S + (long long)t * ldS;
-    const auto rr = make_rsrc(row, (uint32_t)n * 4); // (reads past n_t return 0)
-    // The next U scores per lane are always in flight while the current U are
-    // appended; the first U are fetched before the sample below is used.
+    // the token's split scores: row j's high half at byte 128 (j / 32) +
+    // 2 (j % 32), its low half 64 bytes further on
+    const auto rs = make_rsrc(S16 + (long long)t * 2 * ldS, (uint32_t)((n + 31) >> 5) * 128);
+    auto hi_off = [](int j) { return ((uint32_t)j >> 5) * 128 + ((uint32_t)j & 31) * 2; };
+    auto low_of = [&](uint32_t j) { return buf_load_u16(rs, hi_off((int)j) + 64); };
+    // The next U entries per lane are always in flight while the current U
+    // are appended; the first U are fetched before the sample below is used.
+    // (rows u 64 + lane of a batch: byte 4 (64 u) + this lane's offset)
     constexpr int U = kStreamU;
-    float cur[U], nxt[U];
+    const uint32_t lane_off = hi_off(lane);
+    uint32_t cur[U], nxt[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        cur[u] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
+        cur[u] = buf_load_u16(rs, u * 64 + lane < n ? (uint32_t)(u * 256) + lane_off : kOffNone);
     // Starting threshold from a sample of the row (runs of 64 consecutive
     // rows, evenly spaced: 16 runs for rows of 4096 and more, 4 for rows of
     // 1024..4095, none below): a bound L that about r sampled keys reach, r
     // chosen so that about 1.5 k keys of the whole row are expected to reach L
     // -- most of the row is then dropped at the first compare, the buffer
     // rarely fills, and the final search has about 1.5 k keys to look at
-    // rather than the whole row.  The result does not depend on the estimate:
-    // when fewer than k keys of the row reach L, the row is streamed again
-    // from threshold 0.
+    // rather than the whole row.  L is rounded down to a whole high half.  The
+    // result does not depend on the estimate: when fewer than k keys of the
+    // row reach L, the row is streamed again from threshold 0.
     // (the run count is a template constant, so that the sample's loads issue
     // back to back and the search's counts have no bound checks)
     auto sample_bound = [&](auto runs_c) -> uint64_t {
@@ -104,15 +122,13 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
 #pragma unroll
         for (int s = 0; s < R; ++s) {
             const int j = (int)((long long)s * (n - 64) / (R - 1)) + lane;
-            const uint64_t key = make_key(
-                __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)j * 4, 0, 0)),
-                (uint32_t)j);
-            hi[s] = (uint32_t)(key >> 32);
-            lo[s] = (uint32_t)key;
+            hi[s] = buf_load_u16(rs, hi_off(j));
+            lo[s] = 0xFFFFFFFFu - (uint32_t)j;
         }
         const int r = min(NS, (int)((long long)topk * NS * 3 / (2LL * n)) + 8);
         WaveReduce red;
-        return uniform64(select_bound<R>(hi, lo, R, NS, r, r / 4 + 1, red));
+        const uint64_t L = uniform64(select_bound<R>(hi, lo, R, NS, r, r / 4 + 1, red));
+        return L == 1ull ? L : L & 0xFFFFFFFF00000000ull;
     };
     uint64_t lower = 0;
     if (n >= 4 * 1024)
@@ -121,6 +137,7 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
         lower = sample_bound(std::integral_constant<int, 4>{});
     DSI_STAMP(topk_stamps, t, 1, lane == 0);
     WaveSelect<MAXS> sel;
+    uint64_t *const kbuf = keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP;
 #ifdef DSI_STAMPS
     int streams = 0;
 #endif
@@ -129,28 +146,29 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
 #ifdef DSI_STAMPS
         ++streams;
 #endif
-        sel.init(keys_lds + (size_t)wave * WaveSelect<MAXS>::CAP, topk, lower, kStreamBatch);
+        sel.init(kbuf, topk, lower, kStreamBatch, true);
 #pragma unroll 1
         for (int base = 0; base < n; base += U * 64) {
             const int nb = base + U * 64;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = nb + u * 64 + lane;
-                nxt[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    rr, j < n ? (uint32_t)j * 4 : kOffNone, 0, 0));
+                nxt[u] = buf_load_u16(rs, j < n ? (uint32_t)(nb + u * 64) * 4 + lane_off : kOffNone);
             }
             sel.make_room(kStreamBatch);
+            if (sel.failed)
+                break;
             if (nb <= n) { // a whole batch of visible rows: no bound check per key
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int j = base + u * 64 + lane;
-                    sel.append(make_key(cur[u], (uint32_t)j), true);
+                    sel.append(key_of(cur[u], (uint32_t)j), true);
                 }
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int j = base + u * 64 + lane;
-                    sel.append(make_key(cur[u], (uint32_t)j), j < n);
+                    sel.append(key_of(cur[u], (uint32_t)j), j < n);
                 }
             }
 #pragma unroll
@@ -159,20 +177,36 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restric
         }
         // (after a shrink the buffer holds >= k keys; without one it holds
         // every key that reached the starting threshold)
-        if (sel.cnt >= topk || lower == 0)
+        if (sel.failed || sel.cnt >= topk || lower == 0)
             break;
         lower = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            cur[u] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(u * 64 + lane) * 4, 0, 0));
+            cur[u] = buf_load_u16(rs, u * 64 + lane < n ? (uint32_t)(u * 256) + lane_off
+                                                        : kOffNone);
     }
     DSI_STAMP(topk_stamps, t, 2, lane == 0);
     DSI_STAMP_VALUE(topk_stamps, t, 5, lane == 0, sel.cnt);
 #ifdef DSI_STAMPS
-    DSI_STAMP_VALUE(topk_stamps, t, 6, lane == 0, (long long)streams * 65536 + sel.shrinks);
+    DSI_STAMP_VALUE(topk_stamps, t, 6, lane == 0,
+                    (long long)(streams + sel.failed) * 65536 + sel.shrinks);
 #endif
-    sel.finish();
+    if (sel.failed) {
+        // too many keys share the boundary's high half: the row again, with
+        // exact keys (both halves of every ordered score)
+        wave_lds_sync();
+        sel.init(kbuf, topk, 0, 64);
+#pragma unroll 1
+        for (int base = 0; base < n; base += 64) {
+            const uint32_t j = (uint32_t)(base + lane);
+            const uint32_t off = (int)j < n ? hi_off((int)j) : kOffNone;
+            const uint32_t ord = (buf_load_u16(rs, off) << 16) | buf_load_u16(rs, off + 64);
+            sel.push(key_of(ord, j), (int)j < n);
+        }
+        sel.finish();
+    } else {
+        sel.finish_coarse(low_of, keys_lds + (size_t)wpb * WaveSelect<MAXS>::CAP + wave * 64);
+    }
     DSI_STAMP(topk_stamps, t, 3, lane == 0);
     for (int i = lane; i < topk; i += 64)
         o[i] = key_row(sel.buf[i]);
@@ -444,12 +478,13 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
 }
 
 template <int MAXS>
-hipError_t topk_stream_one(const float *S, long long ldS, const int32_t *pos, int T, int N,
+hipError_t topk_stream_one(const uint16_t *S, long long ldS, const int32_t *pos, int T, int N,
                            int ratio, int topk, int32_t *out, hipStream_t st, Timing *tm)
 {
     // waves (tokens) per work-group: 64 KiB of LDS at most
     const int wpb = MAXS >= 64 ? 2 : 4;
-    const size_t lds = (size_t)wpb * MAXS * 64 * sizeof(uint64_t);
+    // each wave's key buffer, then 64 keys of scratch per wave
+    const size_t lds = (size_t)wpb * (MAXS + 1) * 64 * sizeof(uint64_t);
     return launch_kernel(topk_stream_kernel<MAXS>, dim3((T + wpb - 1) / wpb), dim3(wpb * 64), lds,
                          st, tm, true, true, S, ldS, pos, T, N, ratio, topk, out);
 }
@@ -529,8 +564,8 @@ hipError_t launch_sequential_rows(const int32_t *pos, int T, int N, int ratio, i
                          true, pos, T, N, ratio, topk, out);
 }
 
-hipError_t launch_topk_stream(const float *S, long long ldS, const int32_t *pos, int T, int N,
-                              int ratio, int topk, int32_t *out, hipStream_t st, Timing *tm)
+hipError_t launch_topk_stream(const uint16_t *S, long long ldS, const int32_t *pos, int T,
+                              int N, int ratio, int topk, int32_t *out, hipStream_t st, Timing *tm)
 {
     if (T <= 0)
         return hipSuccess;

@@ -131,8 +131,8 @@ hipError_t hipEventElapsedTime(float *ms, hipEvent_t, hipEvent_t)
 
 namespace dsi {
 
-hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *, long long, hipStream_t,
-                                 Timing *tm)
+hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *, long long, bool,
+                                 hipStream_t, Timing *tm)
 {
     return fake::record("prefill_scorer", p.T, p.N, min_rows, 1, tm);
 }
@@ -143,7 +143,7 @@ hipError_t launch_decode_scorer(const Problem &p, int min_rows, float *, const D
     return fake::record("decode_scorer", p.T, p.N, min_rows, B, tm);
 }
 
-hipError_t launch_topk_stream(const float *, long long, const int32_t *, int T, int N, int,
+hipError_t launch_topk_stream(const uint16_t *, long long, const int32_t *, int T, int N, int,
                               int topk, int32_t *, hipStream_t, Timing *tm)
 {
     return fake::record("topk_stream", T, N, topk, 1, tm);
