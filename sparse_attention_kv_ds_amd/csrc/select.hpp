@@ -490,28 +490,45 @@ struct WaveSelect {
     }
 
     // The same for coarse keys (at least k, whole high words kept by every
-    // shrink).  The high word h holding the k-th key is found by bisection;
-    // the keys above h are in, those below out.  Only the keys of h itself
-    // need their exact order: their ordered scores are completed with the low
-    // 16 bits, low_of(row).  With at most 64 such keys they are ranked one
-    // per lane (scratch: 64 keys of LDS private to the wave) and the best
-    // ones lifted to high word h + 1; otherwise the keys above h are lifted to
-    // (h + 1) << 16, above every completed one, and the exact search keeps k.
-    // Either way the buffer ends with exactly the k best, in row order.
+    // shrink), ending with the k best rows, ascending, in out[0 .. k).  The
+    // high word h holding the k-th key is found by bisection; the keys above
+    // h are in, those below out.  Only the keys of h itself need their exact
+    // order: their ordered scores are completed with the low 16 bits,
+    // low_of(row).  With at most 64 such keys they are ranked one per lane
+    // (scratch: 64 keys of LDS private to the wave) and the rows are written
+    // straight from the slots in order, each key of h asking the lane that
+    // ranked it whether it is in.  With more, the keys above h are lifted to
+    // (h + 1) << 16, above every completed one, the exact search keeps k in
+    // the buffer, and the rows are written from there.
     template <class LOW>
-    __device__ __forceinline__ void finish_coarse(const LOW &low_of, uint64_t *scratch)
+    __device__ __forceinline__ void finish_coarse(const LOW &low_of, uint64_t *scratch,
+                                                  int32_t *out)
     {
         wave_lds_sync();
-        if (cnt <= k)
-            return;
         const int lane = threadIdx.x & 63;
+        if (cnt <= k) {
+            for (int i = lane; i < cnt; i += 64)
+                out[i] = key_row(buf[i]);
+            return;
+        }
         const int nsl = (cnt + 63) >> 6;
         const uint64_t *mine = buf + lane;
         const int rem = cnt - lane;
         uint32_t hi[MAXS];
+        uint32_t lo_r[kLowInLds ? 1 : MAXS];
 #pragma unroll
-        for (int s = 0; s < MAXS; ++s)
-            hi[s] = s * 64 < rem ? (uint32_t)(mine[s * 64] >> 32) : 0u;
+        for (int s = 0; s < MAXS; ++s) {
+            const uint64_t key = s * 64 < rem ? mine[s * 64] : 0ull;
+            hi[s] = (uint32_t)(key >> 32);
+            if constexpr (!kLowInLds)
+                lo_r[s] = (uint32_t)key;
+        }
+        auto row_of = [&](int s) -> int {
+            if constexpr (kLowInLds)
+                return key_row(mine[s * 64]);
+            else
+                return key_row(lo_r[s]);
+        };
         WaveReduce red;
         uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
@@ -537,79 +554,89 @@ struct WaveSelect {
             }
         }
         const uint32_t h = v; // unless cv == k, u == v + 1 and h holds the k-th key
-        uint32_t keep_from = v; // the answer: the keys with high word >= keep_from
-        if (cv != k && cv - cu <= 64) {
-            const int nb = cv - cu, need = k - cu; // 1 <= need < nb
-            // the buffer slots of the keys of h, in order, one per lane
-            uint32_t *bidx = reinterpret_cast<uint32_t *>(scratch);
-            int c = 0;
+        if (cv == k || cv - cu <= 64) {
+            // in[B index] for the keys of h, B index = order among them (one per lane)
+            bool in_b = false;
+            if (cv != k) {
+                const int nb = cv - cu, need = k - cu; // 1 <= need < nb
+                uint32_t *bidx = reinterpret_cast<uint32_t *>(scratch);
+                int c = 0;
 #pragma unroll
-            for (int s = 0; s < MAXS; ++s) {
-                if (s < nsl) {
-                    const bool in = hi[s] == h;
-                    const uint64_t m = ballot(in);
-                    if (in)
-                        bidx[c + mbcnt(m)] = (uint32_t)(s * 64 + lane);
-                    c += popc(m);
+                for (int s = 0; s < MAXS; ++s) {
+                    if (s < nsl) {
+                        const bool b = hi[s] == h;
+                        const uint64_t m = ballot(b);
+                        if (b)
+                            bidx[c + mbcnt(m)] = (uint32_t)(s * 64 + lane);
+                        c += popc(m);
+                    }
                 }
+                wave_lds_sync();
+                const bool has = lane < nb;
+                const uint32_t ix = has ? bidx[lane] : 0u;
+                const uint32_t lw = has ? (uint32_t)buf[ix] : 0u;
+                const uint32_t lo16 = has ? low_of(0xFFFFFFFFu - lw) : 0u;
+                const uint64_t ex = has ? ((uint64_t)((h << 16) | lo16) << 32) | lw : 0ull;
+                wave_lds_sync(); // (the slots are read before the scratch is reused)
+                scratch[lane] = ex;
+                wave_lds_sync();
+                in_b = has && rank_among(scratch, nb, ex) < need;
             }
-            wave_lds_sync();
-            const bool has = lane < nb;
-            const uint32_t ix = has ? bidx[lane] : 0u;
-            const uint64_t key = has ? buf[ix] : 0ull;
-            const uint32_t lo16 = has ? low_of(0xFFFFFFFFu - (uint32_t)key) : 0u;
-            const uint64_t ex = has ? ((uint64_t)((h << 16) | lo16) << 32) | (uint32_t)key : 0ull;
-            wave_lds_sync(); // (the slots are read before the scratch is reused)
-            scratch[lane] = ex;
-            wave_lds_sync();
-            const int above = rank_among(scratch, nb, ex);
-            if (has && above < need)
-                buf[ix] = ((uint64_t)(h + 1) << 32) | (uint32_t)key;
-            wave_lds_sync();
-            keep_from = h + 1;
-        } else if (cv != k) {
-            uint32_t low16[MAXS];
-#pragma unroll
-            for (int s = 0; s < MAXS; ++s) {
-                low16[s] = 0u;
-                if (s < nsl && ballot(hi[s] == h))
-                    low16[s] = hi[s] == h ? low_of(0xFFFFFFFFu - (uint32_t)mine[s * 64]) : 0u;
-            }
-            int nc = 0;
+            // the rows, in order: high word above h, or h and ranked in (cv == k: every
+            // key of h is in)
+            const int in_bits = in_b ? 1 : 0;
+            int nc = 0, bb = 0;
 #pragma unroll
             for (int s = 0; s < MAXS; ++s) {
                 if (s < nsl) {
-                    const uint32_t lw = (uint32_t)mine[s * 64];
-                    const bool keep = hi[s] != 0u && hi[s] >= h;
-                    const uint32_t nh = hi[s] == h ? (h << 16) | low16[s] : (h + 1) << 16;
+                    const bool b = hi[s] == h;
+                    const uint64_t mb = ballot(b);
+                    bool keep = hi[s] > h;
+                    if (cv == k) {
+                        keep = keep || b;
+                    } else if (mb) {
+                        // (every lane takes part: a lane that is switched off
+                        // would read as 0 to the lanes asking it)
+                        const int from = bb + mbcnt(mb);
+                        const int asked = __builtin_amdgcn_ds_bpermute(from * 4, in_bits);
+                        keep = keep || (b && asked != 0);
+                    }
+                    bb += popc(mb);
                     const uint64_t m = ballot(keep);
                     if (keep)
-                        buf[nc + mbcnt(m)] = ((uint64_t)nh << 32) | lw;
+                        out[nc + mbcnt(m)] = row_of(s);
                     nc += popc(m);
                 }
             }
-            wave_lds_sync();
-            cnt = nc;
-            coarse = false; // every key left is exact, or above every one that is
-            shrink(0);
-            wave_lds_sync();
             return;
         }
-        // keep the keys with high word >= keep_from (re-read: some were lifted)
+        uint32_t low16[MAXS];
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            low16[s] = 0u;
+            if (s < nsl && ballot(hi[s] == h))
+                low16[s] = hi[s] == h ? low_of((uint32_t)row_of(s)) : 0u;
+        }
         int nc = 0;
 #pragma unroll
         for (int s = 0; s < MAXS; ++s) {
             if (s < nsl) {
-                const uint64_t key = s * 64 < rem ? mine[s * 64] : 0ull;
-                const bool keep = (uint32_t)(key >> 32) >= keep_from;
+                const uint32_t lw = 0xFFFFFFFFu - (uint32_t)row_of(s);
+                const bool keep = hi[s] != 0u && hi[s] >= h;
+                const uint32_t nh = hi[s] == h ? (h << 16) | low16[s] : (h + 1) << 16;
                 const uint64_t m = ballot(keep);
                 if (keep)
-                    buf[nc + mbcnt(m)] = key;
+                    buf[nc + mbcnt(m)] = ((uint64_t)nh << 32) | lw;
                 nc += popc(m);
             }
         }
         wave_lds_sync();
         cnt = nc;
+        coarse = false; // every key left is exact, or above every one that is
+        shrink(0);
+        wave_lds_sync();
+        for (int i = lane; i < k; i += 64)
+            out[i] = key_row(buf[i]);
     }
 };
 

@@ -204,12 +204,13 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__rest
             sel.push(key_of(ord, j), (int)j < n);
         }
         sel.finish();
+        DSI_STAMP(topk_stamps, t, 3, lane == 0);
+        for (int i = lane; i < topk; i += 64)
+            o[i] = key_row(sel.buf[i]);
     } else {
-        sel.finish_coarse(low_of, keys_lds + (size_t)wpb * WaveSelect<MAXS>::CAP + wave * 64);
+        sel.finish_coarse(low_of, keys_lds + (size_t)wpb * WaveSelect<MAXS>::CAP + wave * 64, o);
+        DSI_STAMP(topk_stamps, t, 3, lane == 0);
     }
-    DSI_STAMP(topk_stamps, t, 3, lane == 0);
-    for (int i = lane; i < topk; i += 64)
-        o[i] = key_row(sel.buf[i]);
     DSI_STAMP(topk_stamps, t, 4, lane == 0);
 }
 
