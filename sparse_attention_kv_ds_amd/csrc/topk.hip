@@ -95,15 +95,6 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__rest
     const auto rs = make_rsrc(S16 + (long long)t * 2 * ldS, (uint32_t)((n + 31) >> 5) * 128);
     auto hi_off = [](int j) { return ((uint32_t)j >> 5) * 128 + ((uint32_t)j & 31) * 2; };
     auto low_of = [&](uint32_t j) { return buf_load_u16(rs, hi_off((int)j) + 64); };
-    // The next U entries per lane are always in flight while the current U
-    // are appended; the first U are fetched before the sample below is used.
-    // (rows u 64 + lane of a batch: byte 4 (64 u) + this lane's offset)
-    constexpr int U = kStreamU;
-    const uint32_t lane_off = hi_off(lane);
-    uint32_t cur[U], nxt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        cur[u] = buf_load_u16(rs, u * 64 + lane < n ? (uint32_t)(u * 256) + lane_off : kOffNone);
     // Starting threshold from a sample of the row (runs of 64 consecutive
     // rows, evenly spaced: 16 runs for rows of 4096 and more, 4 for rows of
     // 1024..4095, none below): a bound L that about r sampled keys reach, r
@@ -113,27 +104,50 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__rest
     // rather than the whole row.  L is rounded down to a whole high half.  The
     // result does not depend on the estimate: when fewer than k keys of the
     // row reach L, the row is streamed again from threshold 0.
-    // (the run count is a template constant, so that the sample's loads issue
-    // back to back and the search's counts have no bound checks)
+    // The sample's loads go out first, then the row's first U entries per
+    // lane, so that the search waits only for the sample.  (The run count is
+    // a template constant, so that the loads issue back to back and the
+    // search's counts have no bound checks.)
+    constexpr int kRunsMax = 16;
+    uint32_t shi[kRunsMax];
+    auto sample_loads = [&](auto runs_c) {
+        constexpr int R = decltype(runs_c)::value;
+#pragma unroll
+        for (int s = 0; s < R; ++s)
+            shi[s] = buf_load_u16(rs, hi_off((int)((long long)s * (n - 64) / (R - 1)) + lane));
+    };
     auto sample_bound = [&](auto runs_c) -> uint64_t {
         constexpr int R = decltype(runs_c)::value;
         constexpr int NS = R * 64; // sample size
         uint32_t hi[R], lo[R];
 #pragma unroll
         for (int s = 0; s < R; ++s) {
-            const int j = (int)((long long)s * (n - 64) / (R - 1)) + lane;
-            hi[s] = buf_load_u16(rs, hi_off(j));
-            lo[s] = 0xFFFFFFFFu - (uint32_t)j;
+            hi[s] = shi[s];
+            lo[s] = 0xFFFFFFFFu - (uint32_t)((int)((long long)s * (n - 64) / (R - 1)) + lane);
         }
         const int r = min(NS, (int)((long long)topk * NS * 3 / (2LL * n)) + 8);
         WaveReduce red;
         const uint64_t L = uniform64(select_bound<R>(hi, lo, R, NS, r, r / 4 + 1, red));
         return L == 1ull ? L : L & 0xFFFFFFFF00000000ull;
     };
+    const int runs = n >= 4 * 1024 ? 16 : (n >= 4 * 256 ? 4 : 0);
+    if (runs == 16)
+        sample_loads(std::integral_constant<int, 16>{});
+    else if (runs == 4)
+        sample_loads(std::integral_constant<int, 4>{});
+    // The next U entries per lane are always in flight while the current U
+    // are appended.  (rows u 64 + lane of a batch: byte 4 (64 u) + this
+    // lane's offset)
+    constexpr int U = kStreamU;
+    const uint32_t lane_off = hi_off(lane);
+    uint32_t cur[U], nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        cur[u] = buf_load_u16(rs, u * 64 + lane < n ? (uint32_t)(u * 256) + lane_off : kOffNone);
     uint64_t lower = 0;
-    if (n >= 4 * 1024)
+    if (runs == 16)
         lower = sample_bound(std::integral_constant<int, 16>{});
-    else if (n >= 4 * 256)
+    else if (runs == 4)
         lower = sample_bound(std::integral_constant<int, 4>{});
     DSI_STAMP(topk_stamps, t, 1, lane == 0);
     WaveSelect<MAXS> sel;
