@@ -623,35 +623,42 @@ def test_long_rows_with_a_top_run_bit_exact(lib, orc):
                    dtype="f16", ratio=ratio, topk=topk, where=f"top run N={N}")
 
 
-@pytest.mark.parametrize("sure,bucket", [(500, 30), (400, 300), (100, 1500), (0, 2000)])
-def test_split_score_boundary_buckets_exact(lib, orc, sure, bucket):
+@pytest.mark.parametrize("sure,bucket,topk", [(500, 30, 512), (400, 300, 512), (100, 1500, 512),
+                                               (0, 2000, 512), (980, 50, 1000),
+                                               (700, 600, 1000), (200, 3000, 1000)])
+def test_split_score_boundary_buckets_exact(lib, orc, sure, bucket, topk):
     """The selection streams the high 16 bits of each ordered score and
     completes only the boundary's high half with the low 16 bits.  Rows of
-    8192: `sure` rows score above every other, `bucket` rows score
-    1024 + m / 256 with distinct m (one high half, different low halves, in an
-    order unrelated to the row), the rest score below.  k = 512 falls inside
-    the bucket, so the answer depends on the low halves: 30 rows are ranked
-    one per lane, 300 go through the exact search, and 1500 or 2000 are more
-    than a streaming shrink can keep as a whole high half, so the row is
-    streamed again with exact scores.  Bit-exact against the oracle."""
-    H, D, topk, ratio, N = 4, 32, 512, 1, 8192
-    rng = np.random.default_rng(sure * 7 + bucket)
+    8192: `sure` rows score above every other, `bucket` rows score distinct
+    values in [1024, 1032) (one high half, different low halves, in an order
+    unrelated to the row), the rest score below.  k falls inside the
+    bucket, so the answer depends on the low halves: 30 or 50 rows are ranked
+    one per lane, 300 or 600 go through the exact search, and 1500 to 3000
+    are more than a streaming shrink can keep as a whole high half, so the
+    row is streamed again with exact scores (k = 1000 uses the larger buffer
+    that reads its low words from LDS).  Bit-exact against the oracle."""
+    H, D, ratio, N = 4, 32, 1, 8192
+    rng = np.random.default_rng(sure * 7 + bucket + topk)
     rows = rng.permutation(N)
     k = np.zeros((N, D), dtype=np.float64)
     hi_rows, b_rows, lo_rows = rows[:sure], rows[sure:sure + bucket], rows[sure + bucket:]
     k[hi_rows, 0] = 300.0
     k[hi_rows, 1] = rng.integers(0, 64, size=sure) / 64.0
     k[b_rows, 0] = 256.0
-    k[b_rows, 1] = rng.permutation(2048)[:bucket] / 1024.0  # s = 4 (256 + m / 1024)
+    # every fp16 value in [1/32, 2) is a multiple of 2^-15, so 256 + k1 and
+    # s = 4 (256 + k1) in [1024, 1032) are exact in fp32: one high half, 6144
+    # distinct scores to draw from
+    frac = np.arange(0x2800, 0x4000, dtype=np.uint16).view(np.float16).astype(np.float64)
+    k[b_rows, 1] = rng.permutation(frac)[:bucket]
     k[lo_rows, 0] = rng.integers(0, 200, size=len(lo_rows))
     q = np.zeros((3, H, D), dtype=np.float64)
     q[:, :, 0] = 1
     q[:, :, 1] = 1
     w = np.ones((3, H), dtype=np.float32)
     pos = np.array([N - 1, N + 4, N - 1], dtype=np.int32)
-    say(f"split-score boundary bucket: {sure} above, {bucket} in the boundary's high half")
+    say(f"split-score boundary bucket: {sure} above, {bucket} in the boundary's high half, k={topk}")
     exact_case(lib, orc, synth.to_bits(q, "f16"), synth.to_bits(k, "f16"), w, pos, H=H, D=D,
-               dtype="f16", ratio=ratio, topk=topk, where=f"bucket {sure}/{bucket}")
+               dtype="f16", ratio=ratio, topk=topk, where=f"bucket {sure}/{bucket} k={topk}")
 
 
 @pytest.mark.parametrize("N,topk", [(8192, 512), (16384, 512), (5000, 100), (2048, 512)])
