@@ -74,6 +74,8 @@ KERNEL_SOURCES = {  # kernel class -> sources whose change invalidates stored co
                      "sparse_attention_kv_ds_amd/csrc/select.hpp"],
     "attention": ["sparse_attention_kv_ds_amd/csrc/attention.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
     "project": ["sparse_attention_kv_ds_amd/csrc/qproj.hip", "sparse_attention_kv_ds_amd/csrc/common.hpp"],
+    "select": ["sparse_attention_kv_ds_amd/csrc/topk.hip", "sparse_attention_kv_ds_amd/csrc/select.hpp",
+               "sparse_attention_kv_ds_amd/csrc/common.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -638,7 +640,10 @@ DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
             "attn32k": ("attention", "sparse_attention_kernel"),
             "attn32k_r128": ("attention", "sparse_attention_kernel"),
             "decode1m_b8": ("decode_score", "decode_scorer_kernel"),
-            "qproj32k": ("project", "qproj_kernel")}
+            "qproj32k": ("project", "qproj_kernel"),
+            # the prefill top-k of the same runs (for the record, not a bench roofline)
+            "prefill32k_select": ("select", "topk_stream_kernel"),
+            "prefill64k_select": ("select", "topk_stream_kernel")}
 
 
 def record_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch: str, copy_write: str):

@@ -148,6 +148,23 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// Split scores of the prefill path (the scorer writes them, the streaming
+// top-k reads them): token t's row of 4 ldS bytes holds, per group of
+// kSplitRows rows, the high 16 bits of the rows' ordered scores
+// (ordered_score), then their low 16 bits.  A group of 32 is one scorer
+// block stored as one whole 128-byte line.  (Groups of 64, whose high halves
+// fill lines of their own, halve what the selection fetches from HBM, but
+// the scorer then writes every line in two halves from two blocks, which
+// costs it more than the selection gains.)
+constexpr int kSplitRows = 32;
+constexpr uint32_t kSplitLow = 2 * kSplitRows; // bytes from a row's high half to its low half
+
+// byte offset of row j's high half within a token's split scores
+__device__ __forceinline__ uint32_t split_hi_off(uint32_t j)
+{
+    return j / kSplitRows * (4 * kSplitRows) + j % kSplitRows * 2;
+}
+
 // the low 16 bits of v
 __device__ __forceinline__ void buf_store_u16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v)
 {

@@ -102,7 +102,7 @@ hipError_t static_scratch(int device, void **ptr);
 // (other entries untouched): split == false, fp32 at S[t * ldS + j]; split,
 // the split scores of launch_topk_stream in token t's 4 ldS bytes at
 // S + t * ldS: row j's high 16 bits of ordered_score(s[t][j]) at byte
-// 128 (j / 32) + 2 (j % 32), its low 16 bits 64 bytes further on.
+// split_hi_off(j), its low 16 bits kSplitLow bytes further on (common.hpp).
 hipError_t launch_prefill_scorer(const Problem &p, int min_rows, float *S, long long ldS,
                                  bool split, hipStream_t st, Timing *tm = nullptr);
 

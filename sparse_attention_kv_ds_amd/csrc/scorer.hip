@@ -45,14 +45,12 @@ constexpr int kStageRows = 64;      // K rows per LDS stage (two 32-row blocks)
 // and masked score stores are dropped (buffer-resource ranges).
 //
 // Output: with SPLIT == false, token t's scores as fp32 at S + t ldS.  With
-// SPLIT, split scores for the streaming top-k: token t's 4 ldS bytes at
-// S + t ldS hold, for every 32-row block, 64 bytes with the high 16 bits of
-// the block's ordered scores (ordered_score) followed by 64 bytes with their
-// low 16 bits, so that the selection reads half the bytes and fetches the
-// low halves only for the rows it cannot order by the high ones.  The same
-// bytes are written either way, in whole 128-byte pieces; with one token per
-// wave the two half-waves store the two halves of a block (one store
-// instruction per block, as for fp32).
+// SPLIT, the split scores of the streaming top-k (common.hpp: per 32-row
+// block, the rows' high halves, then their low halves), so that the
+// selection loads the high halves and the low halves only for the rows it
+// cannot order by the high ones.  The same bytes are written either way, one
+// 128-byte line per block; with one token per wave the two half-waves store
+// the two halves of a block (one store instruction per block, as for fp32).
 // ---------------------------------------------------------------------------
 template <int H, int D, int DT, int WAVES, int SR, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
@@ -226,14 +224,16 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
                 // fused multiply-add reaches -0 only from -0 operands)
                 const uint32_t b = __float_as_uint(v);
                 const uint32_t ov = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
-                // this block's 128 bytes: high halves at +2 col, low halves at +64 + 2 col
-                const uint32_t hi_off = (uint32_t)((st_tok[e] * ldS + jb) * 4 + col * 2);
+                // (the block is one group of split scores: jb is a multiple of 32)
+                static_assert(kSplitRows == 32, "one 32-row block per group");
+                const uint32_t hi_off = (uint32_t)(st_tok[e] * ldS * 4) +
+                                        split_hi_off((uint32_t)jb) + split_hi_off((uint32_t)col);
                 if constexpr (TPW == 1) {
                     // (both halves hold v: the lower stores the high bits)
-                    buf_store_u16(rs, ok ? hi_off + 64u * hf : kOffNone, ov >> lo_shift);
+                    buf_store_u16(rs, ok ? hi_off + kSplitLow * hf : kOffNone, ov >> lo_shift);
                 } else {
                     buf_store_u16(rs, ok ? hi_off : kOffNone, ov >> 16);
-                    buf_store_u16(rs, ok ? hi_off + 64u : kOffNone, ov);
+                    buf_store_u16(rs, ok ? hi_off + kSplitLow : kOffNone, ov);
                 }
             }
         }
@@ -309,6 +309,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_scorer_kernel(
     long long ldS)
 {
     const long long stamp_rec = (long long)blockIdx.y * gridDim.x + blockIdx.x;
+    (void)stamp_rec; // (only the stamps build records)
     DSI_STAMP(decode_stamps, stamp_rec, 0, threadIdx.x == 0);
     // sequence blockIdx.y of a batched call (0 for a single token)
     {

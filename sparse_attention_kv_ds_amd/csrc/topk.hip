@@ -52,9 +52,9 @@ DSI_STAMP_ARRAY(topk_stamps);
 DSI_STAMP_ARRAY(merge_stamps);
 
 // ---------------------------------------------------------------------------
-// prefill: one wave per token over the high halves of its ordered scores
-// (u16 entries S16[2 t ldS + j], j < n_t); the next 1024 are always in flight
-// while the current 1024 are pushed.  The keys are coarse: (high 16 bits of
+// prefill: one wave per token over the high halves of its ordered scores (the
+// split scores at S16 + 2 t ldS, rows j < n_t); the next 1024 are always in
+// flight while the current 1024 are pushed.  The keys are coarse: (high 16 bits of
 // the ordered score, row).  A coarse key order is the score order wherever
 // the high halves differ, so the streaming shrinks keep whole high halves and
 // only the rows that share the boundary's high half need their low halves
@@ -90,11 +90,11 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__rest
             o[i] = i < n ? i : -1;
         return;
     }
-    // the token's split scores: row j's high half at byte 128 (j / 32) +
-    // 2 (j % 32), its low half 64 bytes further on
-    const auto rs = make_rsrc(S16 + (long long)t * 2 * ldS, (uint32_t)((n + 31) >> 5) * 128);
-    auto hi_off = [](int j) { return ((uint32_t)j >> 5) * 128 + ((uint32_t)j & 31) * 2; };
-    auto low_of = [&](uint32_t j) { return buf_load_u16(rs, hi_off((int)j) + 64); };
+    // the token's split scores (common.hpp)
+    const auto rs = make_rsrc(S16 + (long long)t * 2 * ldS,
+                              (uint32_t)((n + kSplitRows - 1) / kSplitRows) * 4 * kSplitRows);
+    auto hi_off = [](int j) { return split_hi_off((uint32_t)j); };
+    auto low_of = [&](uint32_t j) { return buf_load_u16(rs, split_hi_off(j) + kSplitLow); };
     // Starting threshold from a sample of the row (runs of 64 consecutive
     // rows, evenly spaced: 16 runs for rows of 4096 and more, 4 for rows of
     // 1024..4095, none below): a bound L that about r sampled keys reach, r
@@ -139,6 +139,7 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__rest
     // are appended.  (rows u 64 + lane of a batch: byte 4 (64 u) + this
     // lane's offset)
     constexpr int U = kStreamU;
+    static_assert(64 % kSplitRows == 0, "a batch row offset of 64 u moves by 4 * 64 u bytes");
     const uint32_t lane_off = hi_off(lane);
     uint32_t cur[U], nxt[U];
 #pragma unroll
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void topk_stream_kernel(const uint16_t *__rest
         for (int base = 0; base < n; base += 64) {
             const uint32_t j = (uint32_t)(base + lane);
             const uint32_t off = (int)j < n ? hi_off((int)j) : kOffNone;
-            const uint32_t ord = (buf_load_u16(rs, off) << 16) | buf_load_u16(rs, off + 64);
+            const uint32_t ord = (buf_load_u16(rs, off) << 16) | buf_load_u16(rs, off + kSplitLow);
             sel.push(key_of(ord, j), (int)j < n);
         }
         sel.finish();
