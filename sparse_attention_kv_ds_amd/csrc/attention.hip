@@ -247,10 +247,24 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
         const uint64_t vm = ballot(lane < 32 && valid);
         // S^T: lane holds head col, keys 8 (i / 4) + 4 hf + i % 4
         f32x16 s = f32x16{};
+        {
+            // K fragments read PF steps ahead of their MFMAs; the scheduling
+            // fences keep that order (left to itself the compiler reads one
+            // step ahead, and each MFMA waits for its LDS read)
+            constexpr int PF = 2;
+            u32x4 kf[PF + 1];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kst + koff[kk]);
-            s = mfma32<DT>(kf, qf[kk], s);
+            for (int kk = 0; kk < PF && kk < KS; ++kk)
+                kf[kk] = *reinterpret_cast<const u32x4 *>(kst + koff[kk]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                if (kk + PF < KS)
+                    kf[(kk + PF) % (PF + 1)] = *reinterpret_cast<const u32x4 *>(kst + koff[kk + PF]);
+                __builtin_amdgcn_sched_barrier(0);
+                s = mfma32<DT>(kf[kk % (PF + 1)], qf[kk], s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         k_done();
         // empty key slots (partial blocks only) score -inf
@@ -289,6 +303,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
                     o[d][i] *= alpha;
         }
         const float nb2 = m_base == -__builtin_huge_valf() ? 0.f : -m_base;
+        // V^T fragments one MFMA ahead, the first one's reads before the
+        // exponentials, so that no value MFMA waits for its LDS reads
+        // (measured: 3-4 % faster than reading each just before its MFMA)
+        auto vread = [&](int st, int d) -> u32x4 {
+            const unsigned char *vb = vst + voffd[d] + (uint32_t)(16 * st * D) * 2;
+            const uint64_t lo4 = lds_read_tr16(vb);
+            const uint64_t hi4 = lds_read_tr16(vb + 8 * D * 2);
+            return u32x4{(uint32_t)lo4, (uint32_t)(lo4 >> 32), (uint32_t)hi4, (uint32_t)(hi4 >> 32)};
+        };
+        u32x4 vf[2];
+        vf[0] = vread(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -297,18 +323,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
             l_part += p0 + p1;
             pk[i >> 1] = pack2<DT>(p0, p1);
         }
+        __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T . P^T over the block's two 16-key steps
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const u32x4 pf = {pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]};
 #pragma unroll
             for (int d = 0; d < DTL; ++d) {
-                const unsigned char *vb = vst + voffd[d] + (uint32_t)(16 * st * D) * 2;
-                const uint64_t lo4 = lds_read_tr16(vb);
-                const uint64_t hi4 = lds_read_tr16(vb + 8 * D * 2);
-                const u32x4 vf = {(uint32_t)lo4, (uint32_t)(lo4 >> 32), (uint32_t)hi4,
-                                  (uint32_t)(hi4 >> 32)};
-                o[d] = mfma32<DT>(vf, pf, o[d]);
+                const int i = st * DTL + d;
+                if (i + 1 < 2 * DTL)
+                    vf[(i + 1) & 1] = vread((i + 1) / DTL, (i + 1) % DTL);
+                __builtin_amdgcn_sched_barrier(0);
+                o[d] = mfma32<DT>(vf[i & 1], pf, o[d]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };

@@ -182,14 +182,24 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     // busy (three waves fit: one accumulator pair per wave).
     auto block = [&](const unsigned char *kb, int jb) {
         f32x16 c0 = f32x16{}, c1 = f32x16{};
-        u32x4 bq[2];
-        bq[0] = *reinterpret_cast<const u32x4 *>(kb + boff[0]);
+        // the K fragments are read PF steps ahead of their MFMAs; the
+        // scheduling fences keep that order (left to itself the compiler reads
+        // one step ahead, and each MFMA pair then waits for its LDS read:
+        // measured 2-8 % slower)
+        constexpr int PF = 2;
+        u32x4 bq[PF + 1];
+#pragma unroll
+        for (int kk = 0; kk < PF && kk < KS; ++kk)
+            bq[kk] = *reinterpret_cast<const u32x4 *>(kb + boff[kk]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            if (kk + 1 < KS)
-                bq[(kk + 1) & 1] = *reinterpret_cast<const u32x4 *>(kb + boff[kk + 1]);
-            c0 = mfma32<DT>(a[0][kk], bq[kk & 1], c0);
-            c1 = mfma32<DT>(a[1][kk], bq[kk & 1], c1);
+            if (kk + PF < KS)
+                bq[(kk + PF) % (PF + 1)] = *reinterpret_cast<const u32x4 *>(kb + boff[kk + PF]);
+            __builtin_amdgcn_sched_barrier(0);
+            c0 = mfma32<DT>(a[0][kk], bq[kk % (PF + 1)], c0);
+            c1 = mfma32<DT>(a[1][kk], bq[kk % (PF + 1)], c1);
+            __builtin_amdgcn_sched_barrier(0);
         }
         float part[NSLOT][2];
 #pragma unroll
