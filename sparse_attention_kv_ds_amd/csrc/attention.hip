@@ -234,28 +234,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
     // block b from K stage kst and V stage vst; k_done() runs once this
     // wave's K fragments are in registers
     auto compute_block = [&](int b, const unsigned char *kst, const unsigned char *vst,
-                             auto &&k_done) {
-        // valid keys of the block (bit r), the same in every lane; a block with
-        // no valid key goes through with every score -inf (its p are all 0):
-        // an early exit here would give the accumulators a second home across
-        // the loop and cost registers
+                             auto &&pre, auto &&k_done) {
+        // this lane's key slot of the block is valid (read here, used after
+        // the score MFMAs); a block with no valid key goes through with every
+        // score -inf (its p are all 0): an early exit here would give the
+        // accumulators a second home across the loop and cost registers
         bool valid;
         if (b < nb_loc)
             valid = 32 * b + col < n_loc;
         else
             valid = (uint32_t)ids[32 * (b - nb_loc) + col] != kNoRow;
-        const uint64_t vm = ballot(lane < 32 && valid);
         // S^T: lane holds head col, keys 8 (i / 4) + 4 hf + i % 4
         f32x16 s = f32x16{};
         {
             // K fragments read PF steps ahead of their MFMAs; the scheduling
             // fences keep that order (left to itself the compiler reads one
-            // step ahead, and each MFMA waits for its LDS read)
+            // step ahead, and each MFMA waits for its LDS read).  pre() (the
+            // next block's V loads) goes out once the first reads are issued.
             constexpr int PF = 2;
             u32x4 kf[PF + 1];
 #pragma unroll
             for (int kk = 0; kk < PF && kk < KS; ++kk)
                 kf[kk] = *reinterpret_cast<const u32x4 *>(kst + koff[kk]);
+            __builtin_amdgcn_sched_barrier(0);
+            pre();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
             }
         }
         k_done();
+        const uint64_t vm = ballot(lane < 32 && valid);
         // empty key slots (partial blocks only) score -inf
         if ((uint32_t)vm != 0xFFFFFFFFu) {
             const uint32_t mh = (uint32_t)(vm >> (4 * hf));
@@ -376,11 +379,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
         auto step = [&](int b, const unsigned char *vc, unsigned char *vn) {
             const bool more = b + 1 < nb;
             uint32_t row[NI];
-            if (more) {
+            if (more)
                 block_rows(b + 1, row);
-                issue(b + 1, row, vn, false);
-            }
             compute_block(b, ks0, vc, [&] {
+                if (more)
+                    issue(b + 1, row, vn, false);
+            }, [&] {
                 lds_barrier();
                 if (more)
                     issue(b + 1, row, ks0, true);
