@@ -304,6 +304,11 @@ __device__ __forceinline__ uint64_t select_bound(const uint32_t (&hi)[E], const 
             mx = max(mx, hi[s]);
         }
     red.minmax(mn, mx);
+    // no key with a nonzero high word (only NaN scores map to 0): nothing to
+    // separate, keep every key (without this the band below would start
+    // inverted and the search would not end)
+    if (mn > mx)
+        return 1ull;
     // every key's high word is in [v, u): the band starts as [mn, mx] itself
     uint32_t v = mn;
     uint64_t u = (uint64_t)mx + 1;
@@ -538,6 +543,13 @@ struct WaveSelect {
                 mx = max(mx, hi[s]);
             }
         red.minmax(mn, mx);
+        if (mn > mx) {
+            // no key with a nonzero high word (only NaN scores map to 0):
+            // the first k rows, so that the search below always has a band
+            for (int i = lane; i < k; i += 64)
+                out[i] = key_row(buf[i]);
+            return;
+        }
         // #{high >= v} = cv >= k > cu = #{high >= u}
         uint32_t v = mn, u = mx + 1;
         int cv = cnt, cu = 0;
