@@ -171,6 +171,14 @@ __device__ __forceinline__ void buf_store_u16(__amdgpu_buffer_rsrc_t r, uint32_t
     __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, 0);
 }
 
+// 64 bits (0 past the end of the resource)
+__device__ __forceinline__ uint64_t buf_load_u64(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return ((uint64_t)v[1] << 32) | v[0];
+}
+
 // 16 bits, zero-extended (0 past the end of the resource)
 __device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {

@@ -419,6 +419,27 @@ struct WaveSelect {
         cnt += popc(m);
     }
 
+    // four keys per lane, in the order k0 .. k3 within a lane (lane order,
+    // then k0 .. k3: consecutive rows held by one lane stay in row order)
+    __device__ __forceinline__ void append4(uint64_t k0, bool v0, uint64_t k1, bool v1,
+                                            uint64_t k2, bool v2, uint64_t k3, bool v3)
+    {
+        const bool p0 = v0 && k0 > tau, p1 = v1 && k1 > tau;
+        const bool p2 = v2 && k2 > tau, p3 = v3 && k3 > tau;
+        const uint64_t m0 = ballot(p0), m1 = ballot(p1), m2 = ballot(p2), m3 = ballot(p3);
+        const int at0 = cnt + mbcnt(m0) + mbcnt(m1) + mbcnt(m2) + mbcnt(m3);
+        const int at1 = at0 + (p0 ? 1 : 0), at2 = at1 + (p1 ? 1 : 0), at3 = at2 + (p2 ? 1 : 0);
+        if (p0)
+            buf[at0] = k0;
+        if (p1)
+            buf[at1] = k1;
+        if (p2)
+            buf[at2] = k2;
+        if (p3)
+            buf[at3] = k3;
+        cnt += popc(m0) + popc(m1) + popc(m2) + popc(m3);
+    }
+
     // a batch of one key per lane
     __device__ __forceinline__ void push(uint64_t key, bool valid)
     {
