@@ -370,6 +370,46 @@ int ds_sparse_attention_all(const void *q, const void *k_pool, const void *v_poo
                             int64_t T, int64_t N, int64_t L, int n_heads, int head_dim, int dtype,
                             int ratio, int window, float scale, float *out, void *stream);
 
+/*
+ * One attention step with its selection: ds_indexer_score_topk on the
+ * handle (q_index, k_index, w, pos, T, n_index_rows, ratio, topk, writing the
+ * token's rows into idx), then ds_sparse_attention over the local rows plus
+ * the rows in idx (q, k_pool, v_pool, n_pool_rows, k_local, v_local, L,
+ * n_heads, head_dim, window, scale, out), in stream order on `stream`.
+ *
+ * The indexer's compressed rows and the attention's pooled rows are the same
+ * rows of the sequence, kept in two caches.  The call checks that their
+ * counts agree (n_index_rows == n_pool_rows) before anything runs, and
+ * returns DS_ERR_INVALID_ARG when they have diverged ("How I turned one
+ * oversized DeepSeek optimization into three merged oMLX PRs", section "3. Do
+ * not rank candidates when every candidate wins": the change that skips the
+ * scoring when every pooled row fits in the top-k also checks that the
+ * attention's and the indexer's pooled-row counts have not diverged).  When
+ * every pooled row fits (n_index_rows <= topk) no query is scored: idx gets
+ * each token's sequential rows 0 .. n_t - 1 (-1 padded), as from
+ * ds_indexer_score_topk, and the attention reads them.
+ *
+ *   idx     [T][topk] int32, device: written in full (the selection), then read
+ *   out     [T][n_heads][head_dim] float32, device: written in full
+ * The attention's q, k_pool, v_pool, k_local and v_local hold elements of the
+ * handle's dtype.  Layouts, alignment and ownership of every buffer as in the
+ * two calls; the attention's launch is not timed by ds_indexer_timing.
+ *
+ * Returns DS_OK, DS_ERR_INVALID_ARG (NULL handle, diverged row counts, or any
+ * argument either call rejects), DS_ERR_CAPACITY (T, n_index_rows or topk above
+ * the handle's capacities), DS_ERR_UNSUPPORTED (an attention shape outside
+ * ds_sparse_attention's list) or DS_ERR_HIP.  Every check of both steps is made
+ * on the host before the first launch, so a rejected call launches nothing
+ * and writes neither idx nor out.
+ */
+int ds_indexed_sparse_attention(ds_indexer *ix, const void *q_index, const void *k_index,
+                                const float *w, const int32_t *pos, int64_t T,
+                                int64_t n_index_rows, int ratio, int topk, int32_t *idx,
+                                const void *q, const void *k_pool, const void *v_pool,
+                                int64_t n_pool_rows, const void *k_local, const void *v_local,
+                                int64_t L, int n_heads, int head_dim, int window, float scale,
+                                float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -539,13 +539,16 @@ void ds_indexer_destroy(ds_indexer *ix)
 
 namespace {
 
-// shared by both attention entry points: ratio == 0 takes the index list
-// idx[T][topk]; ratio > 0 attends to every visible pooled row (topk == N)
-int attention_call(const void *q, const void *k_pool, const void *v_pool, const void *k_local,
-                   const void *v_local, const int32_t *idx, const int32_t *pos, int64_t T,
-                   int64_t N, int64_t L, int n_heads, int head_dim, int dtype, int64_t topk,
-                   int ratio, int window, float scale, float *out, void *stream)
+// the argument checks shared by every attention entry point, and the problem
+// they describe: ratio == 0 takes the index list idx[T][topk]; ratio > 0
+// attends to every visible pooled row (topk == N).  DS_OK with a.T == 0 means
+// there is nothing to launch.
+int attention_check(const void *q, const void *k_pool, const void *v_pool, const void *k_local,
+                    const void *v_local, const int32_t *idx, const int32_t *pos, int64_t T,
+                    int64_t N, int64_t L, int n_heads, int head_dim, int dtype, int64_t topk,
+                    int ratio, int window, float scale, float *out, dsi::AttnProblem &a)
 {
+    a.T = 0;
     // the softmax temperature is a positive finite number (the kernel takes
     // each head's maximum on the unscaled scores)
     if (T < 0 || N < 0 || L < 0 || topk < 0 || window < 0 || !(scale > 0.f) || scale > 3.0e38f)
@@ -557,7 +560,7 @@ int attention_call(const void *q, const void *k_pool, const void *v_pool, const 
         T * (int64_t)n_heads * head_dim >= ((int64_t)1 << 40))
         return DS_ERR_UNSUPPORTED;
     if (T == 0)
-        return DS_OK;
+        return DS_OK; // (a.T == 0: nothing to launch)
     if (!q || !pos || !out || (ratio == 0 && topk > 0 && !idx) ||
         (N > 0 && (!k_pool || !v_pool)) || (L > 0 && (!k_local || !v_local)))
         return DS_ERR_INVALID_ARG;
@@ -565,7 +568,6 @@ int attention_call(const void *q, const void *k_pool, const void *v_pool, const 
         !aligned(k_local, 16) || !aligned(v_local, 16) || !aligned(out, 16) ||
         !aligned(idx, 4) || !aligned(pos, 4))
         return DS_ERR_INVALID_ARG;
-    dsi::AttnProblem a;
     a.q = q;
     a.kp = k_pool;
     a.vp = v_pool;
@@ -584,6 +586,19 @@ int attention_call(const void *q, const void *k_pool, const void *v_pool, const 
     a.dtype = dtype;
     a.scale = scale;
     a.out = out;
+    return DS_OK;
+}
+
+int attention_call(const void *q, const void *k_pool, const void *v_pool, const void *k_local,
+                   const void *v_local, const int32_t *idx, const int32_t *pos, int64_t T,
+                   int64_t N, int64_t L, int n_heads, int head_dim, int dtype, int64_t topk,
+                   int ratio, int window, float scale, float *out, void *stream)
+{
+    dsi::AttnProblem a;
+    const int st = attention_check(q, k_pool, v_pool, k_local, v_local, idx, pos, T, N, L,
+                                   n_heads, head_dim, dtype, topk, ratio, window, scale, out, a);
+    if (st != DS_OK || a.T == 0)
+        return st;
     return dsi::launch_sparse_attention(a, (hipStream_t)stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
@@ -608,6 +623,45 @@ int ds_sparse_attention_all(const void *q, const void *k_pool, const void *v_poo
         return DS_ERR_INVALID_ARG;
     return attention_call(q, k_pool, v_pool, k_local, v_local, nullptr, pos, T, N, L, n_heads,
                           head_dim, dtype, N, ratio, window, scale, out, stream);
+}
+
+int ds_indexed_sparse_attention(ds_indexer *ix, const void *q_index, const void *k_index,
+                                const float *w, const int32_t *pos, int64_t T,
+                                int64_t n_index_rows, int ratio, int topk, int32_t *idx,
+                                const void *q, const void *k_pool, const void *v_pool,
+                                int64_t n_pool_rows, const void *k_local, const void *v_local,
+                                int64_t L, int n_heads, int head_dim, int window, float scale,
+                                float *out, void *stream)
+{
+    if (!ix)
+        return DS_ERR_INVALID_ARG;
+    // the indexer's compressed rows and the attention's pooled rows are the
+    // same rows: counts that differ mean the two caches have diverged
+    if (n_index_rows != n_pool_rows)
+        return DS_ERR_INVALID_ARG;
+    // every check of both steps before anything is launched
+    int st = check_call(ix, q_index, k_index, w, pos, T, n_index_rows, ratio, idx);
+    if (st != DS_OK)
+        return st;
+    if (topk < 1)
+        return DS_ERR_INVALID_ARG;
+    if (topk > ix->max_topk)
+        return DS_ERR_CAPACITY;
+    dsi::AttnProblem a;
+    st = attention_check(q, k_pool, v_pool, k_local, v_local, idx, pos, T, n_pool_rows, L,
+                         n_heads, head_dim, ix->dtype, topk, 0, window, scale, out, a);
+    if (st != DS_OK)
+        return st;
+    // the selection (the sequential rows when every pooled row fits), then
+    // the attention over it, in stream order
+    st = ds_indexer_score_topk(ix, q_index, k_index, w, pos, T, n_index_rows, ratio, topk, idx,
+                               stream);
+    if (st != DS_OK || a.T == 0)
+        return st;
+    DeviceGuard g(ix->device);
+    if (!g.ok)
+        return DS_ERR_HIP;
+    return dsi::launch_sparse_attention(a, (hipStream_t)stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
 int ds_indexer_stamps_read(int unit, void *host, int64_t bytes)

@@ -38,7 +38,8 @@ EXPORTS = ("ds_indexer_create", "ds_indexer_score_topk", "ds_indexer_destroy",
            "ds_indexer_scores", "ds_indexer_status_str", "ds_indexer_timing",
            "ds_indexer_timing_read", "ds_sparse_attention", "ds_sparse_attention_all",
            "ds_indexer_score_topk_batch", "ds_indexer_project_q", "ds_indexer_project_score_topk",
-           "ds_indexer_score_topk_noalloc", "ds_indexer_stamps_read")
+           "ds_indexer_score_topk_noalloc", "ds_indexer_stamps_read",
+           "ds_indexed_sparse_attention")
 DS_STAMPS_DECODE_SCORE = 0
 DS_STAMPS_TOPK = 1
 DS_STAMPS_MERGE = 2
@@ -92,6 +93,9 @@ def _load() -> ctypes.CDLL:
     lib.ds_sparse_attention_all.restype = I
     lib.ds_sparse_attention_all.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, I, I, I, I,
                                             ctypes.c_float, P, P]
+    lib.ds_indexed_sparse_attention.restype = I
+    lib.ds_indexed_sparse_attention.argtypes = [P, P, P, P, P, I64, I64, I, I, P, P, P, P, I64,
+                                                P, P, I64, I, I, I, ctypes.c_float, P, P]
     return lib
 
 
@@ -169,6 +173,15 @@ def ds_sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, T, N, L, 
                         head_dim, dtype, topk, window, scale, out, stream) -> int:
     return _lib.ds_sparse_attention(q, k_pool, v_pool, k_local, v_local, idx, pos, T, N, L,
                                     n_heads, head_dim, dtype, topk, window, scale, out, stream)
+
+
+def ds_indexed_sparse_attention(handle, q_index, k_index, w, pos, T, n_index_rows, ratio, topk,
+                                idx, q, k_pool, v_pool, n_pool_rows, k_local, v_local, L,
+                                n_heads, head_dim, window, scale, out, stream) -> int:
+    return _lib.ds_indexed_sparse_attention(handle, q_index, k_index, w, pos, T, n_index_rows,
+                                            ratio, topk, idx, q, k_pool, v_pool, n_pool_rows,
+                                            k_local, v_local, L, n_heads, head_dim, window, scale,
+                                            out, stream)
 
 
 # --- torch-facing wrapper -------------------------------------------------------------
@@ -309,6 +322,33 @@ class Indexer:
         if st != DS_OK:
             raise IndexerError(st, "ds_indexer_score_topk_batch")
         return out
+
+    def indexed_sparse_attention(self, q_index, k_index, w, pos, ratio: int, topk: int, q,
+                                 k_pool, v_pool, k_local, v_local, *, window: int, scale: float,
+                                 idx=None, out=None):
+        """The selection and the attention over it in one call
+        (ds_indexed_sparse_attention): q_index, k_index, w, pos as score_topk;
+        q, k_pool, v_pool, k_local, v_local as sparse_attention, in the
+        handle's dtype.  k_index and k_pool must hold the same number of rows
+        (the library refuses the call otherwise).  Returns (idx [T, topk] int32,
+        out [T, HA, D] float32)."""
+        import torch
+        T, N, stream = self._check(q_index, k_index, w, pos)
+        if idx is None:
+            idx = torch.empty((T, topk), dtype=torch.int32, device=q_index.device)
+        elif (idx.dtype != torch.int32 or tuple(idx.shape) != (T, topk) or not idx.is_contiguous()
+              or idx.device != q_index.device):
+            raise ValueError("idx must be a contiguous int32 [T, topk] tensor on q's device")
+        _, HA, D, _, out, _ = _attention_args(q, k_pool, v_pool, k_local, v_local, idx, pos,
+                                              self.dtype, out)
+        st = ds_indexed_sparse_attention(
+            self.handle, q_index.data_ptr(), _ptr(k_index), w.data_ptr(), pos.data_ptr(), T, N,
+            ratio, topk, idx.data_ptr(), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+            _ptr(k_local), _ptr(v_local), k_local.shape[0], HA, D, window, float(scale),
+            out.data_ptr(), stream)
+        if st != DS_OK:
+            raise IndexerError(st, "ds_indexed_sparse_attention")
+        return idx, out
 
     def timing(self, enable: bool) -> None:
         st = ds_indexer_timing(self.handle, 1 if enable else 0)

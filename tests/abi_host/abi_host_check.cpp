@@ -345,6 +345,42 @@ void attention_checks()
                                    0.1f, SC, nullptr));
 }
 
+// the selection plus the attention in one call: the two pooled-row counts
+// must agree, and every argument of both steps is checked before the first
+// launch
+void indexed_attention_checks(ds_indexer *ix)
+{
+    auto call = [&](int64_t T, int64_t n_index, int64_t n_pool, int topk, int heads, float scale,
+                    int32_t *idx, float *out) {
+        return ds_indexed_sparse_attention(ix, Q, K, W, POS, T, n_index, 4, topk, idx, X, K, K,
+                                           n_pool, X, X, 200, heads, 128, 16, scale, out, nullptr);
+    };
+    REJECT(DS_ERR_INVALID_ARG, ds_indexed_sparse_attention(nullptr, Q, K, W, POS, 4, 1000, 4, 512,
+                                                           OUT, X, K, K, 1000, X, X, 200, 64, 128,
+                                                           16, 0.1f, SC, nullptr));
+    // diverged pooled-row counts, either way round
+    REJECT(DS_ERR_INVALID_ARG, call(4, 1000, 999, 512, 64, 0.1f, OUT, SC));
+    REJECT(DS_ERR_INVALID_ARG, call(4, 300, 301, 512, 64, 0.1f, OUT, SC));
+    // the indexer's checks
+    REJECT(DS_ERR_INVALID_ARG, call(4, 1000, 1000, 0, 64, 0.1f, OUT, SC));
+    REJECT(DS_ERR_CAPACITY, call(65, 1000, 1000, 512, 64, 0.1f, OUT, SC));
+    REJECT(DS_ERR_CAPACITY, call(4, 4097, 4097, 512, 64, 0.1f, OUT, SC));
+    REJECT(DS_ERR_CAPACITY, call(4, 1000, 1000, 513, 64, 0.1f, OUT, SC));
+    REJECT(DS_ERR_INVALID_ARG, call(4, 1000, 1000, 512, 64, 0.1f, off(OUT, 2), SC));
+    // the attention's checks
+    REJECT(DS_ERR_INVALID_ARG, call(4, 1000, 1000, 512, 64, 0.0f, OUT, SC));
+    REJECT(DS_ERR_INVALID_ARG, call(4, 1000, 1000, 512, 64, 0.1f, OUT, off(SC, 4)));
+    REJECT(DS_ERR_INVALID_ARG, call(4, 1000, 1000, 512, 64, 0.1f, OUT, nullptr));
+    REJECT(DS_ERR_UNSUPPORTED, call(4, 1000, 1000, 512, 48, 0.1f, OUT, SC));
+    ACCEPT(({}), call(0, 1000, 1000, 512, 64, 0.1f, OUT, SC));
+    ACCEPT(({"prefill_scorer", "topk_stream", "sparse_attention"}),
+           call(4, 1000, 1000, 512, 64, 0.1f, OUT, SC));
+    // every pooled row fits: sequential rows, no scoring, then the attention
+    ACCEPT(({"sequential_rows", "sparse_attention"}), call(4, 300, 300, 512, 64, 0.1f, OUT, SC));
+    ACCEPT(({"decode_scorer", "decode_select", "sparse_attention"}),
+           call(1, 4000, 4000, 512, 64, 0.1f, OUT, SC));
+}
+
 } // namespace
 
 int main()
@@ -369,6 +405,7 @@ int main()
     timing_checks(ix);
     noalloc_checks();
     attention_checks();
+    indexed_attention_checks(ix);
     ds_indexer_destroy(ix);
     ds_indexer_destroy(wide);
     ds_indexer_destroy(big);

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                                            "ds_indexer_score_topk_batch", "ds_indexer_project_q",
                                            "ds_indexer_project_score_topk",
                                            "ds_indexer_score_topk_noalloc",
-                                           "ds_indexer_stamps_read"])
+                                           "ds_indexer_stamps_read",
+                                           "ds_indexed_sparse_attention"])
 
 
 def test_every_declared_symbol_is_exported(ix):

@@ -214,3 +214,89 @@ def test_deterministic(ix):
     a = run_gpu(ix, d, "bf16", 64, 0.088)
     b = run_gpu(ix, d, "bf16", 64, 0.088)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# the selection and the attention in one call (ds_indexed_sparse_attention)
+# ---------------------------------------------------------------------------
+
+def indexed_case(seed, T, N, p_lo, p_hi, topk, L, window, H=8, D=64, HA=32, dtype="f16"):
+    """Integer-valued indexer inputs (every fp32 sum exact) at ratio 4 and
+    Gaussian attention inputs over the same N pooled rows."""
+    rng = np.random.default_rng(seed)
+    q_idx, k_idx, w = synth.draw(T, N, H, D, dtype, "int", seed=seed)
+    sk = 1.0 / np.sqrt(D)
+    d = {"q": synth.to_bits(rng.standard_normal((T, HA, D)) * sk * 2, dtype),
+         "kp": synth.to_bits(rng.standard_normal((N, D)) * sk, dtype),
+         "vp": synth.to_bits(rng.standard_normal((N, D)), dtype),
+         "kl": synth.to_bits(rng.standard_normal((L, D)) * sk, dtype),
+         "vl": synth.to_bits(rng.standard_normal((L, D)), dtype),
+         "pos": np.sort(rng.integers(p_lo, p_hi + 1, size=T)).astype(np.int32)}
+    return q_idx, k_idx, w, d
+
+
+def run_indexed(ix, h, q_idx, k_idx, w, d, *, topk, window, scale, extra_pool_rows=0):
+    import torch
+    dev = torch.device("cuda", 0)
+    t = to_dev({**d, "idx": np.zeros((1, 1), dtype=np.int32)})
+    if extra_pool_rows:
+        pad = torch.zeros((extra_pool_rows, t["kp"].shape[1]), dtype=t["kp"].dtype, device=dev)
+        t["kp"] = torch.cat([t["kp"], pad]).contiguous()
+        t["vp"] = torch.cat([t["vp"], pad]).contiguous()
+    qi = torch.from_numpy(q_idx.view(np.int16)).to(dev)
+    ki = torch.from_numpy(k_idx.view(np.int16)).to(dev)
+    wt = torch.from_numpy(w).to(dev)
+    T = d["pos"].shape[0]
+    idx = torch.full((T, topk), -7, dtype=torch.int32, device=dev)
+    out = torch.full((T, t["q"].shape[1], t["q"].shape[2]), 3.0, dtype=torch.float32, device=dev)
+    try:
+        h.indexed_sparse_attention(qi, ki, wt, t["pos"], 4, topk, t["q"], t["kp"], t["vp"],
+                                   t["kl"], t["vl"], window=window, scale=scale, idx=idx, out=out)
+        err = None
+    except ix.IndexerError as e:
+        err = e
+    torch.cuda.synchronize()
+    return err, idx.cpu().numpy(), out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("seed,T,N,p_lo,p_hi,topk", [
+    (1, 70, 250, 700, 999, 64),      # selection for most tokens, all-fit for the earliest
+    (2, 33, 600, 2000, 2399, 100),   # selection everywhere
+    (3, 40, 50, -3, 300, 64),        # every pooled row fits: no scoring at all
+])
+def test_indexed_attention_against_oracle(ix, orc, seed, T, N, p_lo, p_hi, topk):
+    """idx bit-exact against the indexer oracle, out against the attention
+    oracle over the oracle's own selection."""
+    H, D, HA, dtype, L, window = 8, 64, 32, "f16", 2500, 48
+    scale = 1.0 / np.sqrt(D)
+    q_idx, k_idx, w, d = indexed_case(seed, T, N, p_lo, p_hi, topk, L, window, H=H, D=D, HA=HA,
+                                      dtype=dtype)
+    h = ix.Indexer(H, D, dtype, max_topk=topk, max_tokens=T, max_rows=N)
+    try:
+        err, idx, out = run_indexed(ix, h, q_idx, k_idx, w, d, topk=topk, window=window,
+                                    scale=scale)
+    finally:
+        h.close()
+    assert err is None, err
+    want_idx = orc.score_topk(q_idx, k_idx, w, d["pos"], H=H, D=D, dtype=dtype, ratio=4,
+                              topk=topk, threads=8)
+    np.testing.assert_array_equal(idx, want_idx)
+    want = orc.sparse_attention(d["q"], d["kp"], d["vp"], d["kl"], d["vl"], want_idx, d["pos"],
+                                dtype=dtype, window=window, scale=scale, threads=8)
+    check(out, want, d, dtype, f"indexed seed {seed}")
+
+
+def test_indexed_attention_refuses_diverged_pool_counts(ix):
+    """Pooled-row counts that differ between the indexer's and the attention's
+    rows: DS_ERR_INVALID_ARG, and neither idx nor out is written."""
+    H, D, HA, dtype, T, N, topk = 8, 64, 32, "f16", 20, 300, 64
+    q_idx, k_idx, w, d = indexed_case(9, T, N, 800, 1100, topk, 1200, 16, H=H, D=D, HA=HA,
+                                      dtype=dtype)
+    h = ix.Indexer(H, D, dtype, max_topk=topk, max_tokens=T, max_rows=N + 1)
+    try:
+        err, idx, out = run_indexed(ix, h, q_idx, k_idx, w, d, topk=topk, window=16,
+                                    scale=0.125, extra_pool_rows=1)
+    finally:
+        h.close()
+    assert err is not None and err.status == ix.DS_ERR_INVALID_ARG
+    assert (idx == -7).all() and (out == 3.0).all()
