@@ -409,18 +409,55 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3
     // o = O / l for head col (the two halves' parts of l added)
     float l = add_other_half(l_part);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *ot = out + ((long long)t * HA + wave * 32 + col) * D;
+    if constexpr (WAVES <= 3) {
+        // One 32-wide value tile at a time goes through this wave's own LDS
+        // region (a stage array, free after the last block: 32 heads x 32
+        // floats, the eight 16-byte chunks of head h's row at chunk ^ (h % 8))
+        // and out as whole 128-byte pieces, eight heads per store.  (A lane
+        // holds four 16-byte pieces of one head per tile, 512 bytes apart from
+        // its neighbours': stored directly, every store writes 32 partial
+        // lines.)  Every stage array holds 4 KiB at D = 64 and 128.
+        static_assert(BLK_B >= 32 * 32 * 4, "a stage array holds one 32 x 32 float tile");
+        float *const stg = reinterpret_cast<float *>(wave == 0 ? ks0 : (wave == 1 ? vs0 : vs1));
+        const auto ro = make_rsrc(out + ((long long)t * HA + wave * 32) * D, 32u * D * 4);
 #pragma unroll
-    for (int d = 0; d < DTL; ++d)
+        for (int d = 0; d < DTL; ++d) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float4 v;
-            v.x = o[d][4 * r] * inv;
-            v.y = o[d][4 * r + 1] * inv;
-            v.z = o[d][4 * r + 2] * inv;
-            v.w = o[d][4 * r + 3] * inv;
-            *reinterpret_cast<float4 *>(ot + 32 * d + 8 * r + 4 * hf) = v;
+            for (int r = 0; r < 4; ++r) {
+                float4 v;
+                v.x = o[d][4 * r] * inv;
+                v.y = o[d][4 * r + 1] * inv;
+                v.z = o[d][4 * r + 2] * inv;
+                v.w = o[d][4 * r + 3] * inv;
+                // value columns 8 r + 4 hf .. + 3 of the tile: chunk 2 r + hf
+                *reinterpret_cast<float4 *>(stg + col * 32 + 4 * ((2 * r + hf) ^ (col & 7))) = v;
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 8 * j + (lane >> 3), c = lane & 7;
+                const float4 v = *reinterpret_cast<const float4 *>(stg + h * 32 + 4 * (c ^ (h & 7)));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                                       (uint32_t)(h * D + 32 * d + 4 * c) * 4, 0, 0);
+            }
+            wave_lds_sync();
         }
+    } else {
+        // four waves (128 heads): no stage array of its own for the fourth,
+        // so every lane stores its pieces directly
+        float *ot = out + ((long long)t * HA + wave * 32 + col) * D;
+#pragma unroll
+        for (int d = 0; d < DTL; ++d)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float4 v;
+                v.x = o[d][4 * r] * inv;
+                v.y = o[d][4 * r + 1] * inv;
+                v.z = o[d][4 * r + 2] * inv;
+                v.w = o[d][4 * r + 3] * inv;
+                *reinterpret_cast<float4 *>(ot + 32 * d + 8 * r + 4 * hf) = v;
+            }
+    }
     DSI_STAMP(attn_stamps, t, 3, threadIdx.x == 0);
 }
 
