@@ -515,9 +515,10 @@ def ceilings(reps: int = 20):
     a vendor (hipBLASLt, through torch.matmul) dense 8192^3 GEMM on
     integer-valued fp16 operands and on Gaussian fp16 / bf16 operands (the
     matrix cores draw more power on random mantissas and the clock drops),
-    and a plain device copy of 64 MiB (torch copy_ over 8 rotating buffer
-    pairs, so that every pass reads and writes HBM).  Times are events around back-to-back
-    launches on one stream."""
+    a plain device copy of 64 MiB (torch copy_ over 8 rotating buffer
+    pairs, so that every pass reads and writes HBM), and plain reads of 64 MiB
+    and 512 MiB (torch sum).  Times are events around back-to-back launches on
+    one stream."""
     import torch
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev).manual_seed(0)
@@ -558,6 +559,23 @@ def ceilings(reps: int = 20):
     out["copy_64MiB"] = {"GBps_read_plus_write": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "us": t * 1e6}
     log(f"[ceilings] device copy of 64 MiB (torch copy_, 8 rotating buffer pairs): {t * 1e6:.1f} us, "
         f"{gbs:.0f} GB/s read + write ({gbs / PEAK_HBM_GBS * 100:.1f} % of 8 TB/s)")
+    # read-only: a vendor reduction (torch sum into float32) over one 64 MiB
+    # buffer per call (8 rotating buffers, the single-sequence decode's K), and
+    # over 512 MiB in one call (the eight-sequence decode's K)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    t = timed(lambda i: torch.sum(src[i % 8], dim=0, dtype=torch.float32, out=acc), 8 * reps)
+    gbs = 64 * 2 ** 20 / t / 1e9
+    out["read_64MiB"] = {"GBps": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "us": t * 1e6}
+    log(f"[ceilings] read of 64 MiB (torch sum, 8 rotating buffers): {t * 1e6:.1f} us, "
+        f"{gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f} % of 8 TB/s)")
+    del dst
+    big = torch.cat(src)
+    del src
+    t = timed(lambda i: torch.sum(big, dim=0, dtype=torch.float32, out=acc), reps)
+    gbs = 512 * 2 ** 20 / t / 1e9
+    out["read_512MiB"] = {"GBps": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "us": t * 1e6}
+    log(f"[ceilings] read of 512 MiB (torch sum, one buffer): {t * 1e6:.1f} us, "
+        f"{gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f} % of 8 TB/s)")
     print(json.dumps(out))
 
 
