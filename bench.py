@@ -653,6 +653,7 @@ def _pmc_table(directory: str):
 
 
 DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
+            "prefill8k": ("score", "prefill_scorer_kernel"),
             "prefill32k": ("score", "prefill_scorer_kernel"),
             "prefill64k": ("score", "prefill_scorer_kernel"),
             "attn32k": ("attention", "sparse_attention_kernel"),
@@ -660,6 +661,7 @@ DOMINANT = {"decode1m": ("decode_score", "decode_scorer_kernel"),
             "decode1m_b8": ("decode_score", "decode_scorer_kernel"),
             "qproj32k": ("project", "qproj_kernel"),
             # the prefill top-k of the same runs (for the record, not a bench roofline)
+            "prefill8k_select": ("select", "topk_stream_kernel"),
             "prefill32k_select": ("select", "topk_stream_kernel"),
             "prefill64k_select": ("select", "topk_stream_kernel")}
 

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     // heads, and the store of s[t][jb + col].  The VALU work of one wave's
     // epilogue runs while the other waves of its SIMD keep the matrix core
     // busy (three waves fit: one accumulator pair per wave).
-    auto block = [&](const unsigned char *kb, int jb) {
+    auto block = [&](const unsigned char *kb, int jb) __attribute__((always_inline)) {
         f32x16 c0 = f32x16{}, c1 = f32x16{};
         // the K fragments are read PF steps ahead of their MFMAs; the
         // scheduling fences keep that order (left to itself the compiler reads
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_scorer_kernel(
     };
 
     // the blocks of one stage (rows js.. in LDS at kt)
-    auto run_stage = [&](const unsigned char *kt, int js) {
+    auto run_stage = [&](const unsigned char *kt, int js) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < SR / 32; ++b) {
             if (b > 0 && js + 32 * b >= j_end)
