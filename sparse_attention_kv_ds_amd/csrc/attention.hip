@@ -32,7 +32,9 @@
 //   * O^T += V_blk^T . P^T on the MFMA: P comes straight from the S^T
 //     accumulators (converted to the value type), V^T fragments from the
 //     row-major V block by LDS transpose reads (ds_read_b64_tr_b16).
-// Output fp32, o = O / (sum of p), 0 for a token with no row.
+// Output fp32, o = O / (sum of p), 0 for a token with no row, written a
+// 32-wide value tile at a time through the free stage arrays as whole
+// 128-byte pieces.
 #include "common.hpp"
 #include "launch.hpp"
 
