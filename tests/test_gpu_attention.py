@@ -263,11 +263,13 @@ def run_indexed(ix, h, q_idx, k_idx, w, d, *, topk, window, scale, extra_pool_ro
     (1, 70, 250, 700, 999, 64),      # selection for most tokens, all-fit for the earliest
     (2, 33, 600, 2000, 2399, 100),   # selection everywhere
     (3, 40, 50, -3, 300, 64),        # every pooled row fits: no scoring at all
+    (4, 1, 3000, 11999, 11999, 512), # one token: the single-token decode path, then attention
 ])
 def test_indexed_attention_against_oracle(ix, orc, seed, T, N, p_lo, p_hi, topk):
     """idx bit-exact against the indexer oracle, out against the attention
     oracle over the oracle's own selection."""
-    H, D, HA, dtype, L, window = 8, 64, 32, "f16", 2500, 48
+    H, D, HA, dtype, window = 8, 64, 32, "f16", 48
+    L = max(2500, p_hi + 1)  # raw rows up to the last position
     scale = 1.0 / np.sqrt(D)
     q_idx, k_idx, w, d = indexed_case(seed, T, N, p_lo, p_hi, topk, L, window, H=H, D=D, HA=HA,
                                       dtype=dtype)
