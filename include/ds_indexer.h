@@ -28,7 +28,9 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting: the caller keeps every buffer alive and
  *     unmodified until the stream reaches that point.  No host synchronisation
- *     happens inside a call.
+ *     happens inside a call.  A call enqueues kernel launches only (no
+ *     allocation, copy or memset on the stream), so the compute calls can be
+ *     captured into a HIP graph and replayed (with kernel timing off).
  *   - A handle owns device scratch (the score matrix and selection candidates);
  *     two calls on one handle must not run concurrently (use one handle per
  *     concurrently used stream).
